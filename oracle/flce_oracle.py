@@ -1,0 +1,279 @@
+"""Plain fp64 CPU oracle for fused linear cross-entropy (FLCE).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP library.
+
+What it computes is the plain definition of the loss on materialised logits,
+because the fused method reaches exactly that result (up to rounding order) and
+only avoids storing the [N, V] logits:
+
+* page "Cutting LLM Memory by 84%: A Deep Dive into Fused Kernels",
+  section "The maths behind Fused Linear Cross-Entropy / Definition and Forward
+  Pass": with a one-hot target the cross-entropy of softmax(x.W) collapses to
+  LSE(logits) - (target logit), evaluated with the row maximum subtracted;
+* same page, "Backward Pass": matmul gradients dX = G.W^T, dW = X^T.G
+  (section "Matrix Multiplication"), the cross-entropy gradient
+  softmax - onehot (section "Cross-Entropy"), their chain-rule product
+  (section "Fused Linear Cross-Entropy") and the batch reduction of the weight
+  gradient by sum or mean (the note that closes that section);
+* same page, "Kernel Implementation", step 1: rows whose target equals
+  ignore_index (default -100) contribute a loss of 0;
+* page "[CuteDSL] FLCE: 2-SM online-softmax fast path (Blackwell)" (Liger-Kernel
+  PR #1291), Summary: the option set bias, softcap, label_smoothing, z-loss
+  (lse_square_scale), ignore_index, mean/sum reduction and forward-only
+  reduction='none';
+* page "Add efficient Cross-Entropy by cuda kernel" (TransformerEngine PR #995),
+  review of the backward kernel: label smoothing subtracts a uniform term from
+  the softmax gradient.
+
+Readings taken where the pages are silent or their equations were lost (every
+displayed equation of the first page is missing from the extracted text):
+
+* W is stored [V, D] (nn.Linear layout); logits r = X.W^T + b.
+* softcap c > 0: z = c * tanh(r / c), applied after the bias and before the
+  LSE, target logit, smoothing and z-loss; c <= 0 means off.
+* label smoothing eps: target distribution q = (1 - eps) onehot + eps / V
+  (PyTorch convention; the Megatron form on the TransformerEngine page is the
+  same family with eps' = eps V / (V - 1)).
+* z-loss: + s * lse^2 per valid row, reduced like the cross-entropy term.
+* mean divides by n_valid (rows whose target is not ignore_index); with
+  n_valid = 0 the loss and every gradient are 0.
+* ignored rows report lse = 0 and row_loss = 0.
+* grad_output g scales every gradient; scale = g / n_valid (mean) or g (sum).
+
+Parity status of each function is stated in its docstring; every function is
+pinned by tests in ``tests/test_oracle_pins.py`` except where a docstring says
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Iterator, Optional, Tuple
+
+import numpy as np
+
+ROW_BLOCK = 1024
+
+
+@dataclasses.dataclass(frozen=True)
+class LossOptions:
+    ignore_index: int = -100
+    label_smoothing: float = 0.0
+    lse_square_scale: float = 0.0
+    softcap: float = 0.0
+    reduction: str = "mean"
+
+
+# --------------------------------------------------------------------- inputs
+
+def to_f64(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
+    """Exact widening of the stored inputs: uint16 arrays hold bf16 bit
+    patterns (the upper half of an IEEE fp32), float arrays widen as is."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        wide = a.astype(np.uint32) << np.uint32(16)
+        return wide.view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------- pieces
+
+def logits(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray],
+           softcap: float) -> np.ndarray:
+    """Logits of a block of rows: z = X.W^T (+ b), then the optional softcap
+    z = c tanh(z / c).  Pinned: closed forms at W = 0, the torch special case,
+    finite differences, brute force."""
+    r = x @ w.T
+    if bias is not None:
+        r = r + bias[None, :]
+    if softcap > 0.0:
+        r = softcap * np.tanh(r / softcap)
+    return r
+
+
+def log_sum_exp(z: np.ndarray) -> np.ndarray:
+    """Row-wise LSE with the row maximum subtracted first (numerically stable
+    softmax, page "Cutting LLM Memory by 84%", "Definition and Forward
+    Pass").  Pinned: ln V at W = 0, the online merge, brute force."""
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
+def log_sum_exp_online(z: np.ndarray, block: int) -> np.ndarray:
+    """The same LSE reached by the online-softmax recurrence over vocabulary
+    blocks (page "Cutting LLM Memory by 84%", "Definition and Forward Pass",
+    step 2: a running maximum m and a running sum of exponentials d, the sum
+    rescaled by exp(m_old - m_new) whenever the maximum grows).  Used only to
+    pin the merge rule that the GPU epilogue relies on."""
+    n, v = z.shape
+    m = np.full(n, -np.inf)
+    d = np.zeros(n)
+    for v0 in range(0, v, block):
+        blk = z[:, v0:v0 + block]
+        m_new = np.maximum(m, blk.max(axis=1))
+        d = d * np.exp(m - m_new) + np.exp(blk - m_new[:, None]).sum(axis=1)
+        m = m_new
+    return m + np.log(d)
+
+
+def valid_rows(targets: np.ndarray, opts: LossOptions) -> np.ndarray:
+    return np.asarray(targets) != opts.ignore_index
+
+
+def check_targets(targets: np.ndarray, v: int, opts: LossOptions) -> None:
+    t = np.asarray(targets)
+    bad = (t != opts.ignore_index) & ((t < 0) | (t >= v))
+    if bad.any():
+        raise ValueError("target outside [0, V) and not ignore_index")
+
+
+def row_losses(z: np.ndarray, lse: np.ndarray, targets: np.ndarray,
+               opts: LossOptions) -> np.ndarray:
+    """Per-row loss of valid rows: the cross-entropy between the smoothed
+    target distribution q = (1-eps) onehot_t + eps/V and softmax(z),
+    -sum_v q_v (z_v - lse) = lse - (1-eps) z_t - (eps/V) sum_v z_v, plus the
+    z-loss s lse^2.  Ignored rows get 0."""
+    n, v = z.shape
+    valid = valid_rows(targets, opts)
+    t = np.where(valid, targets, 0)
+    zt = z[np.arange(n), t]
+    eps = opts.label_smoothing
+    out = lse - (1.0 - eps) * zt
+    if eps != 0.0:
+        out = out - (eps / v) * z.sum(axis=1)
+    if opts.lse_square_scale != 0.0:
+        out = out + opts.lse_square_scale * lse * lse
+    return np.where(valid, out, 0.0)
+
+
+def grad_logits(z: np.ndarray, lse: np.ndarray, targets: np.ndarray,
+                opts: LossOptions) -> np.ndarray:
+    """d(row_loss)/d(pre-softcap logit), unscaled:
+    G = [softmax(z) (1 + 2 s lse) - (1-eps) onehot_t - eps/V] * dz/dr, with
+    dz/dr = 1 - (z/c)^2 under the softcap; zero rows for ignored targets.
+    (page "Cutting LLM Memory by 84%", "Cross-Entropy": prediction minus
+    ground truth.)  Pinned: finite differences, torch autograd, row sums."""
+    n, v = z.shape
+    valid = valid_rows(targets, opts)
+    t = np.where(valid, targets, 0)
+    p = np.exp(z - lse[:, None])
+    s = opts.lse_square_scale
+    g = p * (1.0 + 2.0 * s * lse)[:, None] if s != 0.0 else p
+    g[np.arange(n), t] -= (1.0 - opts.label_smoothing)
+    if opts.label_smoothing != 0.0:
+        g -= opts.label_smoothing / v
+    if opts.softcap > 0.0:
+        g *= 1.0 - (z / opts.softcap) ** 2
+    g[~valid] = 0.0
+    return g
+
+
+def grad_scale(opts: LossOptions, n_valid: int, grad_output: float) -> float:
+    """Scale from the unscaled per-row gradient to d(loss): g / n_valid for
+    mean (0 when no row is valid), g for sum.  reduction 'none' has no
+    backward (refused, page "[CuteDSL] FLCE", Summary)."""
+    if opts.reduction == "mean":
+        return grad_output / n_valid if n_valid > 0 else 0.0
+    if opts.reduction == "sum":
+        return grad_output
+    raise ValueError("reduction='none' has no backward")
+
+
+def reduce_loss(row_loss: np.ndarray, n_valid: int, opts: LossOptions):
+    if opts.reduction == "mean":
+        return float(row_loss.sum() / n_valid) if n_valid > 0 else 0.0
+    if opts.reduction == "sum":
+        return float(row_loss.sum())
+    if opts.reduction == "none":
+        return row_loss.copy()
+    raise ValueError(f"unknown reduction {opts.reduction!r}")
+
+
+# ------------------------------------------------------------- whole problem
+
+@dataclasses.dataclass
+class Result:
+    loss: object                     # float, or [N] array for 'none'
+    lse: np.ndarray                  # [N], 0 on ignored rows
+    row_loss: np.ndarray             # [N]
+    n_valid: int
+    dx: Optional[np.ndarray] = None  # [N, D]
+    dw: Optional[np.ndarray] = None  # [V, D]
+    db: Optional[np.ndarray] = None  # [V]
+
+
+def forward(x, w, bias, targets, opts: LossOptions,
+            n_valid: Optional[int] = None, row_block: int = ROW_BLOCK) -> Result:
+    """Loss, per-row LSE and per-row loss.  ``n_valid`` overrides the mean
+    denominator (sampled rows of a larger batch use the full batch's count)."""
+    x, w, bias = to_f64(x), to_f64(w), to_f64(bias)
+    targets = np.asarray(targets)
+    check_targets(targets, w.shape[0], opts)
+    n = x.shape[0]
+    valid = valid_rows(targets, opts)
+    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    lse = np.zeros(n)
+    rl = np.zeros(n)
+    for r0 in range(0, n, row_block):
+        sl = slice(r0, min(n, r0 + row_block))
+        z = logits(x[sl], w, bias, opts.softcap)
+        l = log_sum_exp(z)
+        rl[sl] = row_losses(z, l, targets[sl], opts)
+        lse[sl] = np.where(valid[sl], l, 0.0)
+    return Result(reduce_loss(rl, nv, opts), lse, rl, nv)
+
+
+def forward_backward(x, w, bias, targets, opts: LossOptions,
+                     grad_output: float = 1.0, n_valid: Optional[int] = None,
+                     want_dw: bool = True, row_block: int = ROW_BLOCK) -> Result:
+    """Forward plus dX = scale G.W, dW = scale G^T.X and db = scale sum_n G,
+    logits computed once per block of rows (page "Cutting LLM Memory by 84%",
+    "Fused Linear Cross-Entropy": the chain rule through the linear layer)."""
+    x, w, bias = to_f64(x), to_f64(w), to_f64(bias)
+    targets = np.asarray(targets)
+    check_targets(targets, w.shape[0], opts)
+    n, d = x.shape
+    v = w.shape[0]
+    valid = valid_rows(targets, opts)
+    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    scale = grad_scale(opts, nv, grad_output)
+    lse = np.zeros(n)
+    rl = np.zeros(n)
+    dx = np.zeros((n, d))
+    dw = np.zeros((v, d)) if want_dw else None
+    db = np.zeros(v)
+    for r0 in range(0, n, row_block):
+        sl = slice(r0, min(n, r0 + row_block))
+        z = logits(x[sl], w, bias, opts.softcap)
+        l = log_sum_exp(z)
+        rl[sl] = row_losses(z, l, targets[sl], opts)
+        lse[sl] = np.where(valid[sl], l, 0.0)
+        g = grad_logits(z, l, targets[sl], opts) * scale
+        dx[sl] = g @ w
+        if want_dw:
+            dw += g.T @ x[sl]
+        db += g.sum(axis=0)
+    return Result(reduce_loss(rl, nv, opts), lse, rl, nv, dx, dw, db)
+
+
+def dw_blocks(x, w, bias, targets, opts: LossOptions, grad_output: float = 1.0,
+              n_valid: Optional[int] = None, vocab_block: int = 16384
+              ) -> Iterator[Tuple[int, int, np.ndarray]]:
+    """dW streamed by vocabulary blocks (v0, v1, dW[v0:v1]) so a large fp64
+    weight gradient is never held whole.  Same arithmetic as
+    ``forward_backward``; the LSE is taken over the full vocabulary first."""
+    x, w, bias = to_f64(x), to_f64(w), to_f64(bias)
+    targets = np.asarray(targets)
+    valid = valid_rows(targets, opts)
+    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    scale = grad_scale(opts, nv, grad_output)
+    v = w.shape[0]
+    z = logits(x, w, bias, opts.softcap)
+    l = log_sum_exp(z)
+    g = grad_logits(z, l, targets, opts) * scale
+    del z
+    for v0 in range(0, v, vocab_block):
+        v1 = min(v, v0 + vocab_block)
+        yield v0, v1, g[:, v0:v1].T @ x
