@@ -1,0 +1,156 @@
+/*
+ * flce.h - fused linear cross-entropy (FLCE) for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libflce.so.  The library computes, for hidden states X [N, D],
+ * an LM-head weight W [V, D] (nn.Linear layout, i.e. the logical [D, V]
+ * matrix of the page "Cutting LLM Memory by 84%: A Deep Dive into Fused
+ * Kernels", section "The Logit Bottleneck", stored transposed), an optional
+ * bias b [V] and int32 targets t [N]:
+ *
+ *   r     = X W^T + b                       (logits, never stored)
+ *   z     = c tanh(r / c)   if softcap c > 0, else r
+ *   lse_n = log sum_v exp(z_nv)
+ *   row_n = lse_n - (1-eps) z_{n,t_n} - (eps/V) sum_v z_nv + s lse_n^2
+ *   loss  = sum over valid rows of row_n, divided by n_valid for 'mean'
+ *
+ * Rows with t_n == ignore_index are not valid: their loss and lse are 0 and
+ * their gradient rows are 0 (page "Cutting LLM Memory by 84%", "Kernel
+ * Implementation", step 1).  The backward recomputes softmax tiles from the
+ * saved LSE and forms G = [softmax(z)(1 + 2 s lse) - (1-eps) onehot - eps/V]
+ * (times 1 - (z/c)^2 under the softcap), then dX = scale G W and
+ * dW = scale G^T X, db = scale sum_n G, with scale = g / n_valid ('mean') or g
+ * ('sum') for the upstream gradient g (same page, "Backward Pass" and
+ * "Fused Linear Cross-Entropy"; the option set follows the page
+ * "[CuteDSL] FLCE: 2-SM online-softmax fast path (Blackwell)", Summary).
+ * No [N, V] buffer is ever allocated: the forward keeps only per-row
+ * online-softmax partials, the backward works one vocabulary slice at a time.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are plain HIP device addresses; the caller owns every
+ *    buffer, including the workspace.  The library never allocates or frees
+ *    device memory and never synchronises, except flce_check_status().
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    runs asynchronously; results are valid once that stream has reached the
+ *    end of the call.
+ *  - Tensors are dense row-major.  X, W, dX, bias must be 16-byte aligned;
+ *    D must be a multiple of 8.  N and V are arbitrary (ragged tails are
+ *    handled in the kernels).  N, D, V must be below 2^31.
+ *  - Element type of X, W, bias and dX is params->dtype (bf16 or fp32).
+ *    Loss, lse, row_loss, dW and db are always fp32.  Accumulation is fp32.
+ *  - Every argument is validated on the host before any HIP call, so invalid
+ *    calls return an error without touching the GPU.  Nothing aborts or
+ *    throws across this interface.
+ *  - Results are deterministic: every reduction has a fixed order, and there
+ *    are no global atomics.
+ *  - Concurrent calls that share a workspace race; give each in-flight call
+ *    its own workspace.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flce_status {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARGUMENT = 1,   /* bad size, pointer, alignment or option */
+  FLCE_ERR_UNSUPPORTED = 2,        /* reduction NONE with a backward; device is not gfx950 */
+  FLCE_ERR_WORKSPACE_TOO_SMALL = 3,
+  FLCE_ERR_TARGET_OUT_OF_RANGE = 4,/* a target outside [0, V) that is not ignore_index
+                                      (reported by flce_check_status) */
+  FLCE_ERR_DEVICE = 5              /* a HIP call or kernel launch failed */
+} flce_status;
+
+typedef enum flce_dtype {
+  FLCE_DTYPE_BF16 = 0,
+  FLCE_DTYPE_F32 = 1
+} flce_dtype;
+
+typedef enum flce_reduction {
+  FLCE_REDUCTION_MEAN = 0,         /* sum of valid row losses / n_valid (0 if n_valid == 0) */
+  FLCE_REDUCTION_SUM = 1,
+  FLCE_REDUCTION_NONE = 2          /* per-row losses; forward only */
+} flce_reduction;
+
+typedef struct flce_params {
+  int64_t n;                 /* tokens (rows of X), >= 0 */
+  int64_t d;                 /* hidden size, > 0, multiple of 8 */
+  int64_t v;                 /* vocabulary size, > 0 */
+  int32_t dtype;             /* flce_dtype of X, W, bias and dX */
+  int32_t ignore_index;      /* rows with this target are skipped (usually -100) */
+  float label_smoothing;     /* eps in [0, 1] */
+  float lse_square_scale;    /* z-loss weight s >= 0 */
+  float softcap;             /* c; 0 = off, > 0 caps logits to (-c, c) */
+  int32_t reduction;         /* flce_reduction */
+  int32_t vocab_slice;       /* backward vocabulary slice width; 0 = library default.
+                                Rounded up to a multiple of 256. */
+} flce_params;
+
+/* Bytes of workspace the calls need for these parameters.  with_backward = 0
+ * sizes flce_forward only; 1 sizes flce_backward and flce_fused_fwd_bwd (and
+ * also covers flce_forward).  Returns 0 for invalid parameters.  The size is
+ * O(N (V/1024 + D) + N * vocab_slice), far below the N x V logits. */
+size_t flce_workspace_size(const flce_params* params, int with_backward);
+
+/* Forward: loss and per-row LSE.
+ *  x        [n, d] dtype          w   [v, d] dtype        bias [v] dtype or NULL
+ *  targets  [n] int32
+ *  loss     fp32 [1] for MEAN/SUM, fp32 [n] (per-row losses) for NONE
+ *  lse      fp32 [n], required: log-sum-exp of each valid row, 0 on ignored rows
+ *           (flce_backward needs it)
+ *  row_loss fp32 [n] or NULL: per-row losses (0 on ignored rows)
+ *  ws       workspace of at least flce_workspace_size(params, 0) bytes,
+ *           256-byte aligned
+ * Targets are range-checked on the device; call flce_check_status to read the
+ * result. */
+flce_status flce_forward(const flce_params* params, const void* x, const void* w,
+                         const void* bias, const int32_t* targets, float* loss,
+                         float* lse, float* row_loss, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Backward from the saved LSE (page "[CuteDSL] FLCE", Summary: the backward
+ * recomputes the masked softmax tile by tile over the vocabulary; dW is
+ * contracted over all tokens and written once per vocabulary slice).
+ *  lse          fp32 [n] from flce_forward with the same inputs and options
+ *  grad_output  fp32 [1] device scalar g (d total / d loss), or NULL for 1.0
+ *  dx           [n, d] dtype, overwritten
+ *  dw           fp32 [v, d], overwritten
+ *  dbias        fp32 [v], overwritten; may be NULL only when bias is NULL
+ *  ws           at least flce_workspace_size(params, 1) bytes
+ * reduction NONE returns FLCE_ERR_UNSUPPORTED (a per-token upstream gradient
+ * cannot be folded into the vocabulary-sliced weight-gradient contraction). */
+flce_status flce_backward(const flce_params* params, const void* x, const void* w,
+                          const void* bias, const int32_t* targets, const float* lse,
+                          const float* grad_output, void* dx, float* dw, float* dbias,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Forward and backward in one call with grad_output = 1.0 (the fwd+bwd
+ * benchmark convention of the page "[CuteDSL] FLCE", Benchmarks).  Outputs as
+ * in flce_forward and flce_backward; lse is still required (it is written and
+ * then consumed).  reduction NONE returns FLCE_ERR_UNSUPPORTED. */
+flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const void* w,
+                               const void* bias, const int32_t* targets, float* loss,
+                               float* lse, void* dx, float* dw, float* dbias, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Synchronises `stream`, then reports the device-side target check of the
+ * last call that used this workspace: FLCE_OK or FLCE_ERR_TARGET_OUT_OF_RANGE
+ * (FLCE_ERR_DEVICE if the synchronisation or copy fails).  When it reports an
+ * out-of-range target, that call's numeric results are undefined. */
+flce_status flce_check_status(const void* ws, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* flce_status_string(flce_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int flce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

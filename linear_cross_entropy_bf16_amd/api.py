@@ -1,0 +1,194 @@
+"""PyTorch-facing API of the fused linear cross-entropy.
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream, every step of the computation runs in libflce.so.  Tensors must live
+on a ROCm GPU; there is no CPU path.
+
+    loss = linear_cross_entropy(x, weight, target, bias=None, ignore_index=-100,
+                                label_smoothing=0.0, lse_square_scale=0.0,
+                                softcap=0.0, reduction="mean")
+
+``weight`` is the LM-head matrix in nn.Linear layout [V, D]; ``x`` is [..., D]
+(leading dimensions are flattened into tokens); ``target`` holds class ids with
+the same leading shape.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.DTYPE_BF16, torch.float32: _lib.DTYPE_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != _lib.FLCE_OK:
+        raise _lib.FLCEError(status, what)
+
+
+def _prepare(x, weight, target, bias):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a tensor on a ROCm GPU (device 'cuda')")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    if weight.dtype != x.dtype or (bias is not None and bias.dtype != x.dtype):
+        raise TypeError("x, weight and bias must share one dtype")
+    if weight.dim() != 2 or weight.shape[1] != x.shape[-1]:
+        raise ValueError(f"weight must be [V, D] with D = x.shape[-1]; got {tuple(weight.shape)}")
+    dev = x.device
+    for name, t in (("weight", weight), ("target", target), ("bias", bias)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, x on {dev}")
+    d = x.shape[-1]
+    x2 = x.reshape(-1, d).contiguous()
+    t2 = target.reshape(-1)
+    if t2.numel() != x2.shape[0]:
+        raise ValueError("target must have one entry per row of x")
+    t2 = t2.to(torch.int32).contiguous()
+    w2 = weight.contiguous()
+    b2 = bias.contiguous() if bias is not None else None
+    if b2 is not None and b2.shape != (w2.shape[0],):
+        raise ValueError("bias must be [V]")
+    return x2, w2, t2, b2
+
+
+def make_params(n, d, v, dtype, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0,
+                softcap=0.0, reduction="mean", vocab_slice=0) -> _lib.Params:
+    return _lib.make_params(n, d, v, _DTYPES[dtype], ignore_index, label_smoothing,
+                            lse_square_scale, softcap, reduction, vocab_slice)
+
+
+def workspace_bytes(n, d, v, dtype=torch.bfloat16, with_backward=True, **opts) -> int:
+    return _lib.workspace_size(make_params(n, d, v, dtype, **opts), with_backward)
+
+
+def _workspace(params, with_backward, device) -> Tuple[torch.Tensor, int]:
+    nbytes = _lib.workspace_size(params, with_backward)
+    if nbytes == 0:
+        raise _lib.FLCEError(_lib.FLCE_ERR_INVALID_ARGUMENT, "workspace size")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def forward(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
+            lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
+            check_targets=False):
+    """Returns (loss, lse, row_loss): loss is a 0-d tensor ([N] for 'none'),
+    lse and row_loss are fp32 [N]."""
+    x2, w2, t2, b2 = _prepare(x, weight, target, bias)
+    n, d = x2.shape
+    v = w2.shape[0]
+    p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
+                    reduction, vocab_slice)
+    dev = x2.device
+    ws, nbytes = _workspace(p, False, dev)
+    loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(n, dtype=torch.float32, device=dev)
+    st = _stream(dev)
+    _check(_lib.forward(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(loss), _ptr(lse),
+                        _ptr(row_loss), _ptr(ws), nbytes, st), "flce_forward")
+    if check_targets:
+        _check(_lib.check_status(_ptr(ws), st), "target check")
+    return (loss if reduction == "none" else loss[0]), lse, row_loss
+
+
+def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_index=-100,
+             label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0, reduction="mean",
+             vocab_slice=0):
+    """Returns (dx, dw, db): dx in x's dtype, dw and db fp32 (db None without
+    bias).  grad_output is a device scalar (None = 1.0)."""
+    x2, w2, t2, b2 = _prepare(x, weight, target, bias)
+    n, d = x2.shape
+    v = w2.shape[0]
+    p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
+                    reduction, vocab_slice)
+    dev = x2.device
+    ws, nbytes = _workspace(p, True, dev)
+    g = None
+    if grad_output is not None:
+        g = grad_output.detach().reshape(1).to(device=dev, dtype=torch.float32).contiguous()
+    lse = lse.detach().to(torch.float32).contiguous()
+    dx = torch.empty((n, d), dtype=x2.dtype, device=dev)
+    dw = torch.empty((v, d), dtype=torch.float32, device=dev)
+    db = torch.empty(v, dtype=torch.float32, device=dev) if b2 is not None else None
+    _check(_lib.backward(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(lse), _ptr(g), _ptr(dx),
+                         _ptr(dw), _ptr(db), _ptr(ws), nbytes, _stream(dev)), "flce_backward")
+    return dx.reshape(x.shape), dw, db
+
+
+def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
+                  lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
+                  workspace: Optional[torch.Tensor] = None, out=None):
+    """One call computing (loss, lse, dx, dw, db) with grad_output = 1.
+    ``workspace`` and ``out`` (a tuple of preallocated loss, lse, dx, dw, db)
+    let a caller reuse buffers across steps."""
+    x2, w2, t2, b2 = _prepare(x, weight, target, bias)
+    n, d = x2.shape
+    v = w2.shape[0]
+    p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
+                    reduction, vocab_slice)
+    dev = x2.device
+    nbytes = _lib.workspace_size(p, True)
+    if workspace is None:
+        workspace, nbytes = _workspace(p, True, dev)
+    elif workspace.numel() < nbytes:
+        raise _lib.FLCEError(_lib.FLCE_ERR_WORKSPACE_TOO_SMALL, "fused_fwd_bwd")
+    else:
+        nbytes = workspace.numel()
+    if out is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+        dx = torch.empty((n, d), dtype=x2.dtype, device=dev)
+        dw = torch.empty((v, d), dtype=torch.float32, device=dev)
+        db = torch.empty(v, dtype=torch.float32, device=dev) if b2 is not None else None
+    else:
+        loss, lse, dx, dw, db = out
+    _check(_lib.fused_fwd_bwd(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(loss), _ptr(lse),
+                              _ptr(dx), _ptr(dw), _ptr(db), _ptr(workspace), nbytes, _stream(dev)),
+           "flce_fused_fwd_bwd")
+    return loss[0], lse, dx, dw, db
+
+
+class LinearCrossEntropyFunction(torch.autograd.Function):
+    """Autograd wrapper: the forward keeps only the per-row LSE; the backward
+    recomputes the softmax from it inside the library."""
+
+    @staticmethod
+    def forward(ctx, x, weight, target, bias, ignore_index, label_smoothing, lse_square_scale,
+                softcap, reduction):
+        loss, lse, _ = forward(x, weight, target, bias, ignore_index=ignore_index,
+                               label_smoothing=label_smoothing, lse_square_scale=lse_square_scale,
+                               softcap=softcap, reduction=reduction)
+        ctx.save_for_backward(x, weight, target, bias, lse)
+        ctx.opts = dict(ignore_index=ignore_index, label_smoothing=label_smoothing,
+                        lse_square_scale=lse_square_scale, softcap=softcap, reduction=reduction)
+        ctx.mark_non_differentiable(lse)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        x, weight, target, bias, lse = ctx.saved_tensors
+        if ctx.opts["reduction"] == "none":
+            raise RuntimeError("reduction='none' has no backward in the fused kernel; "
+                               "use 'mean' or 'sum'")
+        dx, dw, db = backward(x, weight, target, lse, grad_output=grad_loss, bias=bias, **ctx.opts)
+        return (dx.to(x.dtype), dw.to(weight.dtype), None,
+                db.to(bias.dtype) if db is not None else None, None, None, None, None, None)
+
+
+def linear_cross_entropy(x, weight, target, bias=None, ignore_index=-100, label_smoothing=0.0,
+                         lse_square_scale=0.0, softcap=0.0, reduction="mean"):
+    """Fused LM-head projection + cross-entropy; differentiable in x, weight
+    and bias (reduction 'mean' or 'sum'; 'none' is forward-only)."""
+    return LinearCrossEntropyFunction.apply(x, weight, target, bias, ignore_index, label_smoothing,
+                                            lse_square_scale, softcap, reduction)

@@ -1,0 +1,432 @@
+// libflce.so: host side of the C ABI declared in include/flce.h.
+//
+// Validation happens entirely on the host before the first HIP call; then the
+// kernels of flce_kernels.hpp are enqueued on the caller's stream in a fixed
+// sequence.  The library allocates nothing: every buffer, the workspace
+// included, belongs to the caller.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <type_traits>
+
+#include "flce.h"
+#include "flce_kernels.hpp"
+
+namespace {
+
+using flce::Ctl;
+namespace tile = flce::tile;
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kDefaultSlice = 8192;    // backward vocabulary slice width
+constexpr int64_t kDbSplits = 64;          // token blocks of the bias-gradient column sums
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ----------------------------------------------------------------- layout
+struct Layout {
+  int64_t elem;           // bytes per X/W element
+  int64_t v_tiles, n_tiles, tiles_per_chunk, n_chunks;
+  int64_t slice, ldg;     // backward slice width (multiple of 256) and G row pitch
+  int64_t n_merge_blocks;
+  // byte offsets from the workspace base
+  int64_t ctl, zt, part_m, part_d, part_s, block_sums, fwd_end;
+  int64_t g, dx_acc, db_part, bwd_end;
+};
+
+Layout make_layout(const flce_params& p) {
+  Layout L{};
+  L.elem = p.dtype == FLCE_DTYPE_BF16 ? 2 : 4;
+  L.v_tiles = cdiv(p.v, tile::kM);
+  L.n_tiles = cdiv(p.n, tile::kN);
+  // Enough workgroups to fill 256 CUs several times over, and at most 8
+  // vocabulary tiles per workgroup so the partials stay small.
+  const int64_t tiles = L.v_tiles * L.n_tiles;
+  int64_t tpc = tiles / 2048;
+  tpc = tpc < 1 ? 1 : (tpc > 8 ? 8 : tpc);
+  L.tiles_per_chunk = tpc;
+  L.n_chunks = cdiv(L.v_tiles, tpc);
+  const int64_t slice_req = p.vocab_slice > 0 ? p.vocab_slice : kDefaultSlice;
+  L.slice = round_up(slice_req < p.v ? slice_req : p.v, tile::kM);
+  L.ldg = L.slice;
+  L.n_merge_blocks = cdiv(p.n, 256);
+
+  int64_t off = 0;
+  L.ctl = off;
+  off += kAlign;
+  const int64_t base = off;
+  L.zt = off;          off = round_up(off + 4 * p.n, kAlign);
+  L.part_m = off;      off = round_up(off + 4 * p.n * L.n_chunks, kAlign);
+  L.part_d = off;      off = round_up(off + 4 * p.n * L.n_chunks, kAlign);
+  L.part_s = off;      off = round_up(off + 4 * p.n * L.n_chunks, kAlign);
+  L.block_sums = off;  off = round_up(off + 8 * L.n_merge_blocks, kAlign);
+  L.fwd_end = off;
+  // Backward region reuses the forward region (the forward's scratch is dead
+  // once its loss is reduced).
+  off = base;
+  L.g = off;           off = round_up(off + L.elem * p.n * L.ldg, kAlign);
+  const bool multi_slice = L.slice < p.v;
+  L.dx_acc = off;
+  if (p.dtype == FLCE_DTYPE_BF16 && multi_slice) off = round_up(off + 4 * p.n * p.d, kAlign);
+  L.db_part = off;     off = round_up(off + 4 * kDbSplits * L.ldg, kAlign);
+  L.bwd_end = off;
+  return L;
+}
+
+// ----------------------------------------------------------------- checks
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+flce_status check_params(const flce_params* p) {
+  if (!p) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->n < 0 || p->n > kMaxDim) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->d <= 0 || p->d > kMaxDim || p->d % 8 != 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->v <= 0 || p->v > kMaxDim) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->dtype != FLCE_DTYPE_BF16 && p->dtype != FLCE_DTYPE_F32) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->reduction != FLCE_REDUCTION_MEAN && p->reduction != FLCE_REDUCTION_SUM &&
+      p->reduction != FLCE_REDUCTION_NONE)
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (!(p->label_smoothing >= 0.f && p->label_smoothing <= 1.f)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!(p->lse_square_scale >= 0.f) || !std::isfinite(p->lse_square_scale))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (!(p->softcap >= 0.f) || !std::isfinite(p->softcap)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->vocab_slice < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  // byte sizes of the largest tensors must fit comfortably in int64
+  const double big = static_cast<double>(p->n) * static_cast<double>(p->v) + p->n * (double)p->d +
+                     p->v * (double)p->d;
+  if (big > 1e17) return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+flce_status check_inputs(const flce_params& p, const void* x, const void* w, const void* bias,
+                         const int32_t* targets) {
+  if (!w || !aligned(w, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p.n > 0 && (!x || !aligned(x, 16) || !targets || !aligned(targets, 4)))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  if (bias && !aligned(bias, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+flce_status check_ws(const void* ws, size_t ws_bytes, int64_t need) {
+  if (!ws || !aligned(ws, kAlign)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (static_cast<int64_t>(ws_bytes) < need) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  return FLCE_OK;
+}
+
+// The kernels are gfx950 code objects only.
+flce_status check_device() {
+  static int known[64];   // 0 unknown, 1 gfx950, 2 other
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_DEVICE;
+  if (dev >= 0 && dev < 64 && known[dev]) return known[dev] == 1 ? FLCE_OK : FLCE_ERR_UNSUPPORTED;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FLCE_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) known[dev] = ok ? 1 : 2;
+  return ok ? FLCE_OK : FLCE_ERR_UNSUPPORTED;
+}
+
+flce_status launched() { return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_DEVICE; }
+
+char* at(void* ws, int64_t off) { return static_cast<char*>(ws) + off; }
+
+void fill(float* p, int64_t count, float value, hipStream_t s) {
+  if (count <= 0) return;
+  hipLaunchKernelGGL(flce::k_fill, dim3(static_cast<unsigned>(cdiv(count, 256))), dim3(256), 0, s,
+                     p, count, value);
+}
+
+int64_t grid8(int64_t tiles) { return round_up(tiles, 8); }
+
+// ----------------------------------------------------------------- forward
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ>
+void launch_fwd(const flce::FwdArgs<T>& a, hipStream_t s) {
+  hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ>), dim3(static_cast<unsigned>(a.grid)),
+                     dim3(tile::kThreads), 0, s, a);
+}
+
+template <typename T>
+flce_status run_forward(const flce_params& p, const Layout& L, const void* x, const void* w,
+                        const void* bias, const int32_t* targets, float* loss, float* lse,
+                        float* row_loss, void* ws, hipStream_t s) {
+  Ctl* ctl = reinterpret_cast<Ctl*>(at(ws, L.ctl));
+  const bool mean = p.reduction == FLCE_REDUCTION_MEAN;
+  hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
+                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl);
+  if (p.n == 0) {
+    if (p.reduction != FLCE_REDUCTION_NONE) fill(loss, 1, 0.f, s);
+    return launched();
+  }
+  flce::FwdArgs<T> a{};
+  a.x = static_cast<const T*>(x);
+  a.w = static_cast<const T*>(w);
+  a.bias = static_cast<const T*>(bias);
+  a.targets = targets;
+  a.n = p.n;
+  a.d = p.d;
+  a.v = p.v;
+  a.softcap = p.softcap;
+  a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
+  a.n_tiles = L.n_tiles;
+  a.v_tiles = L.v_tiles;
+  a.n_chunks = L.n_chunks;
+  a.tiles_per_chunk = L.tiles_per_chunk;
+  a.grid = grid8(L.n_tiles * L.n_chunks);
+  a.part_m = reinterpret_cast<float*>(at(ws, L.part_m));
+  a.part_d = reinterpret_cast<float*>(at(ws, L.part_d));
+  a.part_s = reinterpret_cast<float*>(at(ws, L.part_s));
+  a.zt = reinterpret_cast<float*>(at(ws, L.zt));
+  const bool b = bias != nullptr, c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
+  const int key = (b ? 1 : 0) | (c ? 2 : 0) | (z ? 4 : 0);
+  switch (key) {
+    case 0: launch_fwd<T, false, false, false>(a, s); break;
+    case 1: launch_fwd<T, true, false, false>(a, s); break;
+    case 2: launch_fwd<T, false, true, false>(a, s); break;
+    case 3: launch_fwd<T, true, true, false>(a, s); break;
+    case 4: launch_fwd<T, false, false, true>(a, s); break;
+    case 5: launch_fwd<T, true, false, true>(a, s); break;
+    case 6: launch_fwd<T, false, true, true>(a, s); break;
+    default: launch_fwd<T, true, true, true>(a, s); break;
+  }
+  flce::MergeArgs m{};
+  m.part_m = a.part_m;
+  m.part_d = a.part_d;
+  m.part_s = a.part_s;
+  m.zt = a.zt;
+  m.targets = targets;
+  m.n = p.n;
+  m.v = p.v;
+  m.n_chunks = L.n_chunks;
+  m.ignore_index = p.ignore_index;
+  m.keep_target = 1.0f - p.label_smoothing;
+  m.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
+  m.zloss = p.lse_square_scale;
+  m.lse = lse;
+  m.row_loss = row_loss;
+  m.loss_rows = p.reduction == FLCE_REDUCTION_NONE ? loss : nullptr;
+  m.block_sums = reinterpret_cast<double*>(at(ws, L.block_sums));
+  hipLaunchKernelGGL(flce::k_merge, dim3(static_cast<unsigned>(L.n_merge_blocks)), dim3(256), 0, s, m);
+  if (p.reduction != FLCE_REDUCTION_NONE)
+    hipLaunchKernelGGL(flce::k_loss_final, dim3(1), dim3(256), 0, s, m.block_sums, L.n_merge_blocks,
+                       static_cast<const Ctl*>(ctl), mean ? 1 : 0, loss);
+  return launched();
+}
+
+// ----------------------------------------------------------------- backward
+template <typename T, bool kBias, bool kSoftcap>
+void launch_g(const flce::GArgs<T>& a, hipStream_t s) {
+  hipLaunchKernelGGL((flce::k_bwd_g<T, kBias, kSoftcap>), dim3(static_cast<unsigned>(a.grid)),
+                     dim3(tile::kThreads), 0, s, a);
+}
+
+template <typename T>
+flce_status run_backward(const flce_params& p, const Layout& L, const void* x, const void* w,
+                         const void* bias, const int32_t* targets, const float* lse,
+                         const float* grad_output, void* dx, float* dw, float* dbias, void* ws,
+                         hipStream_t s) {
+  Ctl* ctl = reinterpret_cast<Ctl*>(at(ws, L.ctl));
+  const bool mean = p.reduction == FLCE_REDUCTION_MEAN;
+  hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
+                     grad_output, mean ? 1 : 0, ctl);
+  T* g = reinterpret_cast<T*>(at(ws, L.g));
+  float* dx_acc = std::is_same<T, float>::value ? static_cast<float*>(dx)
+                                                : reinterpret_cast<float*>(at(ws, L.dx_acc));
+  float* db_part = reinterpret_cast<float*>(at(ws, L.db_part));
+  const int64_t n_slices = cdiv(p.v, L.slice);
+  const int64_t d_tiles = cdiv(p.d, tile::kM);
+  const bool has_bias = bias != nullptr;
+  for (int64_t si = 0; si < n_slices; ++si) {
+    const int64_t v0 = si * L.slice;
+    const int64_t len = (p.v - v0) < L.slice ? (p.v - v0) : L.slice;
+    const int64_t s_tiles = cdiv(len, tile::kM);
+    const int64_t gcols = s_tiles * tile::kM;
+    if (p.n > 0) {
+      flce::GArgs<T> ga{};
+      ga.x = static_cast<const T*>(x);
+      ga.w = static_cast<const T*>(w);
+      ga.bias = static_cast<const T*>(bias);
+      ga.targets = targets;
+      ga.lse = lse;
+      ga.n = p.n;
+      ga.d = p.d;
+      ga.v = p.v;
+      ga.ignore_index = p.ignore_index;
+      ga.softcap = p.softcap;
+      ga.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
+      ga.keep_target = 1.0f - p.label_smoothing;
+      ga.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
+      ga.two_s = 2.0f * p.lse_square_scale;
+      ga.v0 = v0;
+      ga.slice_len = len;
+      ga.ldg = L.ldg;
+      ga.g = g;
+      ga.n_tiles = L.n_tiles;
+      ga.s_tiles = s_tiles;
+      ga.grid = grid8(L.n_tiles * s_tiles);
+      const int key = (has_bias ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
+      switch (key) {
+        case 0: launch_g<T, false, false>(ga, s); break;
+        case 1: launch_g<T, true, false>(ga, s); break;
+        case 2: launch_g<T, false, true>(ga, s); break;
+        default: launch_g<T, true, true>(ga, s); break;
+      }
+    }
+    flce::DwArgs<T> wa{};
+    wa.x = static_cast<const T*>(x);
+    wa.g = g;
+    wa.n = p.n;
+    wa.d = p.d;
+    wa.v0 = v0;
+    wa.slice_len = len;
+    wa.ldg = L.ldg;
+    wa.gcols = gcols;
+    wa.ctl = ctl;
+    wa.dw = dw;
+    wa.d_tiles = d_tiles;
+    wa.s_tiles = s_tiles;
+    wa.grid = grid8(d_tiles * s_tiles);
+    hipLaunchKernelGGL((flce::k_dw<T>), dim3(static_cast<unsigned>(wa.grid)), dim3(tile::kThreads), 0,
+                       s, wa);
+    if (p.n > 0) {
+      flce::DxArgs<T> xa{};
+      xa.w = static_cast<const T*>(w);
+      xa.g = g;
+      xa.n = p.n;
+      xa.d = p.d;
+      xa.v = p.v;
+      xa.v0 = v0;
+      xa.kdim = gcols;
+      xa.ldg = L.ldg;
+      xa.ctl = ctl;
+      xa.acc_buf = dx_acc;
+      xa.dx = static_cast<T*>(dx);
+      xa.first = si == 0;
+      xa.last = si + 1 == n_slices;
+      xa.d_tiles = d_tiles;
+      xa.n_tiles = L.n_tiles;
+      xa.grid = grid8(d_tiles * L.n_tiles);
+      hipLaunchKernelGGL((flce::k_dx<T>), dim3(static_cast<unsigned>(xa.grid)), dim3(tile::kThreads),
+                         0, s, xa);
+    }
+    if (has_bias) {
+      const int64_t rps = cdiv(p.n > 0 ? p.n : 1, kDbSplits);
+      hipLaunchKernelGGL((flce::k_db_partial<T>), dim3(static_cast<unsigned>(cdiv(gcols, 256)),
+                                                       static_cast<unsigned>(kDbSplits)),
+                         dim3(256), 0, s, static_cast<const T*>(g), p.n, L.ldg, gcols, rps, db_part);
+      hipLaunchKernelGGL(flce::k_db_final, dim3(static_cast<unsigned>(cdiv(len, 256))), dim3(256), 0, s,
+                         static_cast<const float*>(db_part), kDbSplits, gcols, v0, len,
+                         static_cast<const Ctl*>(ctl), dbias);
+    }
+  }
+  return launched();
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+size_t flce_workspace_size(const flce_params* params, int with_backward) {
+  if (check_params(params) != FLCE_OK) return 0;
+  const Layout L = make_layout(*params);
+  const int64_t need = with_backward ? (L.bwd_end > L.fwd_end ? L.bwd_end : L.fwd_end) : L.fwd_end;
+  return static_cast<size_t>(need);
+}
+
+flce_status flce_forward(const flce_params* params, const void* x, const void* w, const void* bias,
+                         const int32_t* targets, float* loss, float* lse, float* row_loss, void* ws,
+                         size_t ws_bytes, void* stream) {
+  flce_status st = check_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if ((st = check_inputs(p, x, w, bias, targets)) != FLCE_OK) return st;
+  if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p.n > 0 && (!lse || !aligned(lse, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (row_loss && !aligned(row_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  const Layout L = make_layout(p);
+  if ((st = check_ws(ws, ws_bytes, L.fwd_end)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16)
+    return run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s);
+  return run_forward<float>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s);
+}
+
+static flce_status check_backward_args(const flce_params& p, const Layout& L, const float* lse,
+                                       void* dx, float* dw, float* dbias, const void* bias,
+                                       const void* ws, size_t ws_bytes) {
+  if (p.reduction == FLCE_REDUCTION_NONE) return FLCE_ERR_UNSUPPORTED;
+  if (p.n > 0 && (!lse || !aligned(lse, 4) || !dx || !aligned(dx, 16))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!dw || !aligned(dw, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (bias && (!dbias || !aligned(dbias, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  const int64_t need = L.bwd_end > L.fwd_end ? L.bwd_end : L.fwd_end;
+  return check_ws(ws, ws_bytes, need);
+}
+
+flce_status flce_backward(const flce_params* params, const void* x, const void* w, const void* bias,
+                          const int32_t* targets, const float* lse, const float* grad_output, void* dx,
+                          float* dw, float* dbias, void* ws, size_t ws_bytes, void* stream) {
+  flce_status st = check_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if ((st = check_inputs(p, x, w, bias, targets)) != FLCE_OK) return st;
+  if (grad_output && !aligned(grad_output, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  const Layout L = make_layout(p);
+  if ((st = check_backward_args(p, L, lse, dx, dw, dbias, bias, ws, ws_bytes)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16)
+    return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, s);
+  return run_backward<float>(p, L, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, s);
+}
+
+flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const void* w,
+                               const void* bias, const int32_t* targets, float* loss, float* lse,
+                               void* dx, float* dw, float* dbias, void* ws, size_t ws_bytes,
+                               void* stream) {
+  flce_status st = check_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if ((st = check_inputs(p, x, w, bias, targets)) != FLCE_OK) return st;
+  if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  const Layout L = make_layout(p);
+  if ((st = check_backward_args(p, L, lse, dx, dw, dbias, bias, ws, ws_bytes)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16) {
+    st = run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
+    if (st != FLCE_OK) return st;
+    return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s);
+  }
+  st = run_forward<float>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
+  if (st != FLCE_OK) return st;
+  return run_backward<float>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s);
+}
+
+flce_status flce_check_status(const void* ws, void* stream) {
+  if (!ws || !aligned(ws, kAlign)) return FLCE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return FLCE_ERR_DEVICE;
+  Ctl host{};
+  if (hipMemcpy(&host, ws, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return FLCE_ERR_DEVICE;
+  return host.status ? FLCE_ERR_TARGET_OUT_OF_RANGE : FLCE_OK;
+}
+
+const char* flce_status_string(flce_status status) {
+  switch (status) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FLCE_ERR_UNSUPPORTED: return "unsupported";
+    case FLCE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FLCE_ERR_TARGET_OUT_OF_RANGE: return "target out of range";
+    case FLCE_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+int flce_version(void) { return 100; }
+
+}  // extern "C"

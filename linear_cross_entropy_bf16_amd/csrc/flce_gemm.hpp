@@ -1,0 +1,260 @@
+// MFMA tile engine shared by the four contractions of the fused linear
+// cross-entropy (forward logits, recomputed logits, dW and dX).
+//
+// C[m, n] = sum_k A[m, k] * B[n, k] over one 256 x 256 output tile, fp32
+// accumulation, with either operand stored K-major (element (r, k) at
+// base[r * ld + k]) or MN-major (element (r, k) at base[k * ld + r]).  The
+// MN-major case is how the backward reads X and W "through a stride swap"
+// without ever materialising X^T or W^T (page "Cutting LLM Memory by 84%",
+// "Kernel Implementation", the stride-swap note): the 16-byte global loads
+// stay coalesced along the contiguous axis and an 8 x 8 register transpose
+// turns them into K-contiguous LDS rows, so every MFMA fragment read is one
+// 16-byte LDS read.
+//
+// Work split: 256 threads = 4 wave64s in a 2 x 2 grid, each wave owning a
+// 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (bf16) or
+// v_mfma_f32_32x32x2_f32 (fp32).  K advances in slabs of 128 bytes per row
+// (64 bf16 / 32 fp32), double-buffered in LDS (2 x 64 KiB) with the next
+// slab's global loads in flight while the current slab is multiplied.
+//
+// Accumulator layout (per lane l, block (mb, nb), register r in 0..15):
+//   row m = wm*128 + mb*32 + 8*(r/4) + 4*(l/32) + (r%4)
+//   col n = wn*128 + nb*32 + (l%32)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+namespace tile {
+constexpr int kThreads = 256;
+constexpr int kM = 256;                     // output tile rows
+constexpr int kN = 256;                     // output tile columns
+constexpr int kRowBytes = 128;              // one operand row of one K-slab
+constexpr int kOpBytes = kM * kRowBytes;    // one operand, one slab: 32 KiB
+constexpr int kStageBytes = 2 * kOpBytes;   // A + B
+constexpr int kLdsBytes = 2 * kStageBytes;  // double buffer: 128 KiB
+}  // namespace tile
+
+// Elements per 16-byte chunk.  bf16 is carried as raw uint16_t bits.
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> { static constexpr int n = 8; };
+template <> struct Vec<float> { static constexpr int n = 4; };
+
+template <typename T>
+constexpr int slab_k() { return tile::kRowBytes / (int)sizeof(T); }
+
+// LDS address of 16-byte chunk `chunk` (0..7) of tile row `row` (0..255).
+// The XOR swizzle spreads both the 8 rows read by consecutive lanes and the
+// 8 rows written by one transposing thread over all 8 chunk positions, so
+// 16-byte LDS reads and writes are free of bank conflicts.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * tile::kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+template <typename T, bool KMajor>
+struct Operand {
+  const T* base;
+  int64_t ld;   // elements between consecutive stored rows
+  int64_t mn;   // valid extent along M (or N); rows at or beyond it read as 0
+  int64_t k;    // valid extent along K; columns at or beyond it read as 0
+};
+
+// ---------------------------------------------------------------- loaders
+// K-major: thread t loads chunk (t % 8) of rows t/8 + 32 i, i = 0..7.
+// The extent along K must be a multiple of the chunk width (host-checked).
+template <typename T>
+__device__ __forceinline__ void load_slab(u32x4 (&r)[8], const Operand<T, true>& op,
+                                          int64_t mn0, int64_t k0, int tid) {
+  const int64_t k = k0 + (int64_t)(tid & 7) * Vec<T>::n;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = mn0 + (tid >> 3) + 32 * i;
+    if (row < op.mn && k < op.k)
+      r[i] = *reinterpret_cast<const u32x4*>(op.base + row * op.ld + k);
+    else
+      r[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_slab(char* s, const u32x4 (&r)[8],
+                                           const Operand<T, true>&, int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<u32x4*>(s + lds_off((tid >> 3) + 32 * i, tid & 7)) = r[i];
+}
+
+// MN-major bf16: thread t owns the 8 x 8 block of K rows 8 (t/32) .. +7 and
+// M columns 8 (t%32) .. +7; the M extent must be a multiple of 8.
+__device__ __forceinline__ void load_slab(u32x4 (&r)[8], const Operand<uint16_t, false>& op,
+                                          int64_t mn0, int64_t k0, int tid) {
+  const int64_t mn = mn0 + (int64_t)(tid & 31) * 8;
+  const int64_t kb = k0 + (int64_t)(tid >> 5) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t k = kb + i;
+    if (k < op.k && mn < op.mn)
+      r[i] = *reinterpret_cast<const u32x4*>(op.base + k * op.ld + mn);
+    else
+      r[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void store_slab(char* s, const u32x4 (&r)[8],
+                                           const Operand<uint16_t, false>&, int tid) {
+  const int kc = tid >> 5;       // K chunk of the slab
+  const int mb = tid & 31;       // 8-column group
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // column j of the block becomes tile row 8 mb + j
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = r[2 * q][j >> 1];      // K row 2q
+      const uint32_t hi = r[2 * q + 1][j >> 1];  // K row 2q + 1
+      o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    *reinterpret_cast<u32x4*>(s + lds_off(mb * 8 + j, kc)) = o;
+  }
+}
+
+// MN-major fp32: thread t owns two 4 x 4 blocks b = t and t + 256, each the
+// K rows 4 (b/64) .. +3 and M columns 4 (b%64) .. +3; M extent multiple of 4.
+__device__ __forceinline__ void load_slab(u32x4 (&r)[8], const Operand<float, false>& op,
+                                          int64_t mn0, int64_t k0, int tid) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = tid + 256 * h;
+    const int64_t mn = mn0 + (int64_t)(b & 63) * 4;
+    const int64_t kb = k0 + (int64_t)(b >> 6) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t k = kb + i;
+      if (k < op.k && mn < op.mn)
+        r[4 * h + i] = *reinterpret_cast<const u32x4*>(op.base + k * op.ld + mn);
+      else
+        r[4 * h + i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+__device__ __forceinline__ void store_slab(char* s, const u32x4 (&r)[8],
+                                           const Operand<float, false>&, int tid) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = tid + 256 * h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 o{r[4 * h][j], r[4 * h + 1][j], r[4 * h + 2][j], r[4 * h + 3][j]};
+      *reinterpret_cast<u32x4*>(s + lds_off((b & 63) * 4 + j, b >> 6)) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ void mma(f32x16& acc, const u32x4& a, const u32x4& b, uint16_t) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// fp32: the four floats of a chunk are four K steps of 32x32x2; A and B use
+// the same (chunk, element) -> k assignment, so the sum is the same.  (Each
+// element is copied to a scalar before the bit cast: a bit cast applied to a
+// vector-element expression directly reads element 0.)
+__device__ __forceinline__ void mma(f32x16& acc, const u32x4& a, const u32x4& b, float) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t ae = a[e], be = b[e];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ae), __uint_as_float(be), acc, 0, 0, 0);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void compute_slab(const char* sA, const char* sB, f32x16 (&acc)[4][4],
+                                             int wm, int wn, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int chunk = 2 * ks + (lane >> 5);
+    u32x4 fa[4], fb[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      fa[mb] = *reinterpret_cast<const u32x4*>(sA + lds_off(wm * 128 + mb * 32 + (lane & 31), chunk));
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      fb[nb] = *reinterpret_cast<const u32x4*>(sB + lds_off(wn * 128 + nb * 32 + (lane & 31), chunk));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) mma(acc[mb][nb], fa[mb], fb[nb], T{});
+  }
+}
+
+// One 256 x 256 output tile at (m0, n0), K = [0, K).  All 256 threads must
+// call it; it ends with a barrier, so `lds` is free again on return.
+template <typename T, bool AK, bool BK>
+__device__ __forceinline__ void gemm_tile(const Operand<T, AK>& A, const Operand<T, BK>& B,
+                                          int64_t m0, int64_t n0, int64_t K, char* lds,
+                                          f32x16 (&acc)[4][4]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+
+  constexpr int SK = slab_k<T>();
+  const int64_t nslab = (K + SK - 1) / SK;
+  u32x4 ra[8], rb[8];
+  load_slab(ra, A, m0, 0, tid);
+  load_slab(rb, B, n0, 0, tid);
+  store_slab(lds, ra, A, tid);
+  store_slab(lds + tile::kOpBytes, rb, B, tid);
+  __syncthreads();
+  for (int64_t s = 0; s < nslab; ++s) {
+    const bool more = s + 1 < nslab;
+    if (more) {
+      load_slab(ra, A, m0, (s + 1) * SK, tid);
+      load_slab(rb, B, n0, (s + 1) * SK, tid);
+    }
+    const char* cur = lds + (s & 1) * tile::kStageBytes;
+    compute_slab<T>(cur, cur + tile::kOpBytes, acc, wm, wn, lane);
+    if (more) {
+      char* nxt = lds + ((s + 1) & 1) * tile::kStageBytes;
+      store_slab(nxt, ra, A, tid);
+      store_slab(nxt + tile::kOpBytes, rb, B, tid);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- tile order
+// Workgroups are handed to the 8 XCDs round-robin by id.  Remap the id so each
+// XCD walks a contiguous range of logical tiles (grid is a multiple of 8).
+__device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t grid) {
+  const int64_t per = grid >> 3;
+  return (wg & 7) * per + (wg >> 3);
+}
+
+// Grouped raster: logical tile -> (a, b) with `group` consecutive a-tiles
+// sharing each b, so tiles in flight on one XCD reuse each other's panels.
+__device__ __forceinline__ void grouped(int64_t L, int64_t ta, int64_t tb, int64_t group,
+                                        int64_t& a, int64_t& b) {
+  const int64_t per_group = group * tb;
+  const int64_t g = L / per_group;
+  const int64_t in = L - g * per_group;
+  const int64_t a0 = g * group;
+  const int64_t gs = (ta - a0) < group ? (ta - a0) : group;
+  a = a0 + in % gs;
+  b = in / gs;
+}
+
+}  // namespace flce

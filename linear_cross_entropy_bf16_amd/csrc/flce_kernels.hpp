@@ -1,0 +1,550 @@
+// HIP kernels of the fused linear cross-entropy hot path (gfx950).
+//
+//   k_prep        target range check, n_valid, gradient scale
+//   k_fwd         logits tile by tile (MFMA) with an online-softmax epilogue:
+//                 per (row, vocabulary chunk) partial max / sum-exp / sum-z,
+//                 target logit captured by the one tile that holds it
+//   k_merge       partials -> lse, per-row loss, per-block loss sums
+//   k_loss_final  fixed-order sum of the block sums -> scalar loss
+//   k_bwd_g       recomputed logits of one vocabulary slice -> G slice
+//   k_dw          dW[slice] = scale G_slice^T X   (K = N, written once)
+//   k_dx          dX (+)= scale G_slice W_slice   (K = slice width)
+//   k_db_partial / k_db_final   db[slice] = scale sum_n G_slice
+//
+// Every reduction has a fixed order and no kernel uses global atomics, so
+// results are bitwise reproducible run to run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "flce_gemm.hpp"
+
+namespace flce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int64_t kGroup = 8;   // grouped-raster width (tiles sharing a panel)
+
+struct Ctl {           // first bytes of the workspace
+  int32_t n_valid;
+  int32_t status;      // 0 = targets fine, 1 = some target out of range
+  float scale;         // d loss / d (row loss): g / n_valid (mean) or g (sum)
+  float pad;
+};
+
+__device__ __forceinline__ float ld_elem(const uint16_t* p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ float ld_elem(const float* p, int64_t i) { return p[i]; }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+}
+__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh(x) = 1 - 2 / (exp(2x) + 1); absolute error a few ulp of 1, which the
+// softcap scales by c.  Saturates correctly: exp2 -> inf gives 1, -> 0 gives -1.
+__device__ __forceinline__ float fast_tanh(float x) {
+  const float e = fast_exp2(x * (2.0f * kLog2e));
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
+// (m, d) <- (m, d) merged with (m2, d2), both in log2 units: running maximum
+// and sum of 2^(z - m) (page "Cutting LLM Memory by 84%", "Definition and
+// Forward Pass": the online-softmax update).
+__device__ __forceinline__ void lse_merge(float& m, float& d, float m2, float d2) {
+  const float mx = fmaxf(m, m2);
+  if (mx == -INFINITY) return;
+  d = d * fast_exp2(m - mx) + d2 * fast_exp2(m2 - mx);
+  m = mx;
+}
+
+// ------------------------------------------------------------------- prep
+__global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targets, int64_t n,
+                                               int64_t v, int32_t ignore_index,
+                                               const float* __restrict__ grad_output,
+                                               int32_t reduction_mean, Ctl* __restrict__ ctl) {
+  __shared__ int32_t s_cnt[1024];
+  __shared__ int32_t s_bad[1024];
+  int32_t cnt = 0, bad = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) {
+    const int32_t t = targets[i];
+    const bool ign = t == ignore_index;
+    cnt += ign ? 0 : 1;
+    bad |= (!ign && (t < 0 || static_cast<int64_t>(t) >= v)) ? 1 : 0;
+  }
+  s_cnt[threadIdx.x] = cnt;
+  s_bad[threadIdx.x] = bad;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      s_cnt[threadIdx.x] += s_cnt[threadIdx.x + s];
+      s_bad[threadIdx.x] |= s_bad[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int32_t nv = s_cnt[0];
+    const float g = grad_output ? grad_output[0] : 1.0f;
+    ctl->n_valid = nv;
+    ctl->status = s_bad[0];
+    ctl->scale = reduction_mean ? (nv > 0 ? g / static_cast<float>(nv) : 0.0f) : g;
+    ctl->pad = 0.0f;
+  }
+}
+
+// ------------------------------------------------------------------- forward
+template <typename T>
+struct FwdArgs {
+  const T* x;             // [n, d]
+  const T* w;             // [v, d]
+  const T* bias;          // [v] or null
+  const int32_t* targets;
+  int64_t n, d, v;
+  float softcap, inv_softcap;
+  int64_t n_tiles, v_tiles, n_chunks, tiles_per_chunk, grid;
+  float* part_m;          // [n_chunks, n] running max, log2 units
+  float* part_d;          // [n_chunks, n] sum of 2^(z log2e - m)
+  float* part_s;          // [n_chunks, n] sum of z
+  float* zt;              // [n] target logit
+};
+
+// One workgroup: a 256-token tile against `tiles_per_chunk` consecutive
+// 256-wide vocabulary tiles; the logits tile is reduced in registers and
+// never leaves the chip (page "[CuteDSL] FLCE", Summary: the forward stores
+// only the per-row LSE and target logit).
+// kSumZ: label smoothing needs sum_v z of every row.
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fwd(FwdArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
+  __shared__ float xch[3][2][4][32];
+  const int64_t L = xcd_logical(blockIdx.x, a.grid);
+  if (L >= a.n_tiles * a.n_chunks) return;   // whole workgroup leaves together
+  int64_t nt, ch;
+  grouped(L, a.n_tiles, a.n_chunks, kGroup, nt, ch);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t n0 = nt * tile::kN;
+
+  int64_t tgt[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
+    tgt[nb] = tok < a.n ? static_cast<int64_t>(a.targets[tok]) : -1;
+  }
+  float m_run[4], d_run[4], s_run[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) { m_run[nb] = -INFINITY; d_run[nb] = 0.f; s_run[nb] = 0.f; }
+
+  const Operand<T, true> A{a.w, a.d, a.v, a.d};   // rows: vocabulary
+  const Operand<T, true> B{a.x, a.d, a.n, a.d};   // rows: tokens
+  const int64_t vt_end = (ch + 1) * a.tiles_per_chunk < a.v_tiles ? (ch + 1) * a.tiles_per_chunk
+                                                                   : a.v_tiles;
+  for (int64_t vt = ch * a.tiles_per_chunk; vt < vt_end; ++vt) {
+    const int64_t v0 = vt * tile::kM;
+    f32x16 acc[4][4];
+    gemm_tile(A, B, v0, n0, a.d, lds, acc);
+    const int64_t vw = v0 + wm * 128 + 4 * (lane >> 5);   // v of (mb, r) = vw + mb*32 + 8(r/4) + r%4
+
+    if (kBias || kSoftcap) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t v = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
+          const float b = kBias ? (v < a.v ? ld_elem(a.bias, v) : 0.f) : 0.f;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            float z = acc[mb][nb][r] + b;
+            if (kSoftcap) z = a.softcap * fast_tanh(z * a.inv_softcap);
+            acc[mb][nb][r] = z;
+          }
+        }
+    }
+
+    // Target logit: at most one lane-value per row in the whole vocabulary.
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t rel = tgt[nb] - vw;
+      if (rel >= 0 && rel < 128 && (rel & 4) == 0) {
+        const int idx = static_cast<int>((rel >> 5) * 16 + ((rel >> 3) & 3) * 4 + (rel & 3));
+        float z = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z = (mb * 16 + r == idx) ? acc[mb][nb][r] : z;
+        a.zt[n0 + wn * 128 + nb * 32 + (lane & 31)] = z;
+      }
+    }
+
+    const bool full = v0 + tile::kM <= a.v;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      float mt = -INFINITY, sz = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = full || (vw + mb * 32 + 8 * (r >> 2) + (r & 3) < a.v);
+          const float z = acc[mb][nb][r];
+          mt = ok ? fmaxf(mt, z) : mt;
+          if (kSumZ) sz += ok ? z : 0.f;
+        }
+      if (kSumZ) s_run[nb] += sz;
+      if (mt == -INFINITY) continue;
+      const float m_new = fmaxf(m_run[nb], mt * kLog2e);
+      float sum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = full || (vw + mb * 32 + 8 * (r >> 2) + (r & 3) < a.v);
+          const float e = fast_exp2(__builtin_fmaf(acc[mb][nb][r], kLog2e, -m_new));
+          sum += ok ? e : 0.f;
+        }
+      d_run[nb] = d_run[nb] * fast_exp2(m_run[nb] - m_new) + sum;
+      m_run[nb] = m_new;
+    }
+  }
+
+  // Combine the two lane halves (same token, disjoint vocabulary rows) ...
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const float m2 = __shfl_xor(m_run[nb], 32);
+    const float d2 = __shfl_xor(d_run[nb], 32);
+    const float s2 = __shfl_xor(s_run[nb], 32);
+    lse_merge(m_run[nb], d_run[nb], m2, d2);
+    s_run[nb] += s2;
+  }
+  // ... then the two wave rows through LDS, in a fixed order.
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      xch[0][wn][nb][lane] = m_run[nb];
+      xch[1][wn][nb][lane] = d_run[nb];
+      xch[2][wn][nb][lane] = s_run[nb];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      lse_merge(m_run[nb], d_run[nb], xch[0][wn][nb][lane], xch[1][wn][nb][lane]);
+      const float s = s_run[nb] + xch[2][wn][nb][lane];
+      const int64_t tok = n0 + wn * 128 + nb * 32 + lane;
+      if (tok < a.n) {
+        a.part_m[ch * a.n + tok] = m_run[nb];
+        a.part_d[ch * a.n + tok] = d_run[nb];
+        a.part_s[ch * a.n + tok] = s;
+      }
+    }
+  }
+}
+
+struct MergeArgs {
+  const float* part_m;
+  const float* part_d;
+  const float* part_s;
+  const float* zt;
+  const int32_t* targets;
+  int64_t n, v, n_chunks;
+  int32_t ignore_index;
+  float keep_target;    // 1 - eps
+  float eps_over_v;     // eps / V
+  float zloss;          // s
+  float* lse;           // [n]
+  float* row_loss;      // [n] or null
+  float* loss_rows;     // [n] or null (reduction none)
+  double* block_sums;   // [gridDim.x]
+};
+
+// lse = (m + log2 d) ln 2; row loss = lse - (1-eps) z_t - (eps/V) sum z + s lse^2
+// on valid rows, 0 elsewhere.
+__global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
+  __shared__ double red[256];
+  const int64_t tok = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  double row = 0.0;
+  if (tok < a.n) {
+    float m = -INFINITY, d = 0.f, s = 0.f;
+    for (int64_t c = 0; c < a.n_chunks; ++c) {
+      lse_merge(m, d, a.part_m[c * a.n + tok], a.part_d[c * a.n + tok]);
+      s += a.part_s[c * a.n + tok];
+    }
+    const float lse = (m + log2f(d)) * kLn2;
+    const bool valid = a.targets[tok] != a.ignore_index;
+    const float rl = lse - a.keep_target * a.zt[tok] - a.eps_over_v * s + a.zloss * lse * lse;
+    const float rlv = valid ? rl : 0.f;
+    a.lse[tok] = valid ? lse : 0.f;
+    if (a.row_loss) a.row_loss[tok] = rlv;
+    if (a.loss_rows) a.loss_rows[tok] = rlv;
+    row = rlv;
+  }
+  red[threadIdx.x] = row;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.block_sums[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ block_sums,
+                                                    int64_t nblocks, const Ctl* __restrict__ ctl,
+                                                    int32_t reduction_mean, float* __restrict__ loss) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < nblocks; i += 256) s += block_sums[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int32_t nv = ctl->n_valid;
+    loss[0] = static_cast<float>(reduction_mean ? (nv > 0 ? red[0] / nv : 0.0) : red[0]);
+  }
+}
+
+// ------------------------------------------------------------------- backward
+template <typename T>
+struct GArgs {
+  const T* x;
+  const T* w;
+  const T* bias;
+  const int32_t* targets;
+  const float* lse;
+  int64_t n, d, v;
+  int32_t ignore_index;
+  float softcap, inv_softcap;
+  float keep_target;    // 1 - eps
+  float eps_over_v;
+  float two_s;          // 2 s (z-loss)
+  int64_t v0, slice_len, ldg;
+  T* g;                 // [n, ldg] G slice, columns >= slice_len written as 0
+  int64_t n_tiles, s_tiles, grid;
+};
+
+// Recompute one 256 x 256 logits tile of the slice and turn it into
+// G = [p (1 + 2 s lse) - (1-eps) onehot - eps/V] (1 - (z/c)^2), p = exp(z - lse)
+// (page "Cutting LLM Memory by 84%", "Kernel Implementation", backward:
+// probabilities recomputed from the stored LSE, ground truth subtracted).
+template <typename T, bool kBias, bool kSoftcap>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_bwd_g(GArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
+  const int64_t L = xcd_logical(blockIdx.x, a.grid);
+  if (L >= a.n_tiles * a.s_tiles) return;
+  int64_t nt, st;
+  grouped(L, a.n_tiles, a.s_tiles, kGroup, nt, st);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t n0 = nt * tile::kN, vl0 = st * tile::kM;
+
+  const Operand<T, true> A{a.w + a.v0 * a.d, a.d, a.v - a.v0, a.d};
+  const Operand<T, true> B{a.x, a.d, a.n, a.d};
+  f32x16 acc[4][4];
+  gemm_tile(A, B, vl0, n0, a.d, lds, acc);
+
+  const int64_t vw = vl0 + wm * 128 + 4 * (lane >> 5);   // slice-local v of (mb=0, r=0)
+  bool valid[4];
+  float lse2[4], zfac[4];
+  int hit[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
+    const int64_t t = tok < a.n ? static_cast<int64_t>(a.targets[tok]) : -1;
+    valid[nb] = tok < a.n && t != a.ignore_index;
+    const float l = valid[nb] ? a.lse[tok] : 0.f;
+    lse2[nb] = l * kLog2e;
+    zfac[nb] = 1.0f + a.two_s * l;
+    const int64_t rel = t - a.v0 - vw;
+    hit[nb] = (valid[nb] && rel >= 0 && rel < 128 && (rel & 4) == 0)
+                  ? static_cast<int>((rel >> 5) * 16 + ((rel >> 3) & 3) * 4 + (rel & 3))
+                  : -1;
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
+      const bool vin = vl < a.slice_len;
+      const float b = kBias ? (vin ? ld_elem(a.bias, a.v0 + vl) : 0.f) : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        float z = acc[mb][nb][r] + b;
+        float dz = 1.0f;
+        if (kSoftcap) {
+          const float th = fast_tanh(z * a.inv_softcap);
+          z = a.softcap * th;
+          dz = 1.0f - th * th;
+        }
+        const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2[nb]));
+        const float sub = (mb * 16 + r == hit[nb]) ? a.eps_over_v + a.keep_target : a.eps_over_v;
+        float gv = __builtin_fmaf(p, zfac[nb], -sub);
+        if (kSoftcap) gv *= dz;
+        acc[mb][nb][r] = (valid[nb] && vin) ? gv : 0.f;
+      }
+    }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
+    if (tok >= a.n) continue;
+    T* row = a.g + tok * a.ldg;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        store4(row + vw + mb * 32 + 8 * q, acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
+               acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+  }
+}
+
+template <typename T>
+struct DwArgs {
+  const T* x;           // [n, d]
+  const T* g;           // [n, ldg]
+  int64_t n, d, v0, slice_len, ldg, gcols;
+  const Ctl* ctl;
+  float* dw;            // [v, d]
+  int64_t d_tiles, s_tiles, grid;
+};
+
+// dW[v0 + v, :] = scale sum_n G[n, v] X[n, :]: one dedicated contraction over
+// all tokens, each output tile written exactly once (page "Cutting LLM Memory
+// by 84%", "Path to Production": a dW kernel whose programs own a block of W
+// and iterate over the batch).  Computed as C[d, v] so each lane stores four
+// consecutive d.
+template <typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_dw(DwArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
+  const int64_t L = xcd_logical(blockIdx.x, a.grid);
+  if (L >= a.d_tiles * a.s_tiles) return;
+  int64_t dt, st;
+  grouped(L, a.d_tiles, a.s_tiles, kGroup, dt, st);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const Operand<T, false> A{a.x, a.d, a.d, a.n};          // (d, n) at x[n*D + d]
+  const Operand<T, false> B{a.g, a.ldg, a.gcols, a.n};    // (v, n) at g[n*ldg + v]
+  f32x16 acc[4][4];
+  gemm_tile(A, B, dt * tile::kM, st * tile::kN, a.n, lds, acc);
+
+  const float scale = a.ctl->scale;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t vl = st * tile::kN + wn * 128 + nb * 32 + (lane & 31);
+    if (vl >= a.slice_len) continue;
+    float* row = a.dw + (a.v0 + vl) * a.d;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t dd = dt * tile::kM + wm * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
+        if (dd < a.d)
+          store4(row + dd, scale * acc[mb][nb][4 * q], scale * acc[mb][nb][4 * q + 1],
+                 scale * acc[mb][nb][4 * q + 2], scale * acc[mb][nb][4 * q + 3]);
+      }
+  }
+}
+
+template <typename T>
+struct DxArgs {
+  const T* w;           // [v, d]
+  const T* g;           // [n, ldg]
+  int64_t n, d, v, v0, kdim, ldg;
+  const Ctl* ctl;
+  float* acc_buf;       // [n, d] fp32 running sum over slices
+  T* dx;                // [n, d]
+  int32_t first, last;
+  int64_t d_tiles, n_tiles, grid;
+};
+
+// dX (+)= scale G_slice W_slice, computed as C[d, n] so each lane owns four
+// consecutive d of one token row: the running fp32 sum is read-modified-
+// written with 16-byte accesses; the last slice writes dX in its own dtype.
+template <typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_dx(DxArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
+  const int64_t L = xcd_logical(blockIdx.x, a.grid);
+  if (L >= a.d_tiles * a.n_tiles) return;
+  int64_t nt, dt;
+  grouped(L, a.n_tiles, a.d_tiles, kGroup, nt, dt);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const Operand<T, false> A{a.w + a.v0 * a.d, a.d, a.d, a.v - a.v0};   // (d, v) at w[v*D + d]
+  const Operand<T, true> B{a.g, a.ldg, a.n, a.kdim};                  // (n, v) at g[n*ldg + v]
+  f32x16 acc[4][4];
+  gemm_tile(A, B, dt * tile::kM, nt * tile::kN, a.kdim, lds, acc);
+
+  const float scale = a.ctl->scale;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t tok = nt * tile::kN + wn * 128 + nb * 32 + (lane & 31);
+    if (tok >= a.n) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t dd = dt * tile::kM + wm * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
+        if (dd >= a.d) continue;
+        float4 val{scale * acc[mb][nb][4 * q], scale * acc[mb][nb][4 * q + 1],
+                   scale * acc[mb][nb][4 * q + 2], scale * acc[mb][nb][4 * q + 3]};
+        float* ap = a.acc_buf + tok * a.d + dd;
+        if (!a.first) {
+          const float4 prev = *reinterpret_cast<const float4*>(ap);
+          val.x += prev.x; val.y += prev.y; val.z += prev.z; val.w += prev.w;
+        }
+        if (a.last)
+          store4(a.dx + tok * a.d + dd, val.x, val.y, val.z, val.w);
+        else
+          *reinterpret_cast<float4*>(ap) = val;
+      }
+  }
+}
+
+// Column sums of the G slice over token blocks, then over blocks in order.
+template <typename T>
+__global__ __launch_bounds__(256) void k_db_partial(const T* __restrict__ g, int64_t n, int64_t ldg,
+                                                    int64_t cols, int64_t rows_per_split,
+                                                    float* __restrict__ part) {
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (col >= cols) return;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per_split;
+  const int64_t r1 = r0 + rows_per_split < n ? r0 + rows_per_split : n;
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) s += ld_elem(g, r * ldg + col);
+  part[static_cast<int64_t>(blockIdx.y) * cols + col] = s;
+}
+
+__global__ __launch_bounds__(256) void k_db_final(const float* __restrict__ part, int64_t splits,
+                                                  int64_t cols, int64_t v0, int64_t slice_len,
+                                                  const Ctl* __restrict__ ctl,
+                                                  float* __restrict__ db) {
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (col >= slice_len) return;
+  float s = 0.f;
+  for (int64_t sp = 0; sp < splits; ++sp) s += part[sp * cols + col];
+  db[v0 + col] = ctl->scale * s;
+}
+
+__global__ __launch_bounds__(256) void k_fill(float* __restrict__ p, int64_t count, float value) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < count) p[i] = value;
+}
+
+}  // namespace flce

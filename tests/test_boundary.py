@@ -1,0 +1,146 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects invalid calls on the host before any HIP call (no GPU needed)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from linear_cross_entropy_bf16_amd import _lib
+from linear_cross_entropy_bf16_amd.build import LIB_PATH, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+# Any 256-byte aligned, never-dereferenced address: every call below is
+# rejected by host validation before a pointer is touched.
+FAKE = 0x7f0000000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    names = {s: lib.flce_status_string(s).decode() for s in range(6)}
+    assert names[0] == "ok"
+    assert names[4] == "target out of range"
+    assert len(set(names.values())) == 6
+    assert lib.flce_status_string(99).decode() == "unknown status"
+    assert _lib.version() >= 100
+
+
+def P(**kw):
+    base = dict(n=256, d=128, v=1024, dtype=_lib.DTYPE_F32)
+    base.update(kw)
+    return _lib.make_params(**base)
+
+
+def test_workspace_size_rejects_bad_params(lib):
+    assert _lib.workspace_size(P(), True) > 0
+    for bad in (P(d=100), P(d=0), P(v=0), P(n=-1), P(dtype=7), P(label_smoothing=1.5),
+                P(label_smoothing=-0.1), P(lse_square_scale=-1.0), P(softcap=-2.0),
+                P(vocab_slice=-1), P(n=1 << 31)):
+        assert _lib.workspace_size(bad, True) == 0
+    assert lib.flce_workspace_size(None, 1) == 0
+
+
+def test_workspace_never_holds_the_logits():
+    g = json.load(open(os.path.join(GOLDEN, "logit_bottleneck_sizes.json")))
+    n, d, v = g["n"], g["d"], g["v"]
+    assert round(n * v / 1e9, 1) == g["logit_elements_billions"]
+    assert round(2 * n * v / 1e9, 1) == g["logits_bf16_gb"]
+    assert round(4 * n * v / 1e9, 1) == g["logits_fp32_gb"]
+    p = _lib.make_params(n, d, v, _lib.DTYPE_BF16)
+    ws = _lib.workspace_size(p, True)
+    assert 0 < ws < 2 * n * v / 4          # under a quarter of one bf16 copy of the logits
+    assert _lib.workspace_size(p, False) < ws
+
+
+def test_workspace_grows_with_slice_and_batch():
+    a = _lib.workspace_size(_lib.make_params(8192, 4096, 128256, 0, vocab_slice=2048), True)
+    b = _lib.workspace_size(_lib.make_params(8192, 4096, 128256, 0, vocab_slice=8192), True)
+    c = _lib.workspace_size(_lib.make_params(16384, 4096, 128256, 0, vocab_slice=8192), True)
+    assert a < b < c
+
+
+def fwd(p, x=FAKE, w=FAKE, bias=None, t=FAKE, loss=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return _lib.forward(p, x, w, bias, t, loss, lse, None, ws, ws_bytes, None)
+
+
+def bwd(p, x=FAKE, w=FAKE, bias=None, t=FAKE, lse=FAKE, dx=FAKE, dw=FAKE, db=None, ws=FAKE,
+        ws_bytes=1 << 40):
+    return _lib.backward(p, x, w, bias, t, lse, None, dx, dw, db, ws, ws_bytes, None)
+
+
+def fused(p, ws_bytes=1 << 40, **kw):
+    args = dict(x=FAKE, w=FAKE, bias=None, t=FAKE, loss=FAKE, lse=FAKE, dx=FAKE, dw=FAKE, db=None,
+                ws=FAKE)
+    args.update(kw)
+    return _lib.fused_fwd_bwd(p, args["x"], args["w"], args["bias"], args["t"], args["loss"],
+                              args["lse"], args["dx"], args["dw"], args["db"], args["ws"], ws_bytes,
+                              None)
+
+
+INVALID = _lib.FLCE_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("call", ["forward", "backward", "fused"])
+def test_host_validation(lib, call):
+    f = {"forward": fwd, "backward": bwd, "fused": fused}[call]
+    assert f(P(d=12)) == INVALID                    # D not a multiple of 8
+    assert f(P(v=0)) == INVALID
+    assert f(P(n=-5)) == INVALID
+    assert f(P(dtype=3)) == INVALID
+    assert f(P(label_smoothing=2.0)) == INVALID
+    assert f(P(reduction=7)) == INVALID
+    assert f(P(softcap=float("nan"))) == INVALID
+    assert f(P(lse_square_scale=float("inf"))) == INVALID
+    assert f(P(), w=None) == INVALID                # missing weight
+    assert f(P(), x=None) == INVALID                # missing x with n > 0
+    assert f(P(), t=None) == INVALID                # missing targets
+    assert f(P(), w=FAKE + 8) == INVALID            # weight not 16-byte aligned
+    assert f(P(), ws=FAKE + 64) == INVALID          # workspace not 256-byte aligned
+    assert f(P(), ws=None) == INVALID
+    assert f(P(), ws_bytes=16) == _lib.FLCE_ERR_WORKSPACE_TOO_SMALL
+    need = _lib.workspace_size(P(), call != "forward")
+    assert f(P(), ws_bytes=need - 1) == _lib.FLCE_ERR_WORKSPACE_TOO_SMALL
+    if call == "forward":
+        assert f(P(), loss=None) == INVALID
+        assert f(P(), lse=None) == INVALID
+    else:
+        assert f(P(), dw=None) == INVALID
+        assert f(P(), dx=FAKE + 4) == INVALID
+        assert f(P(), bias=FAKE, db=None) == INVALID   # bias without a place for its gradient
+
+
+def test_backward_refuses_reduction_none(lib):
+    p = P(reduction=2)
+    assert bwd(p) == _lib.FLCE_ERR_UNSUPPORTED
+    assert fused(p) == _lib.FLCE_ERR_UNSUPPORTED
+
+
+def test_null_params(lib):
+    pp = ctypes.POINTER(_lib.Params)()
+    assert lib.flce_forward(pp, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == INVALID
+    assert lib.flce_check_status(None, None) == INVALID

@@ -1,0 +1,277 @@
+"""HIP path against the fp64 oracle (needs an MI355X).
+
+Full element-by-element comparison on the tiny fp32 and small LM-head
+workloads and on edge cases; the large workloads are checked on a seeded
+512-row sub-batch (its own call) and on 256 sampled rows of the full-size run.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_cross_entropy_bf16_amd import api, workloads as W
+from linear_cross_entropy_bf16_amd._lib import FLCE_ERR_TARGET_OUT_OF_RANGE, FLCEError
+from oracle import flce_oracle as O
+from tests import gpu_utils as U
+
+pytestmark = pytest.mark.gpu
+
+IGN = -100
+
+
+def small_problem(n, d, v, dtype="bf16", bias=False, ignore_frac=0.1, seed=0, w_std=None):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, d), dtype=np.float32)
+    w = rng.standard_normal((v, d), dtype=np.float32) * np.float32(w_std or 1.0 / np.sqrt(d))
+    b = (rng.standard_normal(v, dtype=np.float32) * np.float32(0.3)) if bias else None
+    t = rng.integers(0, v, n).astype(np.int32)
+    k = int(round(ignore_frac * n))
+    if k:
+        t[rng.choice(n, k, replace=False)] = IGN
+    if dtype == "bf16":
+        x, w = W.f32_to_bf16_bits(x), W.f32_to_bf16_bits(w)
+        b = W.f32_to_bf16_bits(b) if b is not None else None
+    return dict(x=x, w=w, bias=b, targets=t)
+
+
+def banner(msg):
+    print(f"\n[gpu] {msg}", flush=True)
+
+
+# ----------------------------------------------------------------- workloads
+def test_tiny_f32_full():
+    wl = W.WORKLOADS["tiny_f32"]
+    banner(f"{wl}")
+    U.compare_full(W.generate(wl), wl.dtype, U.options(wl))
+
+
+def test_small_lm_head_full():
+    wl = W.WORKLOADS["small_lm_head"]
+    banner(f"{wl}")
+    U.compare_full(W.generate(wl), wl.dtype, U.options(wl))
+
+
+LARGE = ["llama3_8b_seq", "llama3_8b_batch8", "wide_vocab_features"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", LARGE)
+def test_large_subbatch(name):
+    """A seeded 512-row sub-batch of the workload as its own call: every
+    output compared, dW streamed by vocabulary blocks."""
+    wl = W.WORKLOADS[name]
+    banner(f"sub-batch of {wl}")
+    full = W.generate(wl)
+    rows = W.sample_rows(wl, 512, salt=1)
+    inp = dict(x=full["x"][rows], w=full["w"], bias=full["bias"], targets=full["targets"][rows])
+    del full
+    o = U.options(wl)
+    got = U.run_fused(inp, wl.dtype, o)
+    ref = O.forward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+    U.assert_loss(got["loss"], ref.loss)
+    U.assert_lse(got["lse"], ref.lse)
+    acc = U.FrobAccumulator()
+    xr = O.to_f64(inp["x"])
+    wr = O.to_f64(inp["w"])
+    br = O.to_f64(inp["bias"])
+    z = O.logits(xr, wr, br, o.softcap)
+    lse = O.log_sum_exp(z)
+    g = O.grad_logits(z, lse, inp["targets"], o) * O.grad_scale(o, ref.n_valid, 1.0)
+    del z
+    U.assert_close(got["dx"], g @ wr, "dX")
+    for v0 in range(0, wl.v, 16384):
+        v1 = min(wl.v, v0 + 16384)
+        acc.add(got["dw"][v0:v1], g[:, v0:v1].T @ xr)
+    acc.check("dW")
+    if got["db"] is not None:
+        U.assert_close(got["db"], g.sum(axis=0), "db")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", LARGE)
+def test_large_sampled_rows(name):
+    """Full-size forward and backward through the two separate entry points;
+    256 sampled rows of row loss, LSE and dX against the oracle (with the full
+    batch's n_valid), plus properties that hold at any size."""
+    wl = W.WORKLOADS[name]
+    banner(f"full-size {wl}")
+    inp = W.generate(wl)
+    o = U.options(wl)
+    x = U.dev_tensor(inp["x"], wl.dtype)
+    w = U.dev_tensor(inp["w"], wl.dtype)
+    b = U.dev_tensor(inp["bias"], wl.dtype) if inp["bias"] is not None else None
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, row_loss = api.forward(x, w, t, b, check_targets=True, **U.lib_opts(o))
+    dx, dw, db = api.backward(x, w, t, lse, None, b, **U.lib_opts(o))
+    torch.cuda.synchronize()
+    rows = W.sample_rows(wl, 256)
+    valid = inp["targets"] != wl.ignore_index
+    n_valid = int(valid.sum())
+    ref = O.forward_backward(inp["x"][rows], inp["w"], inp["bias"], inp["targets"][rows], o,
+                             n_valid=n_valid, want_dw=False)
+    rows_d = torch.from_numpy(rows).cuda()
+    U.assert_lse(U.host(lse[rows_d]), ref.lse)
+    rl = U.host(row_loss)
+    assert np.abs(rl[rows] - ref.row_loss).max() <= U.LSE_ABS * 2
+    U.assert_close(U.host(dx[rows_d]), ref.dx, "dX rows")
+    # the scalar loss is the (mean or sum) reduction of the row losses
+    total = rl.sum()
+    want = total / n_valid if wl.reduction == "mean" else total
+    U.assert_loss(float(loss.item()), want, "loss vs its row losses")
+    # ignored rows: exactly zero
+    ign = ~valid
+    if ign.any():
+        it = torch.from_numpy(np.nonzero(ign)[0]).cuda()
+        assert torch.all(lse[it] == 0) and torch.all(row_loss[it] == 0)
+        assert torch.all(dx[it] == 0)
+    # without z-loss and softcap each row of G sums to 0, so sum_v dW[v, :] = 0
+    if wl.lse_square_scale == 0 and wl.softcap == 0:
+        colsum = dw.double().sum(dim=0)
+        assert colsum.abs().max().item() <= 1e-3 * dw.double().abs().max().item() * 64
+
+
+# ----------------------------------------------------------------- features
+FEATURES = [
+    dict(),
+    dict(label_smoothing=0.1),
+    dict(lse_square_scale=1e-3),
+    dict(softcap=2.0),
+    dict(reduction="sum"),
+    dict(label_smoothing=0.2, lse_square_scale=1e-2, softcap=1.5, reduction="sum"),
+]
+
+
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("feats", FEATURES, ids=lambda f: "-".join(f"{k}={v}" for k, v in f.items()) or "plain")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_features(dtype, feats, bias):
+    inp = small_problem(300, 136, 1000, dtype, bias=bias, seed=3, w_std=0.3)
+    banner(f"features {dtype} {feats} bias={bias}")
+    U.compare_full(inp, dtype, O.LossOptions(**feats))
+
+
+@pytest.mark.parametrize("n,d,v,slice_", [
+    (1, 8, 1, 0), (2, 8, 2, 0), (257, 264, 257, 0), (300, 72, 1000, 256), (513, 200, 1000, 512),
+    (64, 1024, 3000, 1024), (1000, 64, 33, 0), (256, 256, 256, 0), (255, 8, 4097, 1024),
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_shapes(dtype, n, d, v, slice_):
+    """Tails in every dimension, several vocabulary slices with a ragged last
+    slice, K not a multiple of the 64-wide slab, single-class and two-class
+    vocabularies."""
+    inp = small_problem(n, d, v, dtype, bias=True, seed=n + d + v)
+    banner(f"ragged {dtype} n={n} d={d} v={v} slice={slice_}")
+    U.compare_full(inp, dtype, O.LossOptions(label_smoothing=0.05, lse_square_scale=1e-3),
+                   vocab_slice=slice_)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_batch(dtype):
+    inp = small_problem(0, 64, 100, dtype, bias=True)
+    for red in ("mean", "sum"):
+        got = U.run_fused(inp, dtype, O.LossOptions(reduction=red))
+        assert got["loss"] == 0.0 and got["lse"].size == 0 and got["dx"].shape == (0, 64)
+        assert np.all(got["dw"] == 0) and np.all(got["db"] == 0)
+
+
+@pytest.mark.parametrize("red", ["mean", "sum"])
+def test_all_rows_ignored(red):
+    inp = small_problem(100, 64, 500, "bf16", bias=True, ignore_frac=1.0)
+    got = U.run_fused(inp, "bf16", O.LossOptions(reduction=red))
+    assert got["loss"] == 0.0
+    assert np.all(got["lse"] == 0) and np.all(got["dx"] == 0)
+    assert np.all(got["dw"] == 0) and np.all(got["db"] == 0)
+
+
+def test_ignore_index_inside_vocabulary():
+    inp = small_problem(200, 64, 500, "bf16", ignore_frac=0.0, seed=5)
+    inp["targets"][::7] = 3
+    U.compare_full(inp, "bf16", O.LossOptions(ignore_index=3))
+
+
+def test_reduction_none_forward():
+    inp = small_problem(300, 64, 700, "bf16", seed=6)
+    x, w = U.dev_tensor(inp["x"], "bf16"), U.dev_tensor(inp["w"], "bf16")
+    t = torch.from_numpy(inp["targets"]).cuda()
+    loss, lse, row_loss = api.forward(x, w, t, reduction="none", label_smoothing=0.1)
+    ref = O.forward(inp["x"], inp["w"], None, inp["targets"],
+                    O.LossOptions(reduction="none", label_smoothing=0.1))
+    assert np.abs(U.host(loss) - ref.loss).max() <= U.LSE_ABS
+    assert np.array_equal(U.host(loss), U.host(row_loss))
+    with pytest.raises(FLCEError):
+        api.backward(x, w, t, lse, reduction="none")
+
+
+def test_target_out_of_range_is_reported():
+    inp = small_problem(100, 64, 500, "bf16", seed=7)
+    inp["targets"][10] = 500
+    x, w = U.dev_tensor(inp["x"], "bf16"), U.dev_tensor(inp["w"], "bf16")
+    t = torch.from_numpy(inp["targets"]).cuda()
+    with pytest.raises(FLCEError) as e:
+        api.forward(x, w, t, check_targets=True)
+    assert e.value.status == FLCE_ERR_TARGET_OUT_OF_RANGE
+    inp["targets"][10] = -7
+    with pytest.raises(FLCEError):
+        api.forward(x, w, torch.from_numpy(inp["targets"]).cuda(), check_targets=True)
+    inp["targets"][10] = 499
+    api.forward(x, w, torch.from_numpy(inp["targets"]).cuda(), check_targets=True)
+
+
+# ----------------------------------------------------------------- API layers
+def test_deterministic_bitwise():
+    inp = small_problem(700, 264, 3000, "bf16", bias=True, seed=8)
+    o = O.LossOptions(label_smoothing=0.1, softcap=5.0)
+    a = U.run_fused(inp, "bf16", o, vocab_slice=1024)
+    b = U.run_fused(inp, "bf16", o, vocab_slice=1024)
+    for k in ("lse", "dx", "dw", "db"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["loss"] == b["loss"]
+
+
+def test_fused_equals_separate_calls():
+    inp = small_problem(500, 128, 2000, "bf16", bias=True, seed=9)
+    o = O.LossOptions(label_smoothing=0.1, lse_square_scale=1e-3)
+    a = U.run_fused(inp, "bf16", o, vocab_slice=768)
+    x, w = U.dev_tensor(inp["x"], "bf16"), U.dev_tensor(inp["w"], "bf16")
+    b_ = U.dev_tensor(inp["bias"], "bf16")
+    t = torch.from_numpy(inp["targets"]).cuda()
+    loss, lse, _ = api.forward(x, w, t, b_, vocab_slice=768, **U.lib_opts(o))
+    dx, dw, db = api.backward(x, w, t, lse, None, b_, vocab_slice=768, **U.lib_opts(o))
+    assert a["loss"] == float(loss.item())
+    assert np.array_equal(a["dx"], U.host(dx)) and np.array_equal(a["dw"], U.host(dw))
+    assert np.array_equal(a["db"], U.host(db))
+
+
+def test_autograd_function_and_grad_output():
+    """Not-last-layer use: the loss is scaled before backward, so the upstream
+    gradient reaches the library as a device scalar."""
+    inp = small_problem(256, 128, 1500, "bf16", bias=True, seed=10)
+    x = U.dev_tensor(inp["x"], "bf16").requires_grad_(True)
+    w = U.dev_tensor(inp["w"], "bf16").requires_grad_(True)
+    b = U.dev_tensor(inp["bias"], "bf16").requires_grad_(True)
+    t = torch.from_numpy(inp["targets"]).cuda()
+    loss = api.linear_cross_entropy(x, w, t, b, label_smoothing=0.1)
+    (2.5 * loss).backward()
+    o = O.LossOptions(label_smoothing=0.1)
+    ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o, grad_output=2.5)
+    U.assert_loss(float(loss.item()), ref.loss)
+    U.assert_close(U.host(x.grad), ref.dx, "dX")
+    U.assert_close(U.host(w.grad), ref.dw, "dW")
+    U.assert_close(U.host(b.grad), ref.db, "db")
+
+
+def test_noncontiguous_and_batched_inputs():
+    inp = small_problem(240, 64, 800, "bf16", seed=11)
+    ref = O.forward(inp["x"], inp["w"], None, inp["targets"], O.LossOptions())
+    x = U.dev_tensor(inp["x"], "bf16")
+    w = U.dev_tensor(inp["w"], "bf16")
+    t = torch.from_numpy(inp["targets"]).cuda()
+    wide = torch.zeros((240, 128), dtype=torch.bfloat16, device="cuda")
+    wide[:, 32:96] = x
+    xs = wide[:, 32:96]                         # rows strided by 128 elements
+    assert not xs.is_contiguous()
+    U.assert_loss(float(api.linear_cross_entropy(xs, w, t).item()), ref.loss, "strided x")
+    wt = w.t().contiguous().t()                 # column-major weight
+    assert not wt.is_contiguous()
+    U.assert_loss(float(api.linear_cross_entropy(x, wt, t).item()), ref.loss, "column-major W")
+    loss3 = api.linear_cross_entropy(x.reshape(4, 60, 64), w, t.reshape(4, 60).long())
+    U.assert_loss(float(loss3.item()), ref.loss, "batched x")
