@@ -1,0 +1,239 @@
+"""Benchmark: fused linear cross-entropy forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one flce_fused_fwd_bwd call (forward logits + online LSE, loss,
+recomputed softmax, dW and dX; grad_output = 1) over the whole synthetic batch,
+with inputs already resident in HBM.  Prints one JSON line with tokens/s, the
+fraction of the bf16 MFMA peak, peak allocated HBM bytes, the roofline of the
+forward kernel (timed live with HIP events on the library's stream) and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FLCE fwd+bwd tokens/sec, % bf16 MFMA peak, peak HBM bytes at N=65536 D=4096 V=128256"
+PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_F32_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+# The pages' own figure for this shape (B200, CuTe-DSL FLCE, bf16, BT = 65 536,
+# V = 128 256, H = 4096): 194 ms per fwd+bwd, i.e. 337.8 k tokens/s.
+PAGES_TOKENS_PER_S = 65536 / 0.194
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_llama3_8b_batch8_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "linear_cross_entropy_bf16_amd", "csrc", f)
+                  for f in ("flce_gemm.hpp", "flce_kernels.hpp", "flce.hip")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Per-launch HBM bytes of k_fwd from the committed counter summary, or
+    None when it is missing, for another workload, or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, max_rows: int):
+    """The fp64 oracle as it stands on a bounded row sample of the workload
+    (full D and V, dW included)."""
+    import numpy as np
+    from oracle import flce_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    rows = np.arange(min(max_rows, wl.n))
+    o = O.LossOptions(wl.ignore_index, wl.label_smoothing, wl.lse_square_scale, wl.softcap,
+                      wl.reduction)
+    t0 = time.perf_counter()
+    O.forward_backward(inp["x"][rows], inp["w"], inp["bias"], inp["targets"][rows], o)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {len(rows)} of {wl.n} rows of {wl.name} (full D={wl.d}, V={wl.v}, dW "
+                      f"included), fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3_8b_batch8")
+    ap.add_argument("--vocab-slice", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="rows of the workload the CPU oracle baseline runs on (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (each box here "
+              f"has one GPU; the multi-GPU sharding is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from linear_cross_entropy_bf16_amd import api, workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU")
+    dev = torch.device("cuda:0")
+    log(f"generating {wl}")
+    inp = W.generate(wl)
+
+    def put(a):
+        t = torch.from_numpy(a)
+        if wl.dtype == "bf16":
+            t = t.view(torch.bfloat16)
+        return t.to(dev)
+
+    x, w = put(inp["x"]), put(inp["w"])
+    b = put(inp["bias"]) if inp["bias"] is not None else None
+    t = torch.from_numpy(inp["targets"]).to(dev)
+    opts = dict(ignore_index=wl.ignore_index, label_smoothing=wl.label_smoothing,
+                lse_square_scale=wl.lse_square_scale, softcap=wl.softcap, reduction=wl.reduction,
+                vocab_slice=args.vocab_slice)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_alloc = torch.cuda.memory_allocated(dev)
+
+    # Outputs and workspace are allocated once and reused by every step.
+    nbytes = api.workspace_bytes(wl.n, wl.d, wl.v, x.dtype, True, **opts)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = (torch.empty(1, dtype=torch.float32, device=dev),
+           torch.empty(wl.n, dtype=torch.float32, device=dev),
+           torch.empty((wl.n, wl.d), dtype=x.dtype, device=dev),
+           torch.empty((wl.v, wl.d), dtype=torch.float32, device=dev),
+           torch.empty(wl.v, dtype=torch.float32, device=dev) if b is not None else None)
+
+    def step():
+        return api.fused_fwd_bwd(x, w, t, b, workspace=ws, out=out, **opts)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    peak_bytes = torch.cuda.max_memory_allocated(dev)
+    loss = float(out[0].item())
+    log(f"{ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), loss {loss:.6f}")
+
+    # Forward kernel alone: flce_forward is k_fwd plus three launches that
+    # each touch O(N) floats, timed on the same stream.
+    fwd_ws = torch.empty(api.workspace_bytes(wl.n, wl.d, wl.v, x.dtype, False, **opts),
+                         dtype=torch.uint8, device=dev)
+    from linear_cross_entropy_bf16_amd import _lib
+    p = api.make_params(wl.n, wl.d, wl.v, x.dtype, wl.ignore_index, wl.label_smoothing,
+                        wl.lse_square_scale, wl.softcap, wl.reduction, args.vocab_slice)
+    fwd_loss = torch.empty(1, dtype=torch.float32, device=dev)
+    fwd_lse = torch.empty(wl.n, dtype=torch.float32, device=dev)
+
+    def fwd():
+        st = _lib.forward(p, x.data_ptr(), w.data_ptr(), None if b is None else b.data_ptr(),
+                          t.data_ptr(), fwd_loss.data_ptr(), fwd_lse.data_ptr(), None,
+                          fwd_ws.data_ptr(), fwd_ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise _lib.FLCEError(st, "flce_forward")
+
+    fwd()
+    torch.cuda.synchronize()
+    reps = max(3, args.steps)
+    ev0.record(stream)
+    for _ in range(reps):
+        fwd()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = ev0.elapsed_time(ev1) / reps
+    del fwd_ws
+
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    step_tflops = wl.flops_fwd_bwd / (ms * 1e-3) / 1e12
+    fwd_tflops = 2.0 * wl.n * wl.d * wl.v / (fwd_ms * 1e-3) / 1e12
+    tokens_per_s = wl.n / (ms * 1e-3)
+    traffic = measured_traffic(wl.name)
+
+    cpu = None
+    if args.cpu_rows > 0:
+        log(f"cpu oracle baseline on {args.cpu_rows} rows")
+        cpu = cpu_baseline(wl, inp, args.cpu_rows)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tokens_per_s / PAGES_TOKENS_PER_S, 4) if wl.name == "llama3_8b_batch8" else None,
+        "baseline_note": "pages' CuTe-DSL FLCE on B200 at this shape, 194 ms per fwd+bwd (context, "
+                         "other hardware)",
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n": wl.n, "d": wl.d, "v": wl.v, "targets": wl.targets,
+                   "ignore_frac": wl.ignore_frac, "reduction": wl.reduction, "bias": wl.bias,
+                   "label_smoothing": wl.label_smoothing, "lse_square_scale": wl.lse_square_scale,
+                   "softcap": wl.softcap, "vocab_slice": args.vocab_slice or "default",
+                   "parallelism": "single GPU"},
+        "mfma_frac_step": round(step_tflops / peak, 4),
+        "step_tflops": round(step_tflops, 1),
+        "peak_hbm_bytes": int(peak_bytes),
+        "peak_hbm_bytes_above_inputs": int(peak_bytes - base_alloc),
+        "workspace_bytes": int(nbytes),
+        "loss": loss,
+        "roofline": {
+            "kernel": "k_fwd (forward logits GEMM + online-LSE epilogue)",
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 1),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / peak, 4),
+            "traffic": traffic,
+            "fwd_ms": round(fwd_ms, 3),
+            "flops_per_launch": 2.0 * wl.n * wl.d * wl.v,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
