@@ -87,7 +87,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_batch8")
     ap.add_argument("--vocab-slice", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle baseline runs on (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -194,10 +194,10 @@ __device__ __forceinline__ void compute_slab(const char* sA, const char* sB, f32
   }
 }
 
-// One 256 x 256 output tile at (m0, n0), K = [0, K).  All 256 threads must
-// call it; it ends with a barrier, so `lds` is free again on return.
+// Register-staged path (used for fp32): the next slab's global loads land in
+// VGPRs while the current slab is multiplied, then go to the other LDS buffer.
 template <typename T, bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile(const Operand<T, AK>& A, const Operand<T, BK>& B,
+__device__ __forceinline__ void gemm_tile_regs(const Operand<T, AK>& A, const Operand<T, BK>& B,
                                           int64_t m0, int64_t n0, int64_t K, char* lds,
                                           f32x16 (&acc)[4][4]) {
   const int tid = threadIdx.x;
@@ -234,6 +234,194 @@ __device__ __forceinline__ void gemm_tile(const Operand<T, AK>& A, const Operand
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------- bf16 DMA path
+// bf16 tiles travel global -> LDS with buffer_load ... lds (no staging
+// registers, no LDS store instructions), double-buffered in 64-wide K slabs
+// so every K-major row segment is a whole 128-byte line.  Out-of-range rows
+// and columns are loads with an out-of-range buffer offset, which the
+// hardware turns into zeros, so the loop has no branches.  MN-major operands
+// stay as they are in memory ([k][mn] rows of 512 bytes) and become MFMA
+// fragments through ds_read_b64_tr_b16, which transposes 4 x 16 blocks of
+// 16-bit values across each group of 16 lanes.
+//
+// Per slab: fragments of the next 16-wide K step are read while the MFMAs of
+// the current one run; after the third step the waves meet at one barrier
+// (the next slab has landed, the current buffer is no longer read) and the
+// loads of the slab after next go out, a full slab ahead of their use.
+namespace dma {
+constexpr int kBK = 64;                    // bf16 elements of K per slab
+constexpr int kOpBytes = 32768;            // one operand, one slab
+constexpr int kStageBytes = 2 * kOpBytes;
+constexpr int kLdsBytes = 2 * kStageBytes; // 128 KiB
+constexpr uint32_t kOob = 0x80000000u;     // buffer offset beyond num_records: reads 0
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// K-major slab: 256 rows x 128 bytes.  The 16-byte chunk is swizzled by
+// (row / 2) mod 8: any 16 consecutive rows read at one logical chunk then
+// cover all 16 chunk positions of a 256-byte bank line (two rows per line).
+__device__ __forceinline__ int kmaj_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int kmaj_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ kmaj_swz(row)) << 4);
+}
+// MN-major slab: 64 k-rows x 512 bytes; chunk swizzled by 2 (k mod 4)
+__device__ __forceinline__ int mnmaj_off(int krow, int chunk) {
+  return krow * 512 + ((chunk ^ ((krow & 3) << 1)) << 4);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)kOob, 0x00020000);
+}
+
+// One operand's slab = 32 wave-wide 1 KiB blocks, 8 per wave.
+__device__ __forceinline__ void issue_slab(const Operand<uint16_t, true>& op, int64_t mn0,
+                                           int64_t k0, char* dst, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(op.base + mn0 * op.ld + k0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;
+    const int row = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ kmaj_swz(row);            // logical chunk of this lane's slot
+    const bool ok = (k0 + c * 8 < op.k) && (mn0 + row < op.mn);
+    const uint32_t off = ok ? (uint32_t)((row * op.ld + c * 8) * 2) : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void issue_slab(const Operand<uint16_t, false>& op, int64_t mn0,
+                                           int64_t k0, char* dst, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(op.base + k0 * op.ld + mn0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;
+    const int krow = blk * 2 + (lane >> 5);
+    const int c = (lane & 31) ^ ((krow & 3) << 1);
+    const bool ok = (k0 + krow < op.k) && (mn0 + c * 8 < op.mn);
+    const uint32_t off = ok ? (uint32_t)((krow * op.ld + c * 8) * 2) : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+// Fragments of 4 MFMA blocks (32 rows each, starting at tile row `base`) for
+// K step `ks` (16 wide) of the slab at `src`.
+__device__ __forceinline__ void frags(u32x4 (&f)[4], const char* src, int base, int ks, int lane,
+                                      const Operand<uint16_t, true>&) {
+  const int chunk = 2 * ks + (lane >> 5);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    f[b] = *reinterpret_cast<const u32x4*>(src + kmaj_off(base + b * 32 + (lane & 31), chunk));
+}
+
+__device__ __forceinline__ void frags(u32x4 (&f)[4], const char* src, int base, int ks, int lane,
+                                      const Operand<uint16_t, false>&) {
+  // lane l of group G = l/16 sources 4 consecutive mn at k-row e = (l/4)%4 and
+  // column quad q = l%4; after the transpose it holds 4 consecutive k of
+  // mn = 16 (G%2) + l%16.  Two reads give the 8 k of one 32x32x16 fragment.
+  const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+  const int kbase = ks * 16 + 8 * (g >> 1) + e;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int chunk = ((base + b * 32) >> 3) + 2 * (g & 1) + (q >> 1);
+    uint32_t w[4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int krow = kbase + 4 * r;
+      const char* p = src + mnmaj_off(krow, chunk) + (q & 1) * 8;
+      const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+      const uint2 u = __builtin_bit_cast(uint2, v);
+      w[2 * r] = u.x;
+      w[2 * r + 1] = u.y;
+    }
+    f[b] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+}  // namespace dma
+
+template <bool AK, bool BK>
+__device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t, AK>& A,
+                                              const Operand<uint16_t, BK>& B, int64_t m0,
+                                              int64_t n0, int64_t K, char* lds,
+                                              f32x16 (&acc)[4][4]) {
+  using namespace dma;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
+
+  const int64_t nslab = (K + kBK - 1) / kBK;
+  auto issue = [&](int64_t s) {
+    char* st = lds + (int)(s & 1) * kStageBytes;
+    issue_slab(A, m0, s * kBK, st, wave, lane);
+    issue_slab(B, n0, s * kBK, st + kOpBytes, wave, lane);
+  };
+  auto load_frags = [&](u32x4 (&fa)[4], u32x4 (&fb)[4], int64_t s, int ks) {
+    const char* st = lds + (int)(s & 1) * kStageBytes;
+    frags(fa, st, wm * 128, ks, lane, A);
+    frags(fb, st + kOpBytes, wn * 128, ks, lane, B);
+  };
+  auto mfmas = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) mma(acc[mb][nb], fa[mb], fb[nb], uint16_t{});
+  };
+
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt 0: slab 0 landed
+  __builtin_amdgcn_s_barrier();
+  issue(1);                                // slab 1 (all lanes out of range if K <= 64)
+  u32x4 a0[4], b0[4], a1[4], b1[4];
+  load_frags(a0, b0, 0, 0);
+  // sched_barrier(0) keeps each step's fragment reads ahead of the previous
+  // step's MFMAs, so LDS latency hides under 16 MFMAs.
+  for (int64_t s = 0; s < nslab; ++s) {
+    load_frags(a1, b1, s, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(a0, b0, s, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(a1, b1, s, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    // own loads of slab s+1 landed, own reads of this buffer done; after the
+    // barrier the same holds for every wave
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    issue(s + 2);                           // into the buffer just finished
+    load_frags(a0, b0, s + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);            // drain the loads still in flight
+  __builtin_amdgcn_s_barrier();
+}
+
+// One 256 x 256 output tile at (m0, n0), K = [0, K).  All 256 threads must
+// call it; it ends with a barrier, so `lds` is free again on return.
+template <typename T, bool AK, bool BK>
+__device__ __forceinline__ void gemm_tile(const Operand<T, AK>& A, const Operand<T, BK>& B,
+                                          int64_t m0, int64_t n0, int64_t K, char* lds,
+                                          f32x16 (&acc)[4][4]) {
+  if constexpr (sizeof(T) == 2)
+    gemm_tile_dma<AK, BK>(A, B, m0, n0, K, lds, acc);
+  else
+    gemm_tile_regs<T, AK, BK>(A, B, m0, n0, K, lds, acc);
 }
 
 // ---------------------------------------------------------------- tile order

@@ -137,11 +137,11 @@ void k_fwd(FwdArgs<T> a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t n0 = nt * tile::kN;
 
-  int64_t tgt[4];
+  int32_t tgt[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
-    tgt[nb] = tok < a.n ? static_cast<int64_t>(a.targets[tok]) : -1;
+    tgt[nb] = tok < a.n ? a.targets[tok] : -1;
   }
   float m_run[4], d_run[4], s_run[4];
 #pragma unroll
@@ -155,51 +155,44 @@ void k_fwd(FwdArgs<T> a) {
     const int64_t v0 = vt * tile::kM;
     f32x16 acc[4][4];
     gemm_tile(A, B, v0, n0, a.d, lds, acc);
-    const int64_t vw = v0 + wm * 128 + 4 * (lane >> 5);   // v of (mb, r) = vw + mb*32 + 8(r/4) + r%4
+    // tile-local vocabulary row of (mb, r) = vw + mb*32 + 8(r/4) + r%4
+    const int vw = wm * 128 + 4 * (lane >> 5);
+    const int vlim = a.v - v0 < tile::kM ? static_cast<int>(a.v - v0) : tile::kM;
+    const bool full = vlim == tile::kM;
 
-    if (kBias || kSoftcap) {
+    // One token column at a time: 64 logits of this lane, bias and softcap
+    // applied in registers, never written back to the accumulators.
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      float z[64];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t v = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
-          const float b = kBias ? (v < a.v ? ld_elem(a.bias, v) : 0.f) : 0.f;
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            float z = acc[mb][nb][r] + b;
-            if (kSoftcap) z = a.softcap * fast_tanh(z * a.inv_softcap);
-            acc[mb][nb][r] = z;
-          }
+          const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
+          float zz = acc[mb][nb][r];
+          if (kBias) zz += vl < vlim ? ld_elem(a.bias, v0 + vl) : 0.f;
+          if (kSoftcap) zz = a.softcap * fast_tanh(zz * a.inv_softcap);
+          z[mb * 16 + r] = zz;
         }
-    }
-
-    // Target logit: at most one lane-value per row in the whole vocabulary.
+      // Target logit: at most one lane-value per row in the whole vocabulary.
+      const int64_t rel64 = static_cast<int64_t>(tgt[nb]) - v0 - vw;
+      if (rel64 >= 0 && rel64 < 128 && (rel64 & 4) == 0) {
+        const int rel = static_cast<int>(rel64);
+        const int idx = (rel >> 5) * 16 + ((rel >> 3) & 3) * 4 + (rel & 3);
+        float zt = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int64_t rel = tgt[nb] - vw;
-      if (rel >= 0 && rel < 128 && (rel & 4) == 0) {
-        const int idx = static_cast<int>((rel >> 5) * 16 + ((rel >> 3) & 3) * 4 + (rel & 3));
-        float z = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) z = (mb * 16 + r == idx) ? acc[mb][nb][r] : z;
-        a.zt[n0 + wn * 128 + nb * 32 + (lane & 31)] = z;
+        for (int i = 0; i < 64; ++i) zt = i == idx ? z[i] : zt;
+        a.zt[n0 + wn * 128 + nb * 32 + (lane & 31)] = zt;
       }
-    }
-
-    const bool full = v0 + tile::kM <= a.v;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
       float mt = -INFINITY, sz = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool ok = full || (vw + mb * 32 + 8 * (r >> 2) + (r & 3) < a.v);
-          const float z = acc[mb][nb][r];
-          mt = ok ? fmaxf(mt, z) : mt;
-          if (kSumZ) sz += ok ? z : 0.f;
+          const bool ok = full || (vw + mb * 32 + 8 * (r >> 2) + (r & 3) < vlim);
+          mt = ok ? fmaxf(mt, z[mb * 16 + r]) : mt;
+          if (kSumZ) sz += ok ? z[mb * 16 + r] : 0.f;
         }
       if (kSumZ) s_run[nb] += sz;
       if (mt == -INFINITY) continue;
@@ -209,8 +202,8 @@ void k_fwd(FwdArgs<T> a) {
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool ok = full || (vw + mb * 32 + 8 * (r >> 2) + (r & 3) < a.v);
-          const float e = fast_exp2(__builtin_fmaf(acc[mb][nb][r], kLog2e, -m_new));
+          const bool ok = full || (vw + mb * 32 + 8 * (r >> 2) + (r & 3) < vlim);
+          const float e = fast_exp2(__builtin_fmaf(z[mb * 16 + r], kLog2e, -m_new));
           sum += ok ? e : 0.f;
         }
       d_run[nb] = d_run[nb] * fast_exp2(m_run[nb] - m_new) + sum;
@@ -357,57 +350,48 @@ void k_bwd_g(GArgs<T> a) {
   f32x16 acc[4][4];
   gemm_tile(A, B, vl0, n0, a.d, lds, acc);
 
-  const int64_t vw = vl0 + wm * 128 + 4 * (lane >> 5);   // slice-local v of (mb=0, r=0)
-  bool valid[4];
-  float lse2[4], zfac[4];
-  int hit[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
-    const int64_t t = tok < a.n ? static_cast<int64_t>(a.targets[tok]) : -1;
-    valid[nb] = tok < a.n && t != a.ignore_index;
-    const float l = valid[nb] ? a.lse[tok] : 0.f;
-    lse2[nb] = l * kLog2e;
-    zfac[nb] = 1.0f + a.two_s * l;
-    const int64_t rel = t - a.v0 - vw;
-    hit[nb] = (valid[nb] && rel >= 0 && rel < 128 && (rel & 4) == 0)
-                  ? static_cast<int>((rel >> 5) * 16 + ((rel >> 3) & 3) * 4 + (rel & 3))
-                  : -1;
-  }
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
-      const bool vin = vl < a.slice_len;
-      const float b = kBias ? (vin ? ld_elem(a.bias, a.v0 + vl) : 0.f) : 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        float z = acc[mb][nb][r] + b;
-        float dz = 1.0f;
-        if (kSoftcap) {
-          const float th = fast_tanh(z * a.inv_softcap);
-          z = a.softcap * th;
-          dz = 1.0f - th * th;
-        }
-        const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2[nb]));
-        const float sub = (mb * 16 + r == hit[nb]) ? a.eps_over_v + a.keep_target : a.eps_over_v;
-        float gv = __builtin_fmaf(p, zfac[nb], -sub);
-        if (kSoftcap) gv *= dz;
-        acc[mb][nb][r] = (valid[nb] && vin) ? gv : 0.f;
-      }
-    }
+  const int vw = wm * 128 + 4 * (lane >> 5);              // tile-local v of (mb = 0, r = 0)
+  const int vlim = a.slice_len - vl0 < tile::kM ? static_cast<int>(a.slice_len - vl0) : tile::kM;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
     if (tok >= a.n) continue;
-    T* row = a.g + tok * a.ldg;
+    const int32_t t = a.targets[tok];
+    const bool valid = t != a.ignore_index;
+    const float l = valid ? a.lse[tok] : 0.f;
+    const float lse2 = l * kLog2e;
+    const float zfac = 1.0f + a.two_s * l;
+    const int64_t rel64 = static_cast<int64_t>(t) - a.v0 - vl0 - vw;
+    const int hit = (valid && rel64 >= 0 && rel64 < 128 && (rel64 & 4) == 0)
+                        ? static_cast<int>((rel64 >> 5) * 16 + ((rel64 >> 3) & 3) * 4 + (rel64 & 3))
+                        : -1;
+    T* row = a.g + tok * a.ldg + vl0;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store4(row + vw + mb * 32 + 8 * q, acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
-               acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+      for (int q = 0; q < 4; ++q) {
+        float gv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * q + j;
+          const int vl = vw + mb * 32 + 8 * q + j;
+          const bool vin = vl < vlim;
+          float z = acc[mb][nb][r];
+          if (kBias) z += vin ? ld_elem(a.bias, a.v0 + vl0 + vl) : 0.f;
+          float dz = 1.0f;
+          if (kSoftcap) {
+            const float th = fast_tanh(z * a.inv_softcap);
+            z = a.softcap * th;
+            dz = 1.0f - th * th;
+          }
+          const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2));
+          const float sub = (mb * 16 + r == hit) ? a.eps_over_v + a.keep_target : a.eps_over_v;
+          float g = __builtin_fmaf(p, zfac, -sub);
+          if (kSoftcap) g *= dz;
+          gv[j] = (valid && vin) ? g : 0.f;
+        }
+        store4(row + vw + mb * 32 + 8 * q, gv[0], gv[1], gv[2], gv[3]);
+      }
   }
 }
 
