@@ -20,8 +20,8 @@ using flce::Ctl;
 namespace tile = flce::tile;
 
 constexpr int64_t kAlign = 256;
-constexpr int64_t kDefaultSlice = 8192;    // backward vocabulary slice width
-constexpr int64_t kDbSplits = 64;          // token blocks of the bias-gradient column sums
+constexpr int64_t kMaxSlice = 8192;          // default backward vocabulary slice width ...
+constexpr int64_t kSliceBytes = 512ll << 20; // ... shrunk until one G slice fits in 512 MiB
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -32,10 +32,11 @@ struct Layout {
   int64_t elem;           // bytes per X/W element
   int64_t v_tiles, n_tiles, tiles_per_chunk, n_chunks;
   int64_t slice, ldg;     // backward slice width (multiple of 256) and G row pitch
+  int64_t ldt;            // token pitch of X^T and G^T (N rounded up to 256)
   int64_t n_merge_blocks;
   // byte offsets from the workspace base
   int64_t ctl, zt, part_m, part_d, part_s, block_sums, fwd_end;
-  int64_t g, dx_acc, db_part, bwd_end;
+  int64_t g, gt, xt, wt, dx_acc, bwd_end;
 };
 
 Layout make_layout(const flce_params& p) {
@@ -50,9 +51,14 @@ Layout make_layout(const flce_params& p) {
   tpc = tpc < 1 ? 1 : (tpc > 8 ? 8 : tpc);
   L.tiles_per_chunk = tpc;
   L.n_chunks = cdiv(L.v_tiles, tpc);
-  const int64_t slice_req = p.vocab_slice > 0 ? p.vocab_slice : kDefaultSlice;
-  L.slice = round_up(slice_req < p.v ? slice_req : p.v, tile::kM);
+  int64_t slice = p.vocab_slice;
+  if (slice <= 0) {
+    slice = kMaxSlice;
+    while (slice > tile::kM && p.n * slice * L.elem > kSliceBytes) slice /= 2;
+  }
+  L.slice = round_up(slice < p.v ? slice : p.v, tile::kM);
   L.ldg = L.slice;
+  L.ldt = round_up(p.n, tile::kN);
   L.n_merge_blocks = cdiv(p.n, 256);
 
   int64_t off = 0;
@@ -69,10 +75,12 @@ Layout make_layout(const flce_params& p) {
   // once its loss is reduced).
   off = base;
   L.g = off;           off = round_up(off + L.elem * p.n * L.ldg, kAlign);
+  L.gt = off;          off = round_up(off + L.elem * L.ldg * L.ldt, kAlign);
+  L.xt = off;          off = round_up(off + L.elem * p.d * L.ldt, kAlign);
+  L.wt = off;          off = round_up(off + L.elem * p.d * L.ldg, kAlign);
   const bool multi_slice = L.slice < p.v;
   L.dx_acc = off;
   if (p.dtype == FLCE_DTYPE_BF16 && multi_slice) off = round_up(off + 4 * p.n * p.d, kAlign);
-  L.db_part = off;     off = round_up(off + 4 * kDbSplits * L.ldg, kAlign);
   L.bwd_end = off;
   return L;
 }
@@ -93,7 +101,9 @@ flce_status check_params(const flce_params* p) {
   if (!(p->lse_square_scale >= 0.f) || !std::isfinite(p->lse_square_scale))
     return FLCE_ERR_INVALID_ARGUMENT;
   if (!(p->softcap >= 0.f) || !std::isfinite(p->softcap)) return FLCE_ERR_INVALID_ARGUMENT;
-  if (p->vocab_slice < 0) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->vocab_slice < 0 || p->vocab_slice > (1 << 20)) return FLCE_ERR_INVALID_ARGUMENT;
+  // per-tile buffer offsets are 32-bit: 256 rows of the widest K-major operand
+  if (p->d > (1 << 20) || p->n > (1 << 22)) return FLCE_ERR_INVALID_ARGUMENT;
   // byte sizes of the largest tensors must fit comfortably in int64
   const double big = static_cast<double>(p->n) * static_cast<double>(p->v) + p->n * (double)p->d +
                      p->v * (double)p->d;
@@ -223,6 +233,15 @@ void launch_g(const flce::GArgs<T>& a, hipStream_t s) {
 }
 
 template <typename T>
+void transpose(const T* in, int64_t rows, int64_t cols, int64_t ld_in, T* out, int64_t out_rows,
+               int64_t ld_out_used, int64_t ld_out, hipStream_t s) {
+  const int64_t gx = cdiv(ld_out_used, 64), gy = cdiv(out_rows, 64);
+  if (gx <= 0 || gy <= 0) return;
+  hipLaunchKernelGGL((flce::k_transpose<T>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
+                     dim3(256), 0, s, in, rows, cols, ld_in, out, out_rows, ld_out);
+}
+
+template <typename T>
 flce_status run_backward(const flce_params& p, const Layout& L, const void* x, const void* w,
                          const void* bias, const int32_t* targets, const float* lse,
                          const float* grad_output, void* dx, float* dw, float* dbias, void* ws,
@@ -232,21 +251,30 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
   hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
                      grad_output, mean ? 1 : 0, ctl);
   T* g = reinterpret_cast<T*>(at(ws, L.g));
+  T* gt = reinterpret_cast<T*>(at(ws, L.gt));
+  T* xt = reinterpret_cast<T*>(at(ws, L.xt));
+  T* wt = reinterpret_cast<T*>(at(ws, L.wt));
   float* dx_acc = std::is_same<T, float>::value ? static_cast<float*>(dx)
                                                 : reinterpret_cast<float*>(at(ws, L.dx_acc));
-  float* db_part = reinterpret_cast<float*>(at(ws, L.db_part));
+  const T* X = static_cast<const T*>(x);
+  const T* W = static_cast<const T*>(w);
+  // X^T [d][ldt], tokens >= n zero
+  transpose<T>(X, p.n, p.d, p.d, xt, p.d, L.ldt, L.ldt, s);
   const int64_t n_slices = cdiv(p.v, L.slice);
   const int64_t d_tiles = cdiv(p.d, tile::kM);
+  const int64_t kdim_n = round_up(p.n, 8);
   const bool has_bias = bias != nullptr;
   for (int64_t si = 0; si < n_slices; ++si) {
     const int64_t v0 = si * L.slice;
     const int64_t len = (p.v - v0) < L.slice ? (p.v - v0) : L.slice;
     const int64_t s_tiles = cdiv(len, tile::kM);
     const int64_t gcols = s_tiles * tile::kM;
+    // W^T of the slice [d][ldg], vocabulary >= len zero
+    transpose<T>(W + v0 * p.d, len, p.d, p.d, wt, p.d, gcols, L.ldg, s);
     if (p.n > 0) {
       flce::GArgs<T> ga{};
-      ga.x = static_cast<const T*>(x);
-      ga.w = static_cast<const T*>(w);
+      ga.x = X;
+      ga.w = W;
       ga.bias = static_cast<const T*>(bias);
       ga.targets = targets;
       ga.lse = lse;
@@ -262,7 +290,9 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
       ga.v0 = v0;
       ga.slice_len = len;
       ga.ldg = L.ldg;
+      ga.ldt = L.ldt;
       ga.g = g;
+      ga.gt = gt;
       ga.n_tiles = L.n_tiles;
       ga.s_tiles = s_tiles;
       ga.grid = grid8(L.n_tiles * s_tiles);
@@ -275,13 +305,13 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
       }
     }
     flce::DwArgs<T> wa{};
-    wa.x = static_cast<const T*>(x);
-    wa.g = g;
-    wa.n = p.n;
+    wa.xt = xt;
+    wa.gt = gt;
+    wa.kdim = kdim_n;
     wa.d = p.d;
     wa.v0 = v0;
     wa.slice_len = len;
-    wa.ldg = L.ldg;
+    wa.ldt = L.ldt;
     wa.gcols = gcols;
     wa.ctl = ctl;
     wa.dw = dw;
@@ -292,12 +322,10 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
                        s, wa);
     if (p.n > 0) {
       flce::DxArgs<T> xa{};
-      xa.w = static_cast<const T*>(w);
+      xa.wt = wt;
       xa.g = g;
       xa.n = p.n;
       xa.d = p.d;
-      xa.v = p.v;
-      xa.v0 = v0;
       xa.kdim = gcols;
       xa.ldg = L.ldg;
       xa.ctl = ctl;
@@ -311,15 +339,10 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
       hipLaunchKernelGGL((flce::k_dx<T>), dim3(static_cast<unsigned>(xa.grid)), dim3(tile::kThreads),
                          0, s, xa);
     }
-    if (has_bias) {
-      const int64_t rps = cdiv(p.n > 0 ? p.n : 1, kDbSplits);
-      hipLaunchKernelGGL((flce::k_db_partial<T>), dim3(static_cast<unsigned>(cdiv(gcols, 256)),
-                                                       static_cast<unsigned>(kDbSplits)),
-                         dim3(256), 0, s, static_cast<const T*>(g), p.n, L.ldg, gcols, rps, db_part);
-      hipLaunchKernelGGL(flce::k_db_final, dim3(static_cast<unsigned>(cdiv(len, 256))), dim3(256), 0, s,
-                         static_cast<const float*>(db_part), kDbSplits, gcols, v0, len,
-                         static_cast<const Ctl*>(ctl), dbias);
-    }
+    if (has_bias)
+      hipLaunchKernelGGL((flce::k_db<T>), dim3(static_cast<unsigned>(cdiv(len, 4))), dim3(256), 0, s,
+                         static_cast<const T*>(gt), L.ldt, p.n, v0, len, static_cast<const Ctl*>(ctl),
+                         dbias);
   }
   return launched();
 }

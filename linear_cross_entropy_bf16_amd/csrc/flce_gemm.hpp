@@ -2,14 +2,10 @@
 // cross-entropy (forward logits, recomputed logits, dW and dX).
 //
 // C[m, n] = sum_k A[m, k] * B[n, k] over one 256 x 256 output tile, fp32
-// accumulation, with either operand stored K-major (element (r, k) at
-// base[r * ld + k]) or MN-major (element (r, k) at base[k * ld + r]).  The
-// MN-major case is how the backward reads X and W "through a stride swap"
-// without ever materialising X^T or W^T (page "Cutting LLM Memory by 84%",
-// "Kernel Implementation", the stride-swap note): the 16-byte global loads
-// stay coalesced along the contiguous axis and an 8 x 8 register transpose
-// turns them into K-contiguous LDS rows, so every MFMA fragment read is one
-// 16-byte LDS read.
+// accumulation, both operands stored K-major (element (r, k) at
+// base[r * ld + k]); the backward materialises the transposed operands it
+// needs (X^T once, W^T per vocabulary slice, G in both orientations) because
+// K-major tiles are what this engine streams fastest.
 //
 // Work split: 256 threads = 4 wave64s in a 2 x 2 grid, each wave owning a
 // 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (bf16) or
@@ -57,19 +53,19 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * tile::kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
 }
 
-template <typename T, bool KMajor>
+// K-major operand view: element (r, k) at base[r * ld + k].
+template <typename T>
 struct Operand {
   const T* base;
-  int64_t ld;   // elements between consecutive stored rows
-  int64_t mn;   // valid extent along M (or N); rows at or beyond it read as 0
-  int64_t k;    // valid extent along K; columns at or beyond it read as 0
+  int64_t ld;   // elements between consecutive rows
+  int64_t mn;   // valid rows (M or N extent); rows at or beyond it read as 0
+  int64_t k;    // valid extent along K (multiple of 8); columns beyond read as 0
 };
 
 // ---------------------------------------------------------------- loaders
-// K-major: thread t loads chunk (t % 8) of rows t/8 + 32 i, i = 0..7.
-// The extent along K must be a multiple of the chunk width (host-checked).
+// Thread t loads chunk (t % 8) of rows t/8 + 32 i, i = 0..7.
 template <typename T>
-__device__ __forceinline__ void load_slab(u32x4 (&r)[8], const Operand<T, true>& op,
+__device__ __forceinline__ void load_slab(u32x4 (&r)[8], const Operand<T>& op,
                                           int64_t mn0, int64_t k0, int tid) {
   const int64_t k = k0 + (int64_t)(tid & 7) * Vec<T>::n;
 #pragma unroll
@@ -82,78 +78,10 @@ __device__ __forceinline__ void load_slab(u32x4 (&r)[8], const Operand<T, true>&
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void store_slab(char* s, const u32x4 (&r)[8],
-                                           const Operand<T, true>&, int tid) {
+__device__ __forceinline__ void store_slab(char* s, const u32x4 (&r)[8], int tid) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     *reinterpret_cast<u32x4*>(s + lds_off((tid >> 3) + 32 * i, tid & 7)) = r[i];
-}
-
-// MN-major bf16: thread t owns the 8 x 8 block of K rows 8 (t/32) .. +7 and
-// M columns 8 (t%32) .. +7; the M extent must be a multiple of 8.
-__device__ __forceinline__ void load_slab(u32x4 (&r)[8], const Operand<uint16_t, false>& op,
-                                          int64_t mn0, int64_t k0, int tid) {
-  const int64_t mn = mn0 + (int64_t)(tid & 31) * 8;
-  const int64_t kb = k0 + (int64_t)(tid >> 5) * 8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t k = kb + i;
-    if (k < op.k && mn < op.mn)
-      r[i] = *reinterpret_cast<const u32x4*>(op.base + k * op.ld + mn);
-    else
-      r[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-__device__ __forceinline__ void store_slab(char* s, const u32x4 (&r)[8],
-                                           const Operand<uint16_t, false>&, int tid) {
-  const int kc = tid >> 5;       // K chunk of the slab
-  const int mb = tid & 31;       // 8-column group
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {  // column j of the block becomes tile row 8 mb + j
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = r[2 * q][j >> 1];      // K row 2q
-      const uint32_t hi = r[2 * q + 1][j >> 1];  // K row 2q + 1
-      o[q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    *reinterpret_cast<u32x4*>(s + lds_off(mb * 8 + j, kc)) = o;
-  }
-}
-
-// MN-major fp32: thread t owns two 4 x 4 blocks b = t and t + 256, each the
-// K rows 4 (b/64) .. +3 and M columns 4 (b%64) .. +3; M extent multiple of 4.
-__device__ __forceinline__ void load_slab(u32x4 (&r)[8], const Operand<float, false>& op,
-                                          int64_t mn0, int64_t k0, int tid) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int b = tid + 256 * h;
-    const int64_t mn = mn0 + (int64_t)(b & 63) * 4;
-    const int64_t kb = k0 + (int64_t)(b >> 6) * 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t k = kb + i;
-      if (k < op.k && mn < op.mn)
-        r[4 * h + i] = *reinterpret_cast<const u32x4*>(op.base + k * op.ld + mn);
-      else
-        r[4 * h + i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-__device__ __forceinline__ void store_slab(char* s, const u32x4 (&r)[8],
-                                           const Operand<float, false>&, int tid) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int b = tid + 256 * h;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 o{r[4 * h][j], r[4 * h + 1][j], r[4 * h + 2][j], r[4 * h + 3][j]};
-      *reinterpret_cast<u32x4*>(s + lds_off((b & 63) * 4 + j, b >> 6)) = o;
-    }
-  }
 }
 
 // ---------------------------------------------------------------- MFMA
@@ -196,8 +124,8 @@ __device__ __forceinline__ void compute_slab(const char* sA, const char* sB, f32
 
 // Register-staged path (used for fp32): the next slab's global loads land in
 // VGPRs while the current slab is multiplied, then go to the other LDS buffer.
-template <typename T, bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile_regs(const Operand<T, AK>& A, const Operand<T, BK>& B,
+template <typename T>
+__device__ __forceinline__ void gemm_tile_regs(const Operand<T>& A, const Operand<T>& B,
                                           int64_t m0, int64_t n0, int64_t K, char* lds,
                                           f32x16 (&acc)[4][4]) {
   const int tid = threadIdx.x;
@@ -216,8 +144,8 @@ __device__ __forceinline__ void gemm_tile_regs(const Operand<T, AK>& A, const Op
   u32x4 ra[8], rb[8];
   load_slab(ra, A, m0, 0, tid);
   load_slab(rb, B, n0, 0, tid);
-  store_slab(lds, ra, A, tid);
-  store_slab(lds + tile::kOpBytes, rb, B, tid);
+  store_slab(lds, ra, tid);
+  store_slab(lds + tile::kOpBytes, rb, tid);
   __syncthreads();
   for (int64_t s = 0; s < nslab; ++s) {
     const bool more = s + 1 < nslab;
@@ -229,8 +157,8 @@ __device__ __forceinline__ void gemm_tile_regs(const Operand<T, AK>& A, const Op
     compute_slab<T>(cur, cur + tile::kOpBytes, acc, wm, wn, lane);
     if (more) {
       char* nxt = lds + ((s + 1) & 1) * tile::kStageBytes;
-      store_slab(nxt, ra, A, tid);
-      store_slab(nxt + tile::kOpBytes, rb, B, tid);
+      store_slab(nxt, ra, tid);
+      store_slab(nxt + tile::kOpBytes, rb, tid);
     }
     __syncthreads();
   }
@@ -239,12 +167,9 @@ __device__ __forceinline__ void gemm_tile_regs(const Operand<T, AK>& A, const Op
 // ---------------------------------------------------------------- bf16 DMA path
 // bf16 tiles travel global -> LDS with buffer_load ... lds (no staging
 // registers, no LDS store instructions), double-buffered in 64-wide K slabs
-// so every K-major row segment is a whole 128-byte line.  Out-of-range rows
-// and columns are loads with an out-of-range buffer offset, which the
-// hardware turns into zeros, so the loop has no branches.  MN-major operands
-// stay as they are in memory ([k][mn] rows of 512 bytes) and become MFMA
-// fragments through ds_read_b64_tr_b16, which transposes 4 x 16 blocks of
-// 16-bit values across each group of 16 lanes.
+// so every row segment is a whole 128-byte line.  Out-of-range rows and
+// columns are loads with an out-of-range buffer offset, which the hardware
+// turns into zeros, so the loop has no branches.
 //
 // Per slab: fragments of the next 16-wide K step are read while the MFMAs of
 // the current one run; after the third step the waves meet at one barrier
@@ -268,17 +193,12 @@ __device__ __forceinline__ int kmaj_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int kmaj_off(int row, int chunk) {
   return row * 128 + ((chunk ^ kmaj_swz(row)) << 4);
 }
-// MN-major slab: 64 k-rows x 512 bytes; chunk swizzled by 2 (k mod 4)
-__device__ __forceinline__ int mnmaj_off(int krow, int chunk) {
-  return krow * 512 + ((chunk ^ ((krow & 3) << 1)) << 4);
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)kOob, 0x00020000);
 }
 
 // One operand's slab = 32 wave-wide 1 KiB blocks, 8 per wave.
-__device__ __forceinline__ void issue_slab(const Operand<uint16_t, true>& op, int64_t mn0,
+__device__ __forceinline__ void issue_slab(const Operand<uint16_t>& op, int64_t mn0,
                                            int64_t k0, char* dst, int wave, int lane) {
   const __amdgpu_buffer_rsrc_t r = rsrc(op.base + mn0 * op.ld + k0);
 #pragma unroll
@@ -292,59 +212,32 @@ __device__ __forceinline__ void issue_slab(const Operand<uint16_t, true>& op, in
   }
 }
 
-__device__ __forceinline__ void issue_slab(const Operand<uint16_t, false>& op, int64_t mn0,
-                                           int64_t k0, char* dst, int wave, int lane) {
-  const __amdgpu_buffer_rsrc_t r = rsrc(op.base + k0 * op.ld + mn0);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = wave * 8 + i;
-    const int krow = blk * 2 + (lane >> 5);
-    const int c = (lane & 31) ^ ((krow & 3) << 1);
-    const bool ok = (k0 + krow < op.k) && (mn0 + c * 8 < op.mn);
-    const uint32_t off = ok ? (uint32_t)((krow * op.ld + c * 8) * 2) : kOob;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, off, 0, 0, 0);
-  }
-}
-
 // Fragments of 4 MFMA blocks (32 rows each, starting at tile row `base`) for
 // K step `ks` (16 wide) of the slab at `src`.
-__device__ __forceinline__ void frags(u32x4 (&f)[4], const char* src, int base, int ks, int lane,
-                                      const Operand<uint16_t, true>&) {
+__device__ __forceinline__ void frags(u32x4 (&f)[4], const char* src, int base, int ks, int lane) {
   const int chunk = 2 * ks + (lane >> 5);
 #pragma unroll
   for (int b = 0; b < 4; ++b)
     f[b] = *reinterpret_cast<const u32x4*>(src + kmaj_off(base + b * 32 + (lane & 31), chunk));
 }
 
-__device__ __forceinline__ void frags(u32x4 (&f)[4], const char* src, int base, int ks, int lane,
-                                      const Operand<uint16_t, false>&) {
-  // lane l of group G = l/16 sources 4 consecutive mn at k-row e = (l/4)%4 and
-  // column quad q = l%4; after the transpose it holds 4 consecutive k of
-  // mn = 16 (G%2) + l%16.  Two reads give the 8 k of one 32x32x16 fragment.
-  const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
-  const int kbase = ks * 16 + 8 * (g >> 1) + e;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int chunk = ((base + b * 32) >> 3) + 2 * (g & 1) + (q >> 1);
-    uint32_t w[4];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int krow = kbase + 4 * r;
-      const char* p = src + mnmaj_off(krow, chunk) + (q & 1) * 8;
-      const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-      const uint2 u = __builtin_bit_cast(uint2, v);
-      w[2 * r] = u.x;
-      w[2 * r + 1] = u.y;
-    }
-    f[b] = u32x4{w[0], w[1], w[2], w[3]};
+// Scheduling groups (masks: 0x008 MFMA, 0x100 DS read, 0x020 VMEM read): a
+// fragment read and, in the last step of a slab, a slab load after each of the
+// step's 16 MFMAs.
+template <bool kLoads, int I = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < 16) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    interleave<kLoads, I + 1>();
   }
 }
 
 }  // namespace dma
 
-template <bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t, AK>& A,
-                                              const Operand<uint16_t, BK>& B, int64_t m0,
+__device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
+                                              const Operand<uint16_t>& B, int64_t m0,
                                               int64_t n0, int64_t K, char* lds,
                                               f32x16 (&acc)[4][4]) {
   using namespace dma;
@@ -367,8 +260,8 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t, AK>& A,
   };
   auto load_frags = [&](u32x4 (&fa)[4], u32x4 (&fb)[4], int64_t s, int ks) {
     const char* st = lds + (int)(s & 1) * kStageBytes;
-    frags(fa, st, wm * 128, ks, lane, A);
-    frags(fb, st + kOpBytes, wn * 128, ks, lane, B);
+    frags(fa, st, wm * 128, ks, lane);
+    frags(fb, st + kOpBytes, wn * 128, ks, lane);
   };
   auto mfmas = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
 #pragma unroll
@@ -383,30 +276,28 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t, AK>& A,
   issue(1);                                // slab 1 (all lanes out of range if K <= 64)
   u32x4 a0[4], b0[4], a1[4], b1[4];
   load_frags(a0, b0, 0, 0);
-  // sched_barrier(0) keeps each step's fragment reads ahead of the previous
-  // step's MFMAs, so LDS latency hides under 16 MFMAs.
+  // Within each 16-wide K step the fragment reads of the next step (and, in
+  // the last step, the loads of the slab after next) are interleaved one per
+  // MFMA, so the matrix core never waits behind a burst of memory
+  // instructions issued by its only wave.
   for (int64_t s = 0; s < nslab; ++s) {
     load_frags(a1, b1, s, 1);
-    __builtin_amdgcn_sched_barrier(0);
     mfmas(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave<false>();
     load_frags(a0, b0, s, 2);
-    __builtin_amdgcn_sched_barrier(0);
     mfmas(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave<false>();
     load_frags(a1, b1, s, 3);
-    __builtin_amdgcn_sched_barrier(0);
     mfmas(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave<false>();
     // own loads of slab s+1 landed, own reads of this buffer done; after the
     // barrier the same holds for every wave
     __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
     issue(s + 2);                           // into the buffer just finished
     load_frags(a0, b0, s + 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
     mfmas(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave<true>();
   }
   __builtin_amdgcn_s_waitcnt(0);            // drain the loads still in flight
   __builtin_amdgcn_s_barrier();
@@ -414,14 +305,13 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t, AK>& A,
 
 // One 256 x 256 output tile at (m0, n0), K = [0, K).  All 256 threads must
 // call it; it ends with a barrier, so `lds` is free again on return.
-template <typename T, bool AK, bool BK>
-__device__ __forceinline__ void gemm_tile(const Operand<T, AK>& A, const Operand<T, BK>& B,
-                                          int64_t m0, int64_t n0, int64_t K, char* lds,
-                                          f32x16 (&acc)[4][4]) {
+template <typename T>
+__device__ __forceinline__ void gemm_tile(const Operand<T>& A, const Operand<T>& B, int64_t m0,
+                                          int64_t n0, int64_t K, char* lds, f32x16 (&acc)[4][4]) {
   if constexpr (sizeof(T) == 2)
-    gemm_tile_dma<AK, BK>(A, B, m0, n0, K, lds, acc);
+    gemm_tile_dma(A, B, m0, n0, K, lds, acc);
   else
-    gemm_tile_regs<T, AK, BK>(A, B, m0, n0, K, lds, acc);
+    gemm_tile_regs<T>(A, B, m0, n0, K, lds, acc);
 }
 
 // ---------------------------------------------------------------- tile order

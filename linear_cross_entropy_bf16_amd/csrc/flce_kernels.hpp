@@ -6,10 +6,12 @@
 //                 target logit captured by the one tile that holds it
 //   k_merge       partials -> lse, per-row loss, per-block loss sums
 //   k_loss_final  fixed-order sum of the block sums -> scalar loss
-//   k_bwd_g       recomputed logits of one vocabulary slice -> G slice
+//   k_transpose   X^T once per backward, W^T once per vocabulary slice
+//   k_bwd_g       recomputed logits of one vocabulary slice -> G slice, in
+//                 both orientations
 //   k_dw          dW[slice] = scale G_slice^T X   (K = N, written once)
 //   k_dx          dX (+)= scale G_slice W_slice   (K = slice width)
-//   k_db_partial / k_db_final   db[slice] = scale sum_n G_slice
+//   k_db          db[slice] = scale sum_n G_slice
 //
 // Every reduction has a fixed order and no kernel uses global atomics, so
 // results are bitwise reproducible run to run.
@@ -147,8 +149,8 @@ void k_fwd(FwdArgs<T> a) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) { m_run[nb] = -INFINITY; d_run[nb] = 0.f; s_run[nb] = 0.f; }
 
-  const Operand<T, true> A{a.w, a.d, a.v, a.d};   // rows: vocabulary
-  const Operand<T, true> B{a.x, a.d, a.n, a.d};   // rows: tokens
+  const Operand<T> A{a.w, a.d, a.v, a.d};   // rows: vocabulary
+  const Operand<T> B{a.x, a.d, a.n, a.d};   // rows: tokens
   const int64_t vt_end = (ch + 1) * a.tiles_per_chunk < a.v_tiles ? (ch + 1) * a.tiles_per_chunk
                                                                    : a.v_tiles;
   for (int64_t vt = ch * a.tiles_per_chunk; vt < vt_end; ++vt) {
@@ -311,6 +313,37 @@ __global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ b
 }
 
 // ------------------------------------------------------------------- backward
+// Every backward contraction reads both operands K-major (K contiguous), the
+// layout the MFMA engine streams fastest: X^T is materialised once per
+// backward, W^T once per vocabulary slice, and the G slice is written in both
+// orientations ([tokens][slice] for dX, [slice][tokens] for dW and db).
+
+// out[c][r] = in[r][c] for r < rows, c < cols; 0 for the padding r < ld_out,
+// c < out_rows.  64 x 64 tiles through LDS, coalesced on both sides.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, int64_t rows,
+                                                   int64_t cols, int64_t ld_in,
+                                                   T* __restrict__ out, int64_t out_rows,
+                                                   int64_t ld_out) {
+  __shared__ T t[64][65];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rr = ty + 4 * i;
+    const int64_t r = r0 + rr, c = c0 + tx;
+    t[rr][tx] = (r < rows && c < cols) ? in[r * ld_in + c] : T(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int cc = ty + 4 * i;
+    const int64_t c = c0 + cc, r = r0 + tx;
+    if (c < out_rows && r < ld_out) out[c * ld_out + r] = t[tx][cc];
+  }
+}
+
 template <typename T>
 struct GArgs {
   const T* x;
@@ -324,10 +357,16 @@ struct GArgs {
   float keep_target;    // 1 - eps
   float eps_over_v;
   float two_s;          // 2 s (z-loss)
-  int64_t v0, slice_len, ldg;
-  T* g;                 // [n, ldg] G slice, columns >= slice_len written as 0
+  int64_t v0, slice_len, ldg, ldt;
+  T* g;                 // [n, ldg]       G slice, columns >= slice_len written as 0
+  T* gt;                // [gcols, ldt]   the same slice transposed, tokens >= n as 0
   int64_t n_tiles, s_tiles, grid;
 };
+
+__device__ __forceinline__ void store1(uint16_t* p, float a) {
+  *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
+}
+__device__ __forceinline__ void store1(float* p, float a) { *p = a; }
 
 // Recompute one 256 x 256 logits tile of the slice and turn it into
 // G = [p (1 + 2 s lse) - (1-eps) onehot - eps/V] (1 - (z/c)^2), p = exp(z - lse)
@@ -345,8 +384,8 @@ void k_bwd_g(GArgs<T> a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t n0 = nt * tile::kN, vl0 = st * tile::kM;
 
-  const Operand<T, true> A{a.w + a.v0 * a.d, a.d, a.v - a.v0, a.d};
-  const Operand<T, true> B{a.x, a.d, a.n, a.d};
+  const Operand<T> A{a.w + a.v0 * a.d, a.d, a.v - a.v0, a.d};
+  const Operand<T> B{a.x, a.d, a.n, a.d};
   f32x16 acc[4][4];
   gemm_tile(A, B, vl0, n0, a.d, lds, acc);
 
@@ -355,9 +394,9 @@ void k_bwd_g(GArgs<T> a) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
-    if (tok >= a.n) continue;
-    const int32_t t = a.targets[tok];
-    const bool valid = t != a.ignore_index;
+    const bool tin = tok < a.n;
+    const int32_t t = tin ? a.targets[tok] : a.ignore_index;
+    const bool valid = tin && t != a.ignore_index;
     const float l = valid ? a.lse[tok] : 0.f;
     const float lse2 = l * kLog2e;
     const float zfac = 1.0f + a.two_s * l;
@@ -366,6 +405,7 @@ void k_bwd_g(GArgs<T> a) {
                         ? static_cast<int>((rel64 >> 5) * 16 + ((rel64 >> 3) & 3) * 4 + (rel64 & 3))
                         : -1;
     T* row = a.g + tok * a.ldg + vl0;
+    T* col = a.gt + vl0 * a.ldt + tok;      // element (v, tok) at col[v * ldt]
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -389,17 +429,18 @@ void k_bwd_g(GArgs<T> a) {
           float g = __builtin_fmaf(p, zfac, -sub);
           if (kSoftcap) g *= dz;
           gv[j] = (valid && vin) ? g : 0.f;
+          store1(col + static_cast<int64_t>(vl) * a.ldt, gv[j]);   // tok < ldt always
         }
-        store4(row + vw + mb * 32 + 8 * q, gv[0], gv[1], gv[2], gv[3]);
+        if (tin) store4(row + vw + mb * 32 + 8 * q, gv[0], gv[1], gv[2], gv[3]);
       }
   }
 }
 
 template <typename T>
 struct DwArgs {
-  const T* x;           // [n, d]
-  const T* g;           // [n, ldg]
-  int64_t n, d, v0, slice_len, ldg, gcols;
+  const T* xt;          // [d, ldt]      X^T, tokens >= n are 0
+  const T* gt;          // [gcols, ldt]  G^T slice
+  int64_t kdim, d, v0, slice_len, ldt, gcols;
   const Ctl* ctl;
   float* dw;            // [v, d]
   int64_t d_tiles, s_tiles, grid;
@@ -421,10 +462,10 @@ void k_dw(DwArgs<T> a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const Operand<T, false> A{a.x, a.d, a.d, a.n};          // (d, n) at x[n*D + d]
-  const Operand<T, false> B{a.g, a.ldg, a.gcols, a.n};    // (v, n) at g[n*ldg + v]
+  const Operand<T> A{a.xt, a.ldt, a.d, a.kdim};       // (d, n) at xt[d*ldt + n]
+  const Operand<T> B{a.gt, a.ldt, a.gcols, a.kdim};   // (v, n) at gt[v*ldt + n]
   f32x16 acc[4][4];
-  gemm_tile(A, B, dt * tile::kM, st * tile::kN, a.n, lds, acc);
+  gemm_tile(A, B, dt * tile::kM, st * tile::kN, a.kdim, lds, acc);
 
   const float scale = a.ctl->scale;
 #pragma unroll
@@ -446,9 +487,9 @@ void k_dw(DwArgs<T> a) {
 
 template <typename T>
 struct DxArgs {
-  const T* w;           // [v, d]
+  const T* wt;          // [d, ldg]  W^T slice, vocabulary >= slice length is 0
   const T* g;           // [n, ldg]
-  int64_t n, d, v, v0, kdim, ldg;
+  int64_t n, d, kdim, ldg;
   const Ctl* ctl;
   float* acc_buf;       // [n, d] fp32 running sum over slices
   T* dx;                // [n, d]
@@ -470,8 +511,8 @@ void k_dx(DxArgs<T> a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const Operand<T, false> A{a.w + a.v0 * a.d, a.d, a.d, a.v - a.v0};   // (d, v) at w[v*D + d]
-  const Operand<T, true> B{a.g, a.ldg, a.n, a.kdim};                  // (n, v) at g[n*ldg + v]
+  const Operand<T> A{a.wt, a.ldg, a.d, a.kdim};   // (d, v) at wt[d*ldg + v]
+  const Operand<T> B{a.g, a.ldg, a.n, a.kdim};    // (n, v) at g[n*ldg + v]
   f32x16 acc[4][4];
   gemm_tile(A, B, dt * tile::kM, nt * tile::kN, a.kdim, lds, acc);
 
@@ -501,29 +542,21 @@ void k_dx(DxArgs<T> a) {
   }
 }
 
-// Column sums of the G slice over token blocks, then over blocks in order.
+// db[v0 + v] = scale sum_n G^T[v, n]: one wave per vocabulary row, lanes
+// striding over the tokens, then a fixed-order wave reduction.
 template <typename T>
-__global__ __launch_bounds__(256) void k_db_partial(const T* __restrict__ g, int64_t n, int64_t ldg,
-                                                    int64_t cols, int64_t rows_per_split,
-                                                    float* __restrict__ part) {
-  const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (col >= cols) return;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per_split;
-  const int64_t r1 = r0 + rows_per_split < n ? r0 + rows_per_split : n;
+__global__ __launch_bounds__(256) void k_db(const T* __restrict__ gt, int64_t ldt, int64_t n,
+                                            int64_t v0, int64_t slice_len,
+                                            const Ctl* __restrict__ ctl, float* __restrict__ db) {
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (v >= slice_len) return;
+  const int lane = threadIdx.x & 63;
+  const T* row = gt + v * ldt;
   float s = 0.f;
-  for (int64_t r = r0; r < r1; ++r) s += ld_elem(g, r * ldg + col);
-  part[static_cast<int64_t>(blockIdx.y) * cols + col] = s;
-}
-
-__global__ __launch_bounds__(256) void k_db_final(const float* __restrict__ part, int64_t splits,
-                                                  int64_t cols, int64_t v0, int64_t slice_len,
-                                                  const Ctl* __restrict__ ctl,
-                                                  float* __restrict__ db) {
-  const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (col >= slice_len) return;
-  float s = 0.f;
-  for (int64_t sp = 0; sp < splits; ++sp) s += part[sp * cols + col];
-  db[v0 + col] = ctl->scale * s;
+  for (int64_t i = lane; i < n; i += 64) s += ld_elem(row, i);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) db[v0 + v] = ctl->scale * s;
 }
 
 __global__ __launch_bounds__(256) void k_fill(float* __restrict__ p, int64_t count, float value) {
