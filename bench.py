@@ -89,7 +89,19 @@ def main():
     ap.add_argument("--vocab-slice", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle baseline runs on (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        a = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel() * 4}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (each box here "
               f"has one GPU; the multi-GPU sharding is described in DESIGN.md).", file=sys.stderr)
