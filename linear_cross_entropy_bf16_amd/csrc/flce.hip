@@ -23,6 +23,10 @@ constexpr int64_t kAlign = 256;
 constexpr int64_t kMaxSlice = 8192;          // default backward vocabulary slice width ...
 constexpr int64_t kSliceBytes = 512ll << 20; // ... shrunk until one G slice fits in 512 MiB
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+// Output tiles per raster group along the token dimension: consecutive
+// workgroups on one XCD share W tiles in that XCD's L2 (4 measured ~2% faster
+// than 2 or 8 at 65536 x 4096 x 128256, and far faster than 16 or 32).
+constexpr int kRasterGroup = 4;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -44,11 +48,13 @@ Layout make_layout(const flce_params& p) {
   L.elem = p.dtype == FLCE_DTYPE_BF16 ? 2 : 4;
   L.v_tiles = cdiv(p.v, tile::kM);
   L.n_tiles = cdiv(p.n, tile::kN);
-  // Enough workgroups to fill 256 CUs several times over, and at most 8
-  // vocabulary tiles per workgroup so the partials stay small.
+  // Enough workgroups to fill 256 CUs several times over, and at most 4
+  // vocabulary tiles per workgroup so the partials stay small (measured at
+  // 65536 x 4096 x 128256: 1, 2, 4 and 8 tiles per workgroup lie within 4%,
+  // 4 is the fastest).
   const int64_t tiles = L.v_tiles * L.n_tiles;
-  int64_t tpc = tiles / 2048;
-  tpc = tpc < 1 ? 1 : (tpc > 8 ? 8 : tpc);
+  int64_t tpc = tiles / 4096;
+  tpc = tpc < 1 ? 1 : (tpc > 4 ? 4 : tpc);
   L.tiles_per_chunk = tpc;
   L.n_chunks = cdiv(L.v_tiles, tpc);
   int64_t slice = p.vocab_slice;
@@ -185,6 +191,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.n_chunks = L.n_chunks;
   a.tiles_per_chunk = L.tiles_per_chunk;
   a.grid = grid8(L.n_tiles * L.n_chunks);
+  a.group = kRasterGroup;
   a.part_m = reinterpret_cast<float*>(at(ws, L.part_m));
   a.part_d = reinterpret_cast<float*>(at(ws, L.part_d));
   a.part_s = reinterpret_cast<float*>(at(ws, L.part_s));
@@ -296,6 +303,7 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
       ga.n_tiles = L.n_tiles;
       ga.s_tiles = s_tiles;
       ga.grid = grid8(L.n_tiles * s_tiles);
+      ga.group = kRasterGroup;
       const int key = (has_bias ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
       switch (key) {
         case 0: launch_g<T, false, false>(ga, s); break;

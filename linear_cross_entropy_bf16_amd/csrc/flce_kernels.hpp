@@ -113,12 +113,66 @@ struct FwdArgs {
   const int32_t* targets;
   int64_t n, d, v;
   float softcap, inv_softcap;
-  int64_t n_tiles, v_tiles, n_chunks, tiles_per_chunk, grid;
+  int64_t n_tiles, v_tiles, n_chunks, tiles_per_chunk, grid, group;
   float* part_m;          // [n_chunks, n] running max, log2 units
   float* part_d;          // [n_chunks, n] sum of 2^(z log2e - m)
   float* part_s;          // [n_chunks, n] sum of z
   float* zt;              // [n] target logit
 };
+
+// max without NaN canonicalisation (logits here are finite)
+__device__ __forceinline__ float fmax_fast(float a, float b) { return a > b ? a : b; }
+
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked>
+__device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32x16 (&acc)[4][4],
+                                                  int64_t v0, int vw, int vlim,
+                                                  const int32_t (&tgt)[4], int64_t n0, int wn,
+                                                  int lane, float (&m_run)[4], float (&d_run)[4],
+                                                  float (&s_run)[4]) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t rel64 = static_cast<int64_t>(tgt[nb]) - v0 - vw;
+    const bool hit_col = rel64 >= 0 && rel64 < 128 && (rel64 & 4) == 0;
+    const int rel = hit_col ? static_cast<int>(rel64) : -1;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      float z[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
+        float zz = acc[mb][nb][r];
+        if (kBias) zz += (!kMasked || vl < vlim) ? ld_elem(a.bias, v0 + vl) : 0.f;
+        if (kSoftcap) zz = a.softcap * fast_tanh(zz * a.inv_softcap);
+        // masked rows (beyond V) drop out of the max and the sums
+        z[r] = (!kMasked || vl < vlim) ? zz : -INFINITY;
+      }
+      // Target logit: at most one lane-value per row in the whole vocabulary.
+      if ((rel >> 5) == mb) {
+        const int idx = ((rel >> 3) & 3) * 4 + (rel & 3);
+        float zt = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zt = r == idx ? z[r] : zt;
+        a.zt[n0 + wn * 128 + nb * 32 + (lane & 31)] = zt;
+      }
+      float mt = z[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmax_fast(mt, z[r]);
+      if (kSumZ) {
+        float sz = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sz += (!kMasked || z[r] != -INFINITY) ? z[r] : 0.f;
+        s_run[nb] += sz;
+      }
+      if (kMasked && mt == -INFINITY) continue;
+      const float m_new = fmax_fast(m_run[nb], mt * kLog2e);
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(z[r], kLog2e, -m_new));
+      d_run[nb] = d_run[nb] * fast_exp2(m_run[nb] - m_new) + sum;
+      m_run[nb] = m_new;
+    }
+  }
+}
 
 // One workgroup: a 256-token tile against `tiles_per_chunk` consecutive
 // 256-wide vocabulary tiles; the logits tile is reduced in registers and
@@ -133,7 +187,7 @@ void k_fwd(FwdArgs<T> a) {
   const int64_t L = xcd_logical(blockIdx.x, a.grid);
   if (L >= a.n_tiles * a.n_chunks) return;   // whole workgroup leaves together
   int64_t nt, ch;
-  grouped(L, a.n_tiles, a.n_chunks, kGroup, nt, ch);
+  grouped(L, a.n_tiles, a.n_chunks, a.group, nt, ch);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -162,55 +216,16 @@ void k_fwd(FwdArgs<T> a) {
     const int vlim = a.v - v0 < tile::kM ? static_cast<int>(a.v - v0) : tile::kM;
     const bool full = vlim == tile::kM;
 
-    // One token column at a time: 64 logits of this lane, bias and softcap
-    // applied in registers, never written back to the accumulators.
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      float z[64];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
-          float zz = acc[mb][nb][r];
-          if (kBias) zz += vl < vlim ? ld_elem(a.bias, v0 + vl) : 0.f;
-          if (kSoftcap) zz = a.softcap * fast_tanh(zz * a.inv_softcap);
-          z[mb * 16 + r] = zz;
-        }
-      // Target logit: at most one lane-value per row in the whole vocabulary.
-      const int64_t rel64 = static_cast<int64_t>(tgt[nb]) - v0 - vw;
-      if (rel64 >= 0 && rel64 < 128 && (rel64 & 4) == 0) {
-        const int rel = static_cast<int>(rel64);
-        const int idx = (rel >> 5) * 16 + ((rel >> 3) & 3) * 4 + (rel & 3);
-        float zt = 0.f;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) zt = i == idx ? z[i] : zt;
-        a.zt[n0 + wn * 128 + nb * 32 + (lane & 31)] = zt;
-      }
-      float mt = -INFINITY, sz = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = full || (vw + mb * 32 + 8 * (r >> 2) + (r & 3) < vlim);
-          mt = ok ? fmaxf(mt, z[mb * 16 + r]) : mt;
-          if (kSumZ) sz += ok ? z[mb * 16 + r] : 0.f;
-        }
-      if (kSumZ) s_run[nb] += sz;
-      if (mt == -INFINITY) continue;
-      const float m_new = fmaxf(m_run[nb], mt * kLog2e);
-      float sum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = full || (vw + mb * 32 + 8 * (r >> 2) + (r & 3) < vlim);
-          const float e = fast_exp2(__builtin_fmaf(z[mb * 16 + r], kLog2e, -m_new));
-          sum += ok ? e : 0.f;
-        }
-      d_run[nb] = d_run[nb] * fast_exp2(m_run[nb] - m_new) + sum;
-      m_run[nb] = m_new;
-    }
+    // One token column and one 32-row block at a time: 16 logits of this lane,
+    // bias and softcap applied in registers, merged into the running
+    // (max, sum-exp) of the column; the accumulators are never written back.
+    // Only the last vocabulary tile can be partial; it takes the masked path.
+    if (full)
+      fwd_tile_epilogue<T, kBias, kSoftcap, kSumZ, false>(a, acc, v0, vw, vlim, tgt, n0, wn, lane,
+                                                           m_run, d_run, s_run);
+    else
+      fwd_tile_epilogue<T, kBias, kSoftcap, kSumZ, true>(a, acc, v0, vw, vlim, tgt, n0, wn, lane,
+                                                          m_run, d_run, s_run);
   }
 
   // Combine the two lane halves (same token, disjoint vocabulary rows) ...
@@ -360,7 +375,7 @@ struct GArgs {
   int64_t v0, slice_len, ldg, ldt;
   T* g;                 // [n, ldg]       G slice, columns >= slice_len written as 0
   T* gt;                // [gcols, ldt]   the same slice transposed, tokens >= n as 0
-  int64_t n_tiles, s_tiles, grid;
+  int64_t n_tiles, s_tiles, grid, group;
 };
 
 __device__ __forceinline__ void store1(uint16_t* p, float a) {
@@ -379,7 +394,7 @@ void k_bwd_g(GArgs<T> a) {
   const int64_t L = xcd_logical(blockIdx.x, a.grid);
   if (L >= a.n_tiles * a.s_tiles) return;
   int64_t nt, st;
-  grouped(L, a.n_tiles, a.s_tiles, kGroup, nt, st);
+  grouped(L, a.n_tiles, a.s_tiles, a.group, nt, st);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t n0 = nt * tile::kN, vl0 = st * tile::kM;
@@ -405,7 +420,8 @@ void k_bwd_g(GArgs<T> a) {
                         ? static_cast<int>((rel64 >> 5) * 16 + ((rel64 >> 3) & 3) * 4 + (rel64 & 3))
                         : -1;
     T* row = a.g + tok * a.ldg + vl0;
-    T* col = a.gt + vl0 * a.ldt + tok;      // element (v, tok) at col[v * ldt]
+    T* col = a.gt + (vl0 + vw) * a.ldt + tok;   // element (vw + i, tok) at col[i * ldt]
+    const int ldt = static_cast<int>(a.ldt);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -429,7 +445,7 @@ void k_bwd_g(GArgs<T> a) {
           float g = __builtin_fmaf(p, zfac, -sub);
           if (kSoftcap) g *= dz;
           gv[j] = (valid && vin) ? g : 0.f;
-          store1(col + static_cast<int64_t>(vl) * a.ldt, gv[j]);   // tok < ldt always
+          store1(col + (mb * 32 + 8 * q + j) * ldt, gv[j]);   // tok < ldt always
         }
         if (tin) store4(row + vw + mb * 32 + 8 * q, gv[0], gv[1], gv[2], gv[3]);
       }
