@@ -10,8 +10,9 @@
 // Work split: 256 threads = 4 wave64s in a 2 x 2 grid, each wave owning a
 // 128 x 128 quarter as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (bf16) or
 // v_mfma_f32_32x32x2_f32 (fp32).  K advances in slabs of 128 bytes per row
-// (64 bf16 / 32 fp32), double-buffered in LDS (2 x 64 KiB) with the next
-// slab's global loads in flight while the current slab is multiplied.
+// (64 bf16 / 32 fp32) staged in LDS while later slabs' global loads are in
+// flight: bf16 through a ring of five 32 KiB operand slots (all 160 KiB of a
+// gfx950 CU), fp32 through a 2 x 64 KiB double buffer.
 //
 // Accumulator layout (per lane l, block (mb, nb), register r in 0..15):
 //   row m = wm*128 + mb*32 + 8*(r/4) + 4*(l/32) + (r%4)
@@ -34,7 +35,7 @@ constexpr int kN = 256;                     // output tile columns
 constexpr int kRowBytes = 128;              // one operand row of one K-slab
 constexpr int kOpBytes = kM * kRowBytes;    // one operand, one slab: 32 KiB
 constexpr int kStageBytes = 2 * kOpBytes;   // A + B
-constexpr int kLdsBytes = 2 * kStageBytes;  // double buffer: 128 KiB
+constexpr int kLdsBytes = 5 * kOpBytes;     // bf16 ring (fp32 uses 2 stages of it): 160 KiB
 }  // namespace tile
 
 // Elements per 16-byte chunk.  bf16 is carried as raw uint16_t bits.
@@ -171,16 +172,32 @@ __device__ __forceinline__ void gemm_tile_regs(const Operand<T>& A, const Operan
 // columns are loads with an out-of-range buffer offset, which the hardware
 // turns into zeros, so the loop has no branches.
 //
-// Per slab: fragments of the next 16-wide K step are read while the MFMAs of
-// the current one run; after the third step the waves meet at one barrier
-// (the next slab has landed, the current buffer is no longer read) and the
-// loads of the slab after next go out, a full slab ahead of their use.
+// Operand slabs stream through a ring of five LDS slots in the order A0 B0
+// A1 B1 A2 ...; slab j of that stream sits in slot j mod 5.  Per slab:
+// fragments of the next 16-wide K step are read while the MFMAs of the current
+// one run; after the third step the waves meet at one barrier (slab s+1 has
+// landed, slab s is no longer read).  B(s+2) then goes out into A(s)'s slot
+// with the fourth step, and A(s+3) into B(s)'s slot with the first step of
+// slab s+1: B lands a slab ahead of its use, A two slabs ahead.
+//
+// Measured on a 8192 x 8192 x 4096 product (one CU per tile, Gaussian data):
+// with a double buffer all 16 loads of a wave went out in one 512-cycle step
+// while the address unit needs ~1450 cycles for a slab's 64 KiB, the waves
+// stalled on load issue and the matrix cores were busy 67% of the cycles; the
+// ring spreads the loads over two steps and leaves slack for the A half, 79%.
 namespace dma {
 constexpr int kBK = 64;                    // bf16 elements of K per slab
 constexpr int kOpBytes = 32768;            // one operand, one slab
-constexpr int kStageBytes = 2 * kOpBytes;
-constexpr int kLdsBytes = 2 * kStageBytes; // 128 KiB
+constexpr int kSlots = 5;
+constexpr int kLdsBytes = kSlots * kOpBytes; // 160 KiB
+static_assert(kLdsBytes == tile::kLdsBytes, "LDS sizes disagree");
 constexpr uint32_t kOob = 0x80000000u;     // buffer offset beyond num_records: reads 0
+
+// s_waitcnt immediate (gfx9 layout): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; lgkm = 15 leaves LDS/scalar loads unchecked.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -222,8 +239,8 @@ __device__ __forceinline__ void frags(u32x4 (&f)[4], const char* src, int base, 
 }
 
 // Scheduling groups (masks: 0x008 MFMA, 0x100 DS read, 0x020 VMEM read): a
-// fragment read and, in the last step of a slab, a slab load after each of the
-// step's 16 MFMAs.
+// fragment read and, in the steps that carry them, a slab load after each of
+// the step's 16 MFMAs.
 template <bool kLoads, int I = 0>
 __device__ __forceinline__ void interleave() {
   if constexpr (I < 16) {
@@ -253,15 +270,17 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
 
   const int64_t nslab = (K + kBK - 1) / kBK;
-  auto issue = [&](int64_t s) {
-    char* st = lds + (int)(s & 1) * kStageBytes;
-    issue_slab(A, m0, s * kBK, st, wave, lane);
-    issue_slab(B, n0, s * kBK, st + kOpBytes, wave, lane);
+  // p = slot of A(s); the stream positions after it follow as p + 1, p + 2, ...
+  int p = 0;
+  auto slot = [&](int c) -> char* {
+    int q = p + c;
+    q = q >= kSlots ? q - kSlots : q;
+    return lds + q * kOpBytes;
   };
-  auto load_frags = [&](u32x4 (&fa)[4], u32x4 (&fb)[4], int64_t s, int ks) {
-    const char* st = lds + (int)(s & 1) * kStageBytes;
-    frags(fa, st, wm * 128, ks, lane);
-    frags(fb, st + kOpBytes, wn * 128, ks, lane);
+  // c = 0: fragments of slab s, c = 2: of slab s+1
+  auto load_frags = [&](u32x4 (&fa)[4], u32x4 (&fb)[4], int c, int ks) {
+    frags(fa, slot(c), wm * 128, ks, lane);
+    frags(fb, slot(c + 1), wn * 128, ks, lane);
   };
   auto mfmas = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
 #pragma unroll
@@ -270,34 +289,35 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
       for (int nb = 0; nb < 4; ++nb) mma(acc[mb][nb], fa[mb], fb[nb], uint16_t{});
   };
 
-  issue(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt 0: slab 0 landed
+  // Slabs past the end of K are all out of range and land as zeros.
+  issue_slab(A, m0, 0, slot(0), wave, lane);
+  issue_slab(B, n0, 0, slot(1), wave, lane);
+  issue_slab(A, m0, kBK, slot(2), wave, lane);
+  issue_slab(B, n0, kBK, slot(3), wave, lane);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 15));   // A0, B0 landed
   __builtin_amdgcn_s_barrier();
-  issue(1);                                // slab 1 (all lanes out of range if K <= 64)
   u32x4 a0[4], b0[4], a1[4], b1[4];
   load_frags(a0, b0, 0, 0);
-  // Within each 16-wide K step the fragment reads of the next step (and, in
-  // the last step, the loads of the slab after next) are interleaved one per
-  // MFMA, so the matrix core never waits behind a burst of memory
-  // instructions issued by its only wave.
   for (int64_t s = 0; s < nslab; ++s) {
-    load_frags(a1, b1, s, 1);
+    issue_slab(A, m0, (s + 2) * kBK, slot(4), wave, lane);   // B(s-1)'s slot
+    load_frags(a1, b1, 0, 1);
     mfmas(a0, b0);
-    interleave<false>();
-    load_frags(a0, b0, s, 2);
+    interleave<true>();
+    load_frags(a0, b0, 0, 2);
     mfmas(a1, b1);
     interleave<false>();
-    load_frags(a1, b1, s, 3);
+    load_frags(a1, b1, 0, 3);
     mfmas(a0, b0);
     interleave<false>();
-    // own loads of slab s+1 landed, own reads of this buffer done; after the
-    // barrier the same holds for every wave
-    __builtin_amdgcn_s_waitcnt(0x0070);
+    // every load but A(s+2) done, so A(s+1) and B(s+1) landed (own loads);
+    // own reads of slab s done; after the barrier both hold for every wave
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
     __builtin_amdgcn_s_barrier();
-    issue(s + 2);                           // into the buffer just finished
-    load_frags(a0, b0, s + 1, 0);
+    issue_slab(B, n0, (s + 2) * kBK, slot(5), wave, lane);   // A(s)'s slot
+    load_frags(a0, b0, 2, 0);
     mfmas(a1, b1);
     interleave<true>();
+    p = p >= 3 ? p - 3 : p + 2;
   }
   __builtin_amdgcn_s_waitcnt(0);            // drain the loads still in flight
   __builtin_amdgcn_s_barrier();

@@ -183,7 +183,8 @@ template <typename T, bool kBias, bool kSoftcap, bool kSumZ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fwd(FwdArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
-  __shared__ float xch[3][2][4][32];
+  // wave-row exchange of the final partials; gemm_tile has released `lds` by then
+  float (*xch)[2][4][32] = reinterpret_cast<float (*)[2][4][32]>(lds);
   const int64_t L = xcd_logical(blockIdx.x, a.grid);
   if (L >= a.n_tiles * a.n_chunks) return;   // whole workgroup leaves together
   int64_t nt, ch;
