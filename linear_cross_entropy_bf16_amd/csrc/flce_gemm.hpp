@@ -214,17 +214,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)kOob, 0x00020000);
 }
 
-// One operand's slab = 32 wave-wide 1 KiB blocks, 8 per wave.
+// One operand's slab = 32 wave-wide 1 KiB blocks, 8 per wave.  Bounds are
+// checked in 32 bits against the rows and K columns left in this tile, and
+// the byte offset of a row stays below 2^31 (row < 256, ld * 2 < 2^23 for
+// every operand the library builds or accepts), so in-range lanes never reach
+// the out-of-range marker.
 __device__ __forceinline__ void issue_slab(const Operand<uint16_t>& op, int64_t mn0,
                                            int64_t k0, char* dst, int wave, int lane) {
   const __amdgpu_buffer_rsrc_t r = rsrc(op.base + mn0 * op.ld + k0);
+  const int64_t rows = op.mn - mn0, cols = op.k - k0;
+  const int rows_left = rows < 256 ? static_cast<int>(rows) : 256;
+  const int cols_left = cols < kBK ? static_cast<int>(cols) : kBK;   // may be <= 0
+  const uint32_t ld2 = static_cast<uint32_t>(op.ld) * 2u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int blk = wave * 8 + i;
     const int row = blk * 8 + (lane >> 3);
     const int c = (lane & 7) ^ kmaj_swz(row);            // logical chunk of this lane's slot
-    const bool ok = (k0 + c * 8 < op.k) && (mn0 + row < op.mn);
-    const uint32_t off = ok ? (uint32_t)((row * op.ld + c * 8) * 2) : kOob;
+    const bool ok = (c * 8 < cols_left) && (row < rows_left);
+    const uint32_t off = ok ? static_cast<uint32_t>(row) * ld2 + static_cast<uint32_t>(c * 16) : kOob;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, off, 0, 0, 0);
   }
 }
