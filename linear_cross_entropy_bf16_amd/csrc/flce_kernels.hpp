@@ -384,6 +384,81 @@ __device__ __forceinline__ void store1(uint16_t* p, float a) {
 }
 __device__ __forceinline__ void store1(float* p, float a) { *p = a; }
 
+// bf16 G tile -> G [n, ldg] and G^T [gcols, ldt] through LDS (free again once
+// gemm_tile returns): the tile is staged once per orientation with rows padded
+// to 528 bytes, then every row leaves as 32 coalesced 16-byte stores.
+constexpr int kStagePitch = 264;   // bf16 elements per staged row (256 + 8)
+static_assert(256 * kStagePitch * 2 <= tile::kLdsBytes, "staged G tile exceeds LDS");
+
+template <typename T>
+__device__ __forceinline__ void store_g_staged(const GArgs<T>& a, const f32x16 (&acc)[4][4],
+                                               char* lds, int64_t n0, int64_t vl0, int vw, int wn,
+                                               int lane, int tid) {
+  uint16_t* sm = reinterpret_cast<uint16_t*>(lds);
+  const int tcol = wn * 128 + (lane & 31);        // tile-local token of (nb = 0)
+  // G^T: staged row = vocabulary, 256 tokens per row
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
+        sm[vl * kStagePitch + tcol + nb * 32] =
+            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[mb][nb][r]));
+      }
+  __syncthreads();
+  const int chunk = tid & 31, row0 = tid >> 5;
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    const int row = row0 + 8 * i;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(sm + row * kStagePitch + chunk * 8);
+    *reinterpret_cast<u32x4*>(a.gt + (vl0 + row) * a.ldt + n0 + chunk * 8) = v;
+  }
+  __syncthreads();
+  // G: staged row = token, 256 vocabulary entries per row (4 consecutive per lane)
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        store4(sm + (tcol + nb * 32) * kStagePitch + vw + mb * 32 + 8 * q, acc[mb][nb][4 * q],
+               acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+  __syncthreads();
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    const int row = row0 + 8 * i;
+    if (n0 + row < a.n) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sm + row * kStagePitch + chunk * 8);
+      *reinterpret_cast<u32x4*>(a.g + (n0 + row) * a.ldg + vl0 + chunk * 8) = v;
+    }
+  }
+}
+
+// fp32 G tile (too large to stage): stored from the accumulator layout.
+template <typename T>
+__device__ __forceinline__ void store_g_direct(const GArgs<T>& a, const f32x16 (&acc)[4][4],
+                                               int64_t n0, int64_t vl0, int vw, int wn, int lane) {
+  const int ldt = static_cast<int>(a.ldt);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
+    T* row = a.g + tok * a.ldg + vl0;
+    T* col = a.gt + (vl0 + vw) * a.ldt + tok;   // element (vw + i, tok) at col[i * ldt]
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store1(col + (mb * 32 + 8 * q + j) * ldt, acc[mb][nb][4 * q + j]);
+        if (tok < a.n)
+          store4(row + vw + mb * 32 + 8 * q, acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
+                 acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+      }
+  }
+}
+
 // Recompute one 256 x 256 logits tile of the slice and turn it into
 // G = [p (1 + 2 s lse) - (1-eps) onehot - eps/V] (1 - (z/c)^2), p = exp(z - lse)
 // (page "Cutting LLM Memory by 84%", "Kernel Implementation", backward:
@@ -407,50 +482,53 @@ void k_bwd_g(GArgs<T> a) {
 
   const int vw = wm * 128 + 4 * (lane >> 5);              // tile-local v of (mb = 0, r = 0)
   const int vlim = a.slice_len - vl0 < tile::kM ? static_cast<int>(a.slice_len - vl0) : tile::kM;
+  // G replaces the logits in the accumulators; rows past the slice and
+  // ignored or missing tokens hold 0.  Per-token terms first, then one
+  // vocabulary row (and its bias) at a time across the four token blocks.
+  float lse2[4], zfac[4];
+  int hit[4];
+  bool valid[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
     const bool tin = tok < a.n;
     const int32_t t = tin ? a.targets[tok] : a.ignore_index;
-    const bool valid = tin && t != a.ignore_index;
-    const float l = valid ? a.lse[tok] : 0.f;
-    const float lse2 = l * kLog2e;
-    const float zfac = 1.0f + a.two_s * l;
+    valid[nb] = tin && t != a.ignore_index;
+    const float l = valid[nb] ? a.lse[tok] : 0.f;
+    lse2[nb] = l * kLog2e;
+    zfac[nb] = 1.0f + a.two_s * l;
     const int64_t rel64 = static_cast<int64_t>(t) - a.v0 - vl0 - vw;
-    const int hit = (valid && rel64 >= 0 && rel64 < 128 && (rel64 & 4) == 0)
-                        ? static_cast<int>((rel64 >> 5) * 16 + ((rel64 >> 3) & 3) * 4 + (rel64 & 3))
-                        : -1;
-    T* row = a.g + tok * a.ldg + vl0;
-    T* col = a.gt + (vl0 + vw) * a.ldt + tok;   // element (vw + i, tok) at col[i * ldt]
-    const int ldt = static_cast<int>(a.ldt);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float gv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * q + j;
-          const int vl = vw + mb * 32 + 8 * q + j;
-          const bool vin = vl < vlim;
-          float z = acc[mb][nb][r];
-          if (kBias) z += vin ? ld_elem(a.bias, a.v0 + vl0 + vl) : 0.f;
-          float dz = 1.0f;
-          if (kSoftcap) {
-            const float th = fast_tanh(z * a.inv_softcap);
-            z = a.softcap * th;
-            dz = 1.0f - th * th;
-          }
-          const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2));
-          const float sub = (mb * 16 + r == hit) ? a.eps_over_v + a.keep_target : a.eps_over_v;
-          float g = __builtin_fmaf(p, zfac, -sub);
-          if (kSoftcap) g *= dz;
-          gv[j] = (valid && vin) ? g : 0.f;
-          store1(col + (mb * 32 + 8 * q + j) * ldt, gv[j]);   // tok < ldt always
-        }
-        if (tin) store4(row + vw + mb * 32 + 8 * q, gv[0], gv[1], gv[2], gv[3]);
-      }
+    hit[nb] = (valid[nb] && rel64 >= 0 && rel64 < 128 && (rel64 & 4) == 0)
+                  ? static_cast<int>((rel64 >> 5) * 16 + ((rel64 >> 3) & 3) * 4 + (rel64 & 3))
+                  : -1;
   }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
+      const bool vin = vl < vlim;
+      const float bv = (kBias && vin) ? ld_elem(a.bias, a.v0 + vl0 + vl) : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        float z = acc[mb][nb][r] + bv;
+        float dz = 1.0f;
+        if (kSoftcap) {
+          const float th = fast_tanh(z * a.inv_softcap);
+          z = a.softcap * th;
+          dz = 1.0f - th * th;
+        }
+        const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2[nb]));
+        const float sub = (mb * 16 + r == hit[nb]) ? a.eps_over_v + a.keep_target : a.eps_over_v;
+        float g = __builtin_fmaf(p, zfac[nb], -sub);
+        if (kSoftcap) g *= dz;
+        acc[mb][nb][r] = (valid[nb] && vin) ? g : 0.f;
+      }
+    }
+  if constexpr (sizeof(T) == 2)
+    store_g_staged(a, acc, lds, n0, vl0, vw, wn, lane, tid);
+  else
+    store_g_direct(a, acc, n0, vl0, vw, wn, lane);
 }
 
 template <typename T>
