@@ -592,9 +592,11 @@ struct DxArgs {
   int64_t d_tiles, n_tiles, grid;
 };
 
-// dX (+)= scale G_slice W_slice, computed as C[d, n] so each lane owns four
-// consecutive d of one token row: the running fp32 sum is read-modified-
-// written with 16-byte accesses; the last slice writes dX in its own dtype.
+// dX (+)= scale G_slice W_slice, computed as C[d, n]; the running fp32 sum
+// over slices is read-modified-written row by row, and the last slice writes
+// dX in its own dtype.
+constexpr int kDxPitch = 260;   // fp32 per staged token row (256 + 4)
+static_assert(128 * kDxPitch * 4 <= tile::kLdsBytes, "staged dX half tile exceeds LDS");
 template <typename T>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_dx(DxArgs<T> a) {
@@ -611,29 +613,55 @@ void k_dx(DxArgs<T> a) {
   f32x16 acc[4][4];
   gemm_tile(A, B, dt * tile::kM, nt * tile::kN, a.kdim, lds, acc);
 
+  // The tile goes through LDS (free again once gemm_tile returns) in two
+  // halves of 128 tokens, so the running sum is read-modified-written as whole
+  // 1 KiB rows of 256 fp32 instead of 32-byte pieces of 32 rows.
   const float scale = a.ctl->scale;
+  float* sm = reinterpret_cast<float*>(lds);
+  const int64_t tok0 = nt * tile::kN, d0 = dt * tile::kM;
+  const int chunk = tid & 63, row0 = tid >> 6;
+  const bool cols_ok = d0 + 4 * chunk < a.d;          // d is a multiple of 8
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int64_t tok = nt * tile::kN + wn * 128 + nb * 32 + (lane & 31);
-    if (tok >= a.n) continue;
+  for (int h = 0; h < 2; ++h) {
+    // this half's previous sums are requested first and land while the
+    // tile is being staged
+    float4 prev[32];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int i = 0; i < 32; ++i) {
+      const int64_t tok = tok0 + h * 128 + row0 + 4 * i;
+      prev[i] = float4{0.f, 0.f, 0.f, 0.f};
+      if (!a.first && tok < a.n && cols_ok)
+        prev[i] = *reinterpret_cast<const float4*>(a.acc_buf + tok * a.d + d0 + 4 * chunk);
+    }
+    if (wn == h) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t dd = dt * tile::kM + wm * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
-        if (dd >= a.d) continue;
-        float4 val{scale * acc[mb][nb][4 * q], scale * acc[mb][nb][4 * q + 1],
-                   scale * acc[mb][nb][4 * q + 2], scale * acc[mb][nb][4 * q + 3]};
-        float* ap = a.acc_buf + tok * a.d + dd;
-        if (!a.first) {
-          const float4 prev = *reinterpret_cast<const float4*>(ap);
-          val.x += prev.x; val.y += prev.y; val.z += prev.z; val.w += prev.w;
-        }
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int dl = wm * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
+            *reinterpret_cast<float4*>(sm + (nb * 32 + (lane & 31)) * kDxPitch + dl) =
+                float4{scale * acc[mb][nb][4 * q], scale * acc[mb][nb][4 * q + 1],
+                       scale * acc[mb][nb][4 * q + 2], scale * acc[mb][nb][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int row = row0 + 4 * i;
+      const int64_t tok = tok0 + h * 128 + row;
+      if (tok < a.n && cols_ok) {
+        float4 v = *reinterpret_cast<const float4*>(sm + row * kDxPitch + 4 * chunk);
+        v.x += prev[i].x; v.y += prev[i].y; v.z += prev[i].z; v.w += prev[i].w;
+        const int64_t off = tok * a.d + d0 + 4 * chunk;
         if (a.last)
-          store4(a.dx + tok * a.d + dd, val.x, val.y, val.z, val.w);
+          store4(a.dx + off, v.x, v.y, v.z, v.w);
         else
-          *reinterpret_cast<float4*>(ap) = val;
+          *reinterpret_cast<float4*>(a.acc_buf + off) = v;
       }
+    }
+    __syncthreads();
   }
 }
 
