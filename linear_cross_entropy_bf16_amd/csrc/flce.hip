@@ -43,6 +43,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Layout {
   int64_t elem;           // bytes per X/W element
   int64_t v_tiles, n_tiles, tiles_per_chunk, n_chunks;
+  int64_t v_full, main_chunks;   // whole vocabulary tiles; chunks of the unmasked launch
   int64_t slice, ldg;     // backward slice width (multiple of 256) and G row pitch
   int64_t ldt;            // token pitch of X^T and G^T (N rounded up to 256, plus kPitchPad)
   int64_t n_merge_blocks;
@@ -64,7 +65,11 @@ Layout make_layout(const flce_params& p) {
   int64_t tpc = tiles / 4096;
   tpc = tpc < 1 ? 1 : (tpc > 4 ? 4 : tpc);
   L.tiles_per_chunk = tpc;
-  L.n_chunks = cdiv(L.v_tiles, tpc);
+  // Whole vocabulary tiles go to one launch; a partial last tile (V mod 256
+  // rows) gets its own chunk and launch.
+  L.v_full = p.v / tile::kM;
+  L.main_chunks = cdiv(L.v_full, tpc);
+  L.n_chunks = L.main_chunks + (L.v_full < L.v_tiles ? 1 : 0);
   int64_t slice = p.vocab_slice;
   if (slice <= 0) {
     slice = kMaxSlice;
@@ -167,9 +172,29 @@ int64_t grid8(int64_t tiles) { return round_up(tiles, 8); }
 
 // ----------------------------------------------------------------- forward
 template <typename T, bool kBias, bool kSoftcap, bool kSumZ>
-void launch_fwd(const flce::FwdArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ>), dim3(static_cast<unsigned>(a.grid)),
-                     dim3(tile::kThreads), 0, s, a);
+void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
+  if (L.main_chunks > 0) {
+    flce::FwdArgs<T> m = a;
+    m.vt_base = 0;
+    m.vt_end = L.v_full;
+    m.chunk_base = 0;
+    m.n_chunks = L.main_chunks;
+    m.tiles_per_chunk = L.tiles_per_chunk;
+    m.grid = grid8(L.n_tiles * m.n_chunks);
+    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, false>),
+                       dim3(static_cast<unsigned>(m.grid)), dim3(tile::kThreads), 0, s, m);
+  }
+  if (L.v_full < L.v_tiles) {
+    flce::FwdArgs<T> t = a;
+    t.vt_base = L.v_full;
+    t.vt_end = L.v_tiles;
+    t.chunk_base = L.main_chunks;
+    t.n_chunks = 1;
+    t.tiles_per_chunk = 1;
+    t.grid = grid8(L.n_tiles);
+    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, true>),
+                       dim3(static_cast<unsigned>(t.grid)), dim3(tile::kThreads), 0, s, t);
+  }
 }
 
 template <typename T>
@@ -195,10 +220,6 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.softcap = p.softcap;
   a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
   a.n_tiles = L.n_tiles;
-  a.v_tiles = L.v_tiles;
-  a.n_chunks = L.n_chunks;
-  a.tiles_per_chunk = L.tiles_per_chunk;
-  a.grid = grid8(L.n_tiles * L.n_chunks);
   a.group = kRasterGroup;
   a.part_m = reinterpret_cast<float*>(at(ws, L.part_m));
   a.part_d = reinterpret_cast<float*>(at(ws, L.part_d));
@@ -207,14 +228,14 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   const bool b = bias != nullptr, c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
   const int key = (b ? 1 : 0) | (c ? 2 : 0) | (z ? 4 : 0);
   switch (key) {
-    case 0: launch_fwd<T, false, false, false>(a, s); break;
-    case 1: launch_fwd<T, true, false, false>(a, s); break;
-    case 2: launch_fwd<T, false, true, false>(a, s); break;
-    case 3: launch_fwd<T, true, true, false>(a, s); break;
-    case 4: launch_fwd<T, false, false, true>(a, s); break;
-    case 5: launch_fwd<T, true, false, true>(a, s); break;
-    case 6: launch_fwd<T, false, true, true>(a, s); break;
-    default: launch_fwd<T, true, true, true>(a, s); break;
+    case 0: launch_fwd<T, false, false, false>(a, L, s); break;
+    case 1: launch_fwd<T, true, false, false>(a, L, s); break;
+    case 2: launch_fwd<T, false, true, false>(a, L, s); break;
+    case 3: launch_fwd<T, true, true, false>(a, L, s); break;
+    case 4: launch_fwd<T, false, false, true>(a, L, s); break;
+    case 5: launch_fwd<T, true, false, true>(a, L, s); break;
+    case 6: launch_fwd<T, false, true, true>(a, L, s); break;
+    default: launch_fwd<T, true, true, true>(a, L, s); break;
   }
   flce::MergeArgs m{};
   m.part_m = a.part_m;

@@ -214,26 +214,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)kOob, 0x00020000);
 }
 
-// One operand's slab = 32 wave-wide 1 KiB blocks, 8 per wave.  Bounds are
-// checked in 32 bits against the rows and K columns left in this tile, and
-// the byte offset of a row stays below 2^31 (row < 256, ld * 2 < 2^23 for
-// every operand the library builds or accepts), so in-range lanes never reach
-// the out-of-range marker.
-__device__ __forceinline__ void issue_slab(const Operand<uint16_t>& op, int64_t mn0,
-                                           int64_t k0, char* dst, int wave, int lane) {
-  const __amdgpu_buffer_rsrc_t r = rsrc(op.base + mn0 * op.ld + k0);
-  const int64_t rows = op.mn - mn0, cols = op.k - k0;
+// One operand's slab = 32 wave-wide 1 KiB blocks, 8 per wave.  The byte
+// offsets of a wave's 8 blocks, with rows past the operand already replaced
+// by the out-of-range marker, are fixed for the whole tile; per slab only the
+// K tail is checked.  A row's byte offset stays below 2^31 (row < 256,
+// ld * 2 < 2^23 for every operand the library builds or accepts), so
+// in-range lanes never reach the marker.
+struct SlabStream {
+  const uint16_t* base;   // operand row mn0, column 0
+  int64_t kdim;
+  uint32_t off[8];
+  int c8[2];              // K offset (elements) of this lane's chunk, blocks of even / odd index
+};
+
+__device__ __forceinline__ SlabStream slab_stream(const Operand<uint16_t>& op, int64_t mn0,
+                                                  int wave, int lane) {
+  SlabStream st;
+  st.base = op.base + mn0 * op.ld;
+  st.kdim = op.k;
+  const int64_t rows = op.mn - mn0;
   const int rows_left = rows < 256 ? static_cast<int>(rows) : 256;
-  const int cols_left = cols < kBK ? static_cast<int>(cols) : kBK;   // may be <= 0
   const uint32_t ld2 = static_cast<uint32_t>(op.ld) * 2u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int blk = wave * 8 + i;
-    const int row = blk * 8 + (lane >> 3);
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ kmaj_swz(row);            // logical chunk of this lane's slot
-    const bool ok = (c * 8 < cols_left) && (row < rows_left);
-    const uint32_t off = ok ? static_cast<uint32_t>(row) * ld2 + static_cast<uint32_t>(c * 16) : kOob;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + blk * 1024), 16, off, 0, 0, 0);
+    st.off[i] = row < rows_left ? static_cast<uint32_t>(row) * ld2 + static_cast<uint32_t>(c * 16)
+                                : kOob;
+    if (i < 2) st.c8[i] = c * 8;                         // the swizzle depends on i only via i & 1
+  }
+  return st;
+}
+
+__device__ __forceinline__ void issue_slab(const SlabStream& st, int64_t k0, char* dst, int wave) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(st.base + k0);
+  const int64_t cols = st.kdim - k0;
+  const int cols_left = cols < kBK ? static_cast<int>(cols) : kBK;   // may be <= 0
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool ok = cols_left == kBK || st.c8[i & 1] < cols_left;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (wave * 8 + i) * 1024), 16,
+                                             ok ? st.off[i] : kOob, 0, 0, 0);
   }
 }
 
@@ -268,7 +289,7 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
   using namespace dma;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS addresses in SGPRs
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -298,16 +319,17 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
   };
 
   // Slabs past the end of K are all out of range and land as zeros.
-  issue_slab(A, m0, 0, slot(0), wave, lane);
-  issue_slab(B, n0, 0, slot(1), wave, lane);
-  issue_slab(A, m0, kBK, slot(2), wave, lane);
-  issue_slab(B, n0, kBK, slot(3), wave, lane);
+  const SlabStream sa = slab_stream(A, m0, wave, lane), sb = slab_stream(B, n0, wave, lane);
+  issue_slab(sa, 0, slot(0), wave);
+  issue_slab(sb, 0, slot(1), wave);
+  issue_slab(sa, kBK, slot(2), wave);
+  issue_slab(sb, kBK, slot(3), wave);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 15));   // A0, B0 landed
   __builtin_amdgcn_s_barrier();
   u32x4 a0[4], b0[4], a1[4], b1[4];
   load_frags(a0, b0, 0, 0);
   for (int64_t s = 0; s < nslab; ++s) {
-    issue_slab(A, m0, (s + 2) * kBK, slot(4), wave, lane);   // B(s-1)'s slot
+    issue_slab(sa, (s + 2) * kBK, slot(4), wave);   // B(s-1)'s slot
     load_frags(a1, b1, 0, 1);
     mfmas(a0, b0);
     interleave<true>();
@@ -321,7 +343,7 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
     // own reads of slab s done; after the barrier both hold for every wave
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
     __builtin_amdgcn_s_barrier();
-    issue_slab(B, n0, (s + 2) * kBK, slot(5), wave, lane);   // A(s)'s slot
+    issue_slab(sb, (s + 2) * kBK, slot(5), wave);   // A(s)'s slot
     load_frags(a0, b0, 2, 0);
     mfmas(a1, b1);
     interleave<true>();

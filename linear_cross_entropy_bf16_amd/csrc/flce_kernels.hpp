@@ -113,14 +113,16 @@ struct FwdArgs {
   const int32_t* targets;
   int64_t n, d, v;
   float softcap, inv_softcap;
-  int64_t n_tiles, v_tiles, n_chunks, tiles_per_chunk, grid, group;
+  int64_t n_tiles, n_chunks, tiles_per_chunk, grid, group;
+  int64_t vt_base, vt_end;   // vocabulary tiles [vt_base, vt_end) of this launch
+  int64_t chunk_base;        // partials row of this launch's first chunk
   float* part_m;          // [n_chunks, n] running max, log2 units
   float* part_d;          // [n_chunks, n] sum of 2^(z log2e - m)
   float* part_s;          // [n_chunks, n] sum of z
   float* zt;              // [n] target logit
 };
 
-// max without NaN canonicalisation (logits here are finite)
+// max without NaN canonicalisation (logits here are finite or -inf)
 __device__ __forceinline__ float fmax_fast(float a, float b) { return a > b ? a : b; }
 
 template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked>
@@ -179,7 +181,9 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
 // never leaves the chip (page "[CuteDSL] FLCE", Summary: the forward stores
 // only the per-row LSE and target logit).
 // kSumZ: label smoothing needs sum_v z of every row.
-template <typename T, bool kBias, bool kSoftcap, bool kSumZ>
+// kMasked: this launch covers the one partial vocabulary tile (V mod 256 rows);
+// the main launch covers whole tiles only and carries no masking code.
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fwd(FwdArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
@@ -206,26 +210,21 @@ void k_fwd(FwdArgs<T> a) {
 
   const Operand<T> A{a.w, a.d, a.v, a.d};   // rows: vocabulary
   const Operand<T> B{a.x, a.d, a.n, a.d};   // rows: tokens
-  const int64_t vt_end = (ch + 1) * a.tiles_per_chunk < a.v_tiles ? (ch + 1) * a.tiles_per_chunk
-                                                                   : a.v_tiles;
-  for (int64_t vt = ch * a.tiles_per_chunk; vt < vt_end; ++vt) {
+  const int64_t vt_first = a.vt_base + ch * a.tiles_per_chunk;
+  const int64_t vt_end = vt_first + a.tiles_per_chunk < a.vt_end ? vt_first + a.tiles_per_chunk
+                                                                 : a.vt_end;
+  for (int64_t vt = vt_first; vt < vt_end; ++vt) {
     const int64_t v0 = vt * tile::kM;
     f32x16 acc[4][4];
     gemm_tile(A, B, v0, n0, a.d, lds, acc);
     // tile-local vocabulary row of (mb, r) = vw + mb*32 + 8(r/4) + r%4
     const int vw = wm * 128 + 4 * (lane >> 5);
     const int vlim = a.v - v0 < tile::kM ? static_cast<int>(a.v - v0) : tile::kM;
-    const bool full = vlim == tile::kM;
 
     // One token column and one 32-row block at a time: 16 logits of this lane,
     // bias and softcap applied in registers, merged into the running
     // (max, sum-exp) of the column; the accumulators are never written back.
-    // Only the last vocabulary tile can be partial; it takes the masked path.
-    if (full)
-      fwd_tile_epilogue<T, kBias, kSoftcap, kSumZ, false>(a, acc, v0, vw, vlim, tgt, n0, wn, lane,
-                                                           m_run, d_run, s_run);
-    else
-      fwd_tile_epilogue<T, kBias, kSoftcap, kSumZ, true>(a, acc, v0, vw, vlim, tgt, n0, wn, lane,
+    fwd_tile_epilogue<T, kBias, kSoftcap, kSumZ, kMasked>(a, acc, v0, vw, vlim, tgt, n0, wn, lane,
                                                           m_run, d_run, s_run);
   }
 
@@ -255,9 +254,10 @@ void k_fwd(FwdArgs<T> a) {
       const float s = s_run[nb] + xch[2][wn][nb][lane];
       const int64_t tok = n0 + wn * 128 + nb * 32 + lane;
       if (tok < a.n) {
-        a.part_m[ch * a.n + tok] = m_run[nb];
-        a.part_d[ch * a.n + tok] = d_run[nb];
-        a.part_s[ch * a.n + tok] = s;
+        const int64_t slot = (a.chunk_base + ch) * a.n + tok;
+        a.part_m[slot] = m_run[nb];
+        a.part_d[slot] = d_run[nb];
+        a.part_s[slot] = s;
       }
     }
   }
