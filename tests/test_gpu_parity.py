@@ -129,6 +129,34 @@ def test_large_sampled_rows(name):
         assert colsum.abs().max().item() <= 1e-3 * dw.double().abs().max().item() * 64
 
 
+def test_ragged_vocab_with_multi_tile_chunks():
+    """Enough tiles for four vocabulary tiles per forward workgroup, and V not
+    a multiple of 256: the whole tiles and the partial last tile come from two
+    launches whose partials are merged.  256 sampled rows of LSE, row loss and
+    dX against the oracle; bias, softcap and label smoothing on."""
+    n, d, v = 16384, 256, 65535
+    banner(f"ragged vocabulary, multi-tile chunks n={n} d={d} v={v}")
+    inp = small_problem(n, d, v, bias=True, seed=11)
+    o = O.LossOptions(IGN, 0.1, 1e-4, 20.0, "mean")
+    x, w = U.dev_tensor(inp["x"], "bf16"), U.dev_tensor(inp["w"], "bf16")
+    b = U.dev_tensor(inp["bias"], "bf16")
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, row_loss = api.forward(x, w, t, b, check_targets=True, **U.lib_opts(o))
+    dx, dw, db = api.backward(x, w, t, lse, None, b, **U.lib_opts(o))
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(5).choice(n, 256, replace=False)
+    rows.sort()
+    n_valid = int((inp["targets"] != IGN).sum())
+    ref = O.forward_backward(inp["x"][rows], inp["w"], inp["bias"], inp["targets"][rows], o,
+                             n_valid=n_valid, want_dw=False)
+    rows_d = torch.from_numpy(rows).cuda()
+    U.assert_lse(U.host(lse[rows_d]), ref.lse)
+    rl = U.host(row_loss)
+    assert np.abs(rl[rows] - ref.row_loss).max() <= U.LSE_ABS * 2
+    U.assert_close(U.host(dx[rows_d]), ref.dx, "dX rows")
+    U.assert_loss(float(loss.item()), rl.sum() / n_valid, "loss vs its row losses")
+
+
 # ----------------------------------------------------------------- features
 FEATURES = [
     dict(),
