@@ -48,7 +48,8 @@ struct Layout {
   int64_t ldt;            // token pitch of X^T and G^T (N rounded up to 256, plus kPitchPad)
   int64_t n_merge_blocks;
   // byte offsets from the workspace base
-  int64_t ctl, zt, part_m, part_d, part_s, block_sums, fwd_end;
+  int64_t ctl, rows, tc, xc;   // shared by forward and backward
+  int64_t zt, part_m, part_d, part_s, block_sums, fwd_end;
   int64_t g, gt, xt, wt, dx_acc, bwd_end;
 };
 
@@ -83,6 +84,10 @@ Layout make_layout(const flce_params& p) {
   int64_t off = 0;
   L.ctl = off;
   off += kAlign;
+  // valid rows packed to the front: row map, targets and rows of X
+  L.rows = off;        off = round_up(off + 4 * p.n, kAlign);
+  L.tc = off;          off = round_up(off + 4 * p.n, kAlign);
+  L.xc = off;          off = round_up(off + L.elem * p.n * p.d, kAlign);
   const int64_t base = off;
   L.zt = off;          off = round_up(off + 4 * p.n, kAlign);
   L.part_m = off;      off = round_up(off + 4 * p.n * L.n_chunks, kAlign);
@@ -99,7 +104,7 @@ Layout make_layout(const flce_params& p) {
   L.wt = off;          off = round_up(off + L.elem * p.d * L.ldg, kAlign);
   const bool multi_slice = L.slice < p.v;
   L.dx_acc = off;
-  if (p.dtype == FLCE_DTYPE_BF16 && multi_slice) off = round_up(off + 4 * p.n * p.d, kAlign);
+  if (multi_slice) off = round_up(off + 4 * p.n * p.d, kAlign);   // by packed row
   L.bwd_end = off;
   return L;
 }
@@ -203,17 +208,24 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
                         float* row_loss, void* ws, hipStream_t s) {
   Ctl* ctl = reinterpret_cast<Ctl*>(at(ws, L.ctl));
   const bool mean = p.reduction == FLCE_REDUCTION_MEAN;
+  int32_t* rows = reinterpret_cast<int32_t*>(at(ws, L.rows));
+  int32_t* tc = reinterpret_cast<int32_t*>(at(ws, L.tc));
+  T* xc = reinterpret_cast<T*>(at(ws, L.xc));
   hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl);
+                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows);
   if (p.n == 0) {
     if (p.reduction != FLCE_REDUCTION_NONE) fill(loss, 1, 0.f, s);
     return launched();
   }
+  hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
+                     static_cast<const T*>(x), p.d, targets, static_cast<const int32_t*>(rows),
+                     static_cast<const Ctl*>(ctl), xc, tc);
   flce::FwdArgs<T> a{};
-  a.x = static_cast<const T*>(x);
+  a.x = xc;
   a.w = static_cast<const T*>(w);
   a.bias = static_cast<const T*>(bias);
-  a.targets = targets;
+  a.targets = tc;
+  a.ctl = ctl;
   a.n = p.n;
   a.d = p.d;
   a.v = p.v;
@@ -254,6 +266,8 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   m.row_loss = row_loss;
   m.loss_rows = p.reduction == FLCE_REDUCTION_NONE ? loss : nullptr;
   m.block_sums = reinterpret_cast<double*>(at(ws, L.block_sums));
+  m.rows = rows;
+  m.ctl = ctl;
   hipLaunchKernelGGL(flce::k_merge, dim3(static_cast<unsigned>(L.n_merge_blocks)), dim3(256), 0, s, m);
   if (p.reduction != FLCE_REDUCTION_NONE)
     hipLaunchKernelGGL(flce::k_loss_final, dim3(1), dim3(256), 0, s, m.block_sums, L.n_merge_blocks,
@@ -270,35 +284,40 @@ void launch_g(const flce::GArgs<T>& a, hipStream_t s) {
 
 template <typename T>
 void transpose(const T* in, int64_t rows, int64_t cols, int64_t ld_in, T* out, int64_t out_rows,
-               int64_t ld_out_used, int64_t ld_out, hipStream_t s) {
+               int64_t ld_out_used, int64_t ld_out, hipStream_t s, const Ctl* row_bound = nullptr) {
   const int64_t gx = cdiv(ld_out_used, 64), gy = cdiv(out_rows, 64);
   if (gx <= 0 || gy <= 0) return;
   hipLaunchKernelGGL((flce::k_transpose<T>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
-                     dim3(256), 0, s, in, rows, cols, ld_in, out, out_rows, ld_out);
+                     dim3(256), 0, s, in, rows, cols, ld_in, out, out_rows, ld_out, row_bound);
 }
 
 template <typename T>
 flce_status run_backward(const flce_params& p, const Layout& L, const void* x, const void* w,
                          const void* bias, const int32_t* targets, const float* lse,
                          const float* grad_output, void* dx, float* dw, float* dbias, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, bool packed) {
   Ctl* ctl = reinterpret_cast<Ctl*>(at(ws, L.ctl));
   const bool mean = p.reduction == FLCE_REDUCTION_MEAN;
+  int32_t* rows = reinterpret_cast<int32_t*>(at(ws, L.rows));
+  int32_t* tc = reinterpret_cast<int32_t*>(at(ws, L.tc));
+  T* xc = reinterpret_cast<T*>(at(ws, L.xc));
   hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     grad_output, mean ? 1 : 0, ctl);
+                     grad_output, mean ? 1 : 0, ctl, rows);
+  // the fused call reuses the forward's packed rows
+  if (!packed && p.n > 0)
+    hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
+                       static_cast<const T*>(x), p.d, targets, static_cast<const int32_t*>(rows),
+                       static_cast<const Ctl*>(ctl), xc, tc);
   T* g = reinterpret_cast<T*>(at(ws, L.g));
   T* gt = reinterpret_cast<T*>(at(ws, L.gt));
   T* xt = reinterpret_cast<T*>(at(ws, L.xt));
   T* wt = reinterpret_cast<T*>(at(ws, L.wt));
-  float* dx_acc = std::is_same<T, float>::value ? static_cast<float*>(dx)
-                                                : reinterpret_cast<float*>(at(ws, L.dx_acc));
-  const T* X = static_cast<const T*>(x);
+  float* dx_acc = reinterpret_cast<float*>(at(ws, L.dx_acc));
   const T* W = static_cast<const T*>(w);
-  // X^T [d][ldt], tokens >= n zero
-  transpose<T>(X, p.n, p.d, p.d, xt, p.d, round_up(p.n, tile::kN), L.ldt, s);
+  // X^T of the packed valid rows [d][ldt], tokens >= n_valid zero
+  transpose<T>(xc, p.n, p.d, p.d, xt, p.d, round_up(p.n, tile::kN), L.ldt, s, ctl);
   const int64_t n_slices = cdiv(p.v, L.slice);
   const int64_t d_tiles = cdiv(p.d, tile::kM);
-  const int64_t kdim_n = round_up(p.n, 8);
   const bool has_bias = bias != nullptr;
   for (int64_t si = 0; si < n_slices; ++si) {
     const int64_t v0 = si * L.slice;
@@ -309,10 +328,12 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
     transpose<T>(W + v0 * p.d, len, p.d, p.d, wt, p.d, gcols, L.ldg, s);
     if (p.n > 0) {
       flce::GArgs<T> ga{};
-      ga.x = X;
+      ga.x = xc;
       ga.w = W;
       ga.bias = static_cast<const T*>(bias);
-      ga.targets = targets;
+      ga.targets = tc;
+      ga.rows = rows;
+      ga.ctl = ctl;
       ga.lse = lse;
       ga.n = p.n;
       ga.d = p.d;
@@ -344,7 +365,6 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
     flce::DwArgs<T> wa{};
     wa.xt = xt;
     wa.gt = gt;
-    wa.kdim = kdim_n;
     wa.d = p.d;
     wa.v0 = v0;
     wa.slice_len = len;
@@ -367,20 +387,28 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
       xa.ldg = L.ldg;
       xa.ctl = ctl;
       xa.acc_buf = dx_acc;
+      xa.rows = rows;
       xa.dx = static_cast<T*>(dx);
       xa.first = si == 0;
-      xa.last = si + 1 == n_slices;
       xa.d_tiles = d_tiles;
       xa.n_tiles = L.n_tiles;
       xa.grid = grid8(d_tiles * L.n_tiles);
-      hipLaunchKernelGGL((flce::k_dx<T>), dim3(static_cast<unsigned>(xa.grid)), dim3(tile::kThreads),
-                         0, s, xa);
+      if (si + 1 == n_slices)
+        hipLaunchKernelGGL((flce::k_dx<T, true>), dim3(static_cast<unsigned>(xa.grid)),
+                           dim3(tile::kThreads), 0, s, xa);
+      else
+        hipLaunchKernelGGL((flce::k_dx<T, false>), dim3(static_cast<unsigned>(xa.grid)),
+                           dim3(tile::kThreads), 0, s, xa);
     }
     if (has_bias)
       hipLaunchKernelGGL((flce::k_db<T>), dim3(static_cast<unsigned>(cdiv(len, 4))), dim3(256), 0, s,
                          static_cast<const T*>(gt), L.ldt, p.n, v0, len, static_cast<const Ctl*>(ctl),
                          dbias);
   }
+  // rows of dX with an ignored target (never written by k_dx) are zero
+  if (p.n > 0)
+    hipLaunchKernelGGL((flce::k_zero_ignored_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0,
+                       s, static_cast<T*>(dx), p.d, targets, p.ignore_index);
   return launched();
 }
 
@@ -439,8 +467,9 @@ flce_status flce_backward(const flce_params* params, const void* x, const void* 
   if ((st = check_device()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
-    return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, s);
-  return run_backward<float>(p, L, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, s);
+    return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, s,
+                                  false);
+  return run_backward<float>(p, L, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, s, false);
 }
 
 flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const void* w,
@@ -459,11 +488,11 @@ flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const v
   if (p.dtype == FLCE_DTYPE_BF16) {
     st = run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
     if (st != FLCE_OK) return st;
-    return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s);
+    return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s, true);
   }
   st = run_forward<float>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
   if (st != FLCE_OK) return st;
-  return run_backward<float>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s);
+  return run_backward<float>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s, true);
 }
 
 flce_status flce_check_status(const void* ws, void* stream) {

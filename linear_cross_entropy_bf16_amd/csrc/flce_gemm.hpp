@@ -372,6 +372,16 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t grid) {
   return (wg & 7) * per + (wg >> 3);
 }
 
+// The same for a tile count known only on the device (valid rows): the grid
+// is sized for the upper bound, each XCD takes an equal share of the `total`
+// tiles and its surplus workgroups return false.
+__device__ __forceinline__ bool xcd_logical_n(int64_t wg, int64_t total, int64_t& L) {
+  const int64_t per = (total + 7) >> 3;
+  const int64_t i = wg >> 3;
+  L = (wg & 7) * per + i;
+  return i < per && L < total;
+}
+
 // Grouped raster: logical tile -> (a, b) with `group` consecutive a-tiles
 // sharing each b, so tiles in flight on one XCD reuse each other's panels.
 __device__ __forceinline__ void grouped(int64_t L, int64_t ta, int64_t tb, int64_t group,

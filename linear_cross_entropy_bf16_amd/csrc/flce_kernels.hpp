@@ -74,43 +74,84 @@ __device__ __forceinline__ void lse_merge(float& m, float& d, float m2, float d2
 __global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targets, int64_t n,
                                                int64_t v, int32_t ignore_index,
                                                const float* __restrict__ grad_output,
-                                               int32_t reduction_mean, Ctl* __restrict__ ctl) {
+                                               int32_t reduction_mean, Ctl* __restrict__ ctl,
+                                               int32_t* __restrict__ rows) {
+  // thread t owns rows [t * per, (t + 1) * per); an inclusive scan of the
+  // per-thread counts places each thread's valid rows, in order, in `rows`
   __shared__ int32_t s_cnt[1024];
   __shared__ int32_t s_bad[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t lo = tid * per, hi = lo + per < n ? lo + per : n;
   int32_t cnt = 0, bad = 0;
-  for (int64_t i = threadIdx.x; i < n; i += 1024) {
+  for (int64_t i = lo; i < hi; ++i) {
     const int32_t t = targets[i];
     const bool ign = t == ignore_index;
     cnt += ign ? 0 : 1;
     bad |= (!ign && (t < 0 || static_cast<int64_t>(t) >= v)) ? 1 : 0;
   }
-  s_cnt[threadIdx.x] = cnt;
-  s_bad[threadIdx.x] = bad;
+  s_cnt[tid] = cnt;
+  s_bad[tid] = bad;
   __syncthreads();
-  for (int s = 512; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      s_cnt[threadIdx.x] += s_cnt[threadIdx.x + s];
-      s_bad[threadIdx.x] |= s_bad[threadIdx.x + s];
-    }
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t c = tid >= off ? s_cnt[tid - off] : 0;
+    const int32_t e = tid >= off ? s_bad[tid - off] : 0;
+    __syncthreads();
+    s_cnt[tid] += c;
+    s_bad[tid] |= e;
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    const int32_t nv = s_cnt[0];
+  int32_t k = s_cnt[tid] - cnt;
+  for (int64_t i = lo; i < hi; ++i)
+    if (targets[i] != ignore_index) rows[k++] = static_cast<int32_t>(i);
+  if (tid == 1023) {
+    const int32_t nv = s_cnt[1023];
     const float g = grad_output ? grad_output[0] : 1.0f;
     ctl->n_valid = nv;
-    ctl->status = s_bad[0];
+    ctl->status = s_bad[1023];
     ctl->scale = reduction_mean ? (nv > 0 ? g / static_cast<float>(nv) : 0.0f) : g;
     ctl->pad = 0.0f;
   }
 }
 
+// Valid rows of X (and their targets) packed to the front, in row order: every
+// GEMM below runs on n_valid rows only (ignored rows have zero loss and zero
+// gradient, page "Cutting LLM Memory by 84%", "Kernel Implementation").
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ x, int64_t d,
+                                                     const int32_t* __restrict__ targets,
+                                                     const int32_t* __restrict__ rows,
+                                                     const Ctl* __restrict__ ctl,
+                                                     T* __restrict__ xc, int32_t* __restrict__ tc) {
+  const int64_t j = blockIdx.x;
+  if (j >= ctl->n_valid) return;
+  const int64_t r = rows[j];
+  const uint4* src = reinterpret_cast<const uint4*>(x + r * d);   // d * sizeof(T) is a multiple of 16
+  uint4* dst = reinterpret_cast<uint4*>(xc + j * d);
+  const int64_t vecs = d * static_cast<int64_t>(sizeof(T)) / 16;
+  for (int64_t i = threadIdx.x; i < vecs; i += 256) dst[i] = src[i];
+  if (threadIdx.x == 0) tc[j] = targets[r];
+}
+
+// Rows of dX whose target is ignore_index are zero.
+template <typename T>
+__global__ __launch_bounds__(256) void k_zero_ignored_rows(T* __restrict__ dx, int64_t d,
+                                                           const int32_t* __restrict__ targets,
+                                                           int32_t ignore_index) {
+  const int64_t r = blockIdx.x;
+  if (targets[r] != ignore_index) return;
+  uint4* dst = reinterpret_cast<uint4*>(dx + r * d);
+  const int64_t vecs = d * static_cast<int64_t>(sizeof(T)) / 16;
+  for (int64_t i = threadIdx.x; i < vecs; i += 256) dst[i] = uint4{0u, 0u, 0u, 0u};
+}
+
 // ------------------------------------------------------------------- forward
 template <typename T>
 struct FwdArgs {
-  const T* x;             // [n, d]
+  const T* x;             // [n, d] valid rows packed to the front (n_valid of them)
   const T* w;             // [v, d]
   const T* bias;          // [v] or null
-  const int32_t* targets;
+  const int32_t* targets;  // packed like x
   int64_t n, d, v;
   float softcap, inv_softcap;
   int64_t n_tiles, n_chunks, tiles_per_chunk, grid, group;
@@ -119,7 +160,8 @@ struct FwdArgs {
   float* part_m;          // [n_chunks, n] running max, log2 units
   float* part_d;          // [n_chunks, n] sum of 2^(z log2e - m)
   float* part_s;          // [n_chunks, n] sum of z
-  float* zt;              // [n] target logit
+  float* zt;              // [n] target logit, by packed row
+  const Ctl* ctl;         // n_valid: rows of x (packed) that take part
 };
 
 // max without NaN canonicalisation (logits here are finite or -inf)
@@ -189,10 +231,13 @@ void k_fwd(FwdArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
   // wave-row exchange of the final partials; gemm_tile has released `lds` by then
   float (*xch)[2][4][32] = reinterpret_cast<float (*)[2][4][32]>(lds);
-  const int64_t L = xcd_logical(blockIdx.x, a.grid);
-  if (L >= a.n_tiles * a.n_chunks) return;   // whole workgroup leaves together
+  // token tiles of the valid rows only, spread evenly over the XCDs
+  const int64_t nv = a.ctl->n_valid;
+  const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;
+  int64_t L;
+  if (!xcd_logical_n(blockIdx.x, n_tiles * a.n_chunks, L)) return;   // whole workgroup leaves
   int64_t nt, ch;
-  grouped(L, a.n_tiles, a.n_chunks, a.group, nt, ch);
+  grouped(L, n_tiles, a.n_chunks, a.group, nt, ch);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -202,14 +247,14 @@ void k_fwd(FwdArgs<T> a) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
-    tgt[nb] = tok < a.n ? a.targets[tok] : -1;
+    tgt[nb] = tok < nv ? a.targets[tok] : -1;
   }
   float m_run[4], d_run[4], s_run[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) { m_run[nb] = -INFINITY; d_run[nb] = 0.f; s_run[nb] = 0.f; }
 
   const Operand<T> A{a.w, a.d, a.v, a.d};   // rows: vocabulary
-  const Operand<T> B{a.x, a.d, a.n, a.d};   // rows: tokens
+  const Operand<T> B{a.x, a.d, nv, a.d};    // rows: valid tokens
   const int64_t vt_first = a.vt_base + ch * a.tiles_per_chunk;
   const int64_t vt_end = vt_first + a.tiles_per_chunk < a.vt_end ? vt_first + a.tiles_per_chunk
                                                                  : a.vt_end;
@@ -253,7 +298,7 @@ void k_fwd(FwdArgs<T> a) {
       lse_merge(m_run[nb], d_run[nb], xch[0][wn][nb][lane], xch[1][wn][nb][lane]);
       const float s = s_run[nb] + xch[2][wn][nb][lane];
       const int64_t tok = n0 + wn * 128 + nb * 32 + lane;
-      if (tok < a.n) {
+      if (tok < nv) {
         const int64_t slot = (a.chunk_base + ch) * a.n + tok;
         a.part_m[slot] = m_run[nb];
         a.part_d[slot] = d_run[nb];
@@ -278,28 +323,35 @@ struct MergeArgs {
   float* row_loss;      // [n] or null
   float* loss_rows;     // [n] or null (reduction none)
   double* block_sums;   // [gridDim.x]
+  const int32_t* rows;  // packed row -> row
+  const Ctl* ctl;
 };
 
 // lse = (m + log2 d) ln 2; row loss = lse - (1-eps) z_t - (eps/V) sum z + s lse^2
 // on valid rows, 0 elsewhere.
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   __shared__ double red[256];
-  const int64_t tok = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t nv = a.ctl->n_valid;
   double row = 0.0;
-  if (tok < a.n) {
+  if (j < nv) {                      // packed row j: partials, target logit, sum z by packed index
     float m = -INFINITY, d = 0.f, s = 0.f;
     for (int64_t c = 0; c < a.n_chunks; ++c) {
-      lse_merge(m, d, a.part_m[c * a.n + tok], a.part_d[c * a.n + tok]);
-      s += a.part_s[c * a.n + tok];
+      lse_merge(m, d, a.part_m[c * a.n + j], a.part_d[c * a.n + j]);
+      s += a.part_s[c * a.n + j];
     }
     const float lse = (m + log2f(d)) * kLn2;
-    const bool valid = a.targets[tok] != a.ignore_index;
-    const float rl = lse - a.keep_target * a.zt[tok] - a.eps_over_v * s + a.zloss * lse * lse;
-    const float rlv = valid ? rl : 0.f;
-    a.lse[tok] = valid ? lse : 0.f;
-    if (a.row_loss) a.row_loss[tok] = rlv;
-    if (a.loss_rows) a.loss_rows[tok] = rlv;
-    row = rlv;
+    const float rl = lse - a.keep_target * a.zt[j] - a.eps_over_v * s + a.zloss * lse * lse;
+    const int64_t r = a.rows[j];
+    a.lse[r] = lse;
+    if (a.row_loss) a.row_loss[r] = rl;
+    if (a.loss_rows) a.loss_rows[r] = rl;
+    row = rl;
+  }
+  if (j < a.n && a.targets[j] == a.ignore_index) {   // row j itself, if ignored
+    a.lse[j] = 0.f;
+    if (a.row_loss) a.row_loss[j] = 0.f;
+    if (a.loss_rows) a.loss_rows[j] = 0.f;
   }
   red[threadIdx.x] = row;
   __syncthreads();
@@ -340,8 +392,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, int64_t rows,
                                                    int64_t cols, int64_t ld_in,
                                                    T* __restrict__ out, int64_t out_rows,
-                                                   int64_t ld_out) {
+                                                   int64_t ld_out, const Ctl* __restrict__ ctl) {
   __shared__ T t[64][65];
+  if (ctl && ctl->n_valid < rows) rows = ctl->n_valid;   // X: only the packed valid rows
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -375,8 +428,10 @@ struct GArgs {
   float two_s;          // 2 s (z-loss)
   int64_t v0, slice_len, ldg, ldt;
   T* g;                 // [n, ldg]       G slice, columns >= slice_len written as 0
-  T* gt;                // [gcols, ldt]   the same slice transposed, tokens >= n as 0
+  T* gt;                // [gcols, ldt]   the same slice transposed, tokens >= n_valid as 0
   int64_t n_tiles, s_tiles, grid, group;
+  const int32_t* rows;  // packed row -> row (lse is stored by row)
+  const Ctl* ctl;
 };
 
 __device__ __forceinline__ void store1(uint16_t* p, float a) {
@@ -393,7 +448,7 @@ static_assert(256 * kStagePitch * 2 <= tile::kLdsBytes, "staged G tile exceeds L
 template <typename T>
 __device__ __forceinline__ void store_g_staged(const GArgs<T>& a, const f32x16 (&acc)[4][4],
                                                char* lds, int64_t n0, int64_t vl0, int vw, int wn,
-                                               int lane, int tid) {
+                                               int lane, int tid, int64_t nv) {
   uint16_t* sm = reinterpret_cast<uint16_t*>(lds);
   const int tcol = wn * 128 + (lane & 31);        // tile-local token of (nb = 0)
   // G^T: staged row = vocabulary, 256 tokens per row
@@ -429,7 +484,7 @@ __device__ __forceinline__ void store_g_staged(const GArgs<T>& a, const f32x16 (
 #pragma unroll 4
   for (int i = 0; i < 32; ++i) {
     const int row = row0 + 8 * i;
-    if (n0 + row < a.n) {
+    if (n0 + row < nv) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(sm + row * kStagePitch + chunk * 8);
       *reinterpret_cast<u32x4*>(a.g + (n0 + row) * a.ldg + vl0 + chunk * 8) = v;
     }
@@ -439,7 +494,8 @@ __device__ __forceinline__ void store_g_staged(const GArgs<T>& a, const f32x16 (
 // fp32 G tile (too large to stage): stored from the accumulator layout.
 template <typename T>
 __device__ __forceinline__ void store_g_direct(const GArgs<T>& a, const f32x16 (&acc)[4][4],
-                                               int64_t n0, int64_t vl0, int vw, int wn, int lane) {
+                                               int64_t n0, int64_t vl0, int vw, int wn, int lane,
+                                               int64_t nv) {
   const int ldt = static_cast<int>(a.ldt);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -452,7 +508,7 @@ __device__ __forceinline__ void store_g_direct(const GArgs<T>& a, const f32x16 (
       for (int q = 0; q < 4; ++q) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) store1(col + (mb * 32 + 8 * q + j) * ldt, acc[mb][nb][4 * q + j]);
-        if (tok < a.n)
+        if (tok < nv)
           store4(row + vw + mb * 32 + 8 * q, acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
                  acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
       }
@@ -467,16 +523,18 @@ template <typename T, bool kBias, bool kSoftcap>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bwd_g(GArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
-  const int64_t L = xcd_logical(blockIdx.x, a.grid);
-  if (L >= a.n_tiles * a.s_tiles) return;
+  const int64_t nv = a.ctl->n_valid;
+  const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;   // valid rows only
+  int64_t L;
+  if (!xcd_logical_n(blockIdx.x, n_tiles * a.s_tiles, L)) return;
   int64_t nt, st;
-  grouped(L, a.n_tiles, a.s_tiles, a.group, nt, st);
+  grouped(L, n_tiles, a.s_tiles, a.group, nt, st);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t n0 = nt * tile::kN, vl0 = st * tile::kM;
 
   const Operand<T> A{a.w + a.v0 * a.d, a.d, a.v - a.v0, a.d};
-  const Operand<T> B{a.x, a.d, a.n, a.d};
+  const Operand<T> B{a.x, a.d, nv, a.d};       // packed valid rows
   f32x16 acc[4][4];
   gemm_tile(A, B, vl0, n0, a.d, lds, acc);
 
@@ -491,10 +549,10 @@ void k_bwd_g(GArgs<T> a) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
-    const bool tin = tok < a.n;
+    const bool tin = tok < nv;
     const int32_t t = tin ? a.targets[tok] : a.ignore_index;
     valid[nb] = tin && t != a.ignore_index;
-    const float l = valid[nb] ? a.lse[tok] : 0.f;
+    const float l = valid[nb] ? a.lse[a.rows[tok]] : 0.f;
     lse2[nb] = l * kLog2e;
     zfac[nb] = 1.0f + a.two_s * l;
     const int64_t rel64 = static_cast<int64_t>(t) - a.v0 - vl0 - vw;
@@ -526,16 +584,16 @@ void k_bwd_g(GArgs<T> a) {
       }
     }
   if constexpr (sizeof(T) == 2)
-    store_g_staged(a, acc, lds, n0, vl0, vw, wn, lane, tid);
+    store_g_staged(a, acc, lds, n0, vl0, vw, wn, lane, tid, nv);
   else
-    store_g_direct(a, acc, n0, vl0, vw, wn, lane);
+    store_g_direct(a, acc, n0, vl0, vw, wn, lane, nv);
 }
 
 template <typename T>
 struct DwArgs {
-  const T* xt;          // [d, ldt]      X^T, tokens >= n are 0
+  const T* xt;          // [d, ldt]      X^T of the packed rows, tokens >= n_valid are 0
   const T* gt;          // [gcols, ldt]  G^T slice
-  int64_t kdim, d, v0, slice_len, ldt, gcols;
+  int64_t d, v0, slice_len, ldt, gcols;
   const Ctl* ctl;
   float* dw;            // [v, d]
   int64_t d_tiles, s_tiles, grid;
@@ -557,10 +615,11 @@ void k_dw(DwArgs<T> a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const Operand<T> A{a.xt, a.ldt, a.d, a.kdim};       // (d, n) at xt[d*ldt + n]
-  const Operand<T> B{a.gt, a.ldt, a.gcols, a.kdim};   // (v, n) at gt[v*ldt + n]
+  const int64_t kdim = (static_cast<int64_t>(a.ctl->n_valid) + 7) / 8 * 8;   // packed valid rows
+  const Operand<T> A{a.xt, a.ldt, a.d, kdim};       // (d, n) at xt[d*ldt + n]
+  const Operand<T> B{a.gt, a.ldt, a.gcols, kdim};   // (v, n) at gt[v*ldt + n]
   f32x16 acc[4][4];
-  gemm_tile(A, B, dt * tile::kM, st * tile::kN, a.kdim, lds, acc);
+  gemm_tile(A, B, dt * tile::kM, st * tile::kN, kdim, lds, acc);
 
   const float scale = a.ctl->scale;
 #pragma unroll
@@ -583,13 +642,14 @@ void k_dw(DwArgs<T> a) {
 template <typename T>
 struct DxArgs {
   const T* wt;          // [d, ldg]  W^T slice, vocabulary >= slice length is 0
-  const T* g;           // [n, ldg]
+  const T* g;           // [n, ldg]  packed rows
   int64_t n, d, kdim, ldg;
   const Ctl* ctl;
-  float* acc_buf;       // [n, d] fp32 running sum over slices
+  float* acc_buf;       // [n, d] fp32 running sum over slices, by packed row
   T* dx;                // [n, d]
-  int32_t first, last;
+  int32_t first;
   int64_t d_tiles, n_tiles, grid;
+  const int32_t* rows;  // packed row -> row
 };
 
 // dX (+)= scale G_slice W_slice, computed as C[d, n]; the running fp32 sum
@@ -597,19 +657,21 @@ struct DxArgs {
 // dX in its own dtype.
 constexpr int kDxPitch = 260;   // fp32 per staged token row (256 + 4)
 static_assert(128 * kDxPitch * 4 <= tile::kLdsBytes, "staged dX half tile exceeds LDS");
-template <typename T>
+// kLast: the last slice, which scatters the finished rows to dX.
+template <typename T, bool kLast>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_dx(DxArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
-  const int64_t L = xcd_logical(blockIdx.x, a.grid);
-  if (L >= a.d_tiles * a.n_tiles) return;
+  const int64_t nv = a.ctl->n_valid;
+  const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;   // valid rows only
+  int64_t L;
+  if (!xcd_logical_n(blockIdx.x, a.d_tiles * n_tiles, L)) return;
   int64_t nt, dt;
-  grouped(L, a.n_tiles, a.d_tiles, kGroup, nt, dt);
+  grouped(L, n_tiles, a.d_tiles, kGroup, nt, dt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-
   const Operand<T> A{a.wt, a.ldg, a.d, a.kdim};   // (d, v) at wt[d*ldg + v]
-  const Operand<T> B{a.g, a.ldg, a.n, a.kdim};    // (n, v) at g[n*ldg + v]
+  const Operand<T> B{a.g, a.ldg, nv, a.kdim};     // (packed row, v) at g[n*ldg + v]
   f32x16 acc[4][4];
   gemm_tile(A, B, dt * tile::kM, nt * tile::kN, a.kdim, lds, acc);
 
@@ -626,12 +688,14 @@ void k_dx(DxArgs<T> a) {
     // this half's previous sums are requested first and land while the
     // tile is being staged
     float4 prev[32];
+    int32_t dst_row[kLast ? 32 : 1];   // the row of dX each packed row goes to
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int64_t tok = tok0 + h * 128 + row0 + 4 * i;
       prev[i] = float4{0.f, 0.f, 0.f, 0.f};
-      if (!a.first && tok < a.n && cols_ok)
+      if (!a.first && tok < nv && cols_ok)
         prev[i] = *reinterpret_cast<const float4*>(a.acc_buf + tok * a.d + d0 + 4 * chunk);
+      if constexpr (kLast) dst_row[i] = tok < nv ? a.rows[tok] : 0;
     }
     if (wn == h) {
 #pragma unroll
@@ -651,14 +715,13 @@ void k_dx(DxArgs<T> a) {
     for (int i = 0; i < 32; ++i) {
       const int row = row0 + 4 * i;
       const int64_t tok = tok0 + h * 128 + row;
-      if (tok < a.n && cols_ok) {
+      if (tok < nv && cols_ok) {
         float4 v = *reinterpret_cast<const float4*>(sm + row * kDxPitch + 4 * chunk);
         v.x += prev[i].x; v.y += prev[i].y; v.z += prev[i].z; v.w += prev[i].w;
-        const int64_t off = tok * a.d + d0 + 4 * chunk;
-        if (a.last)
-          store4(a.dx + off, v.x, v.y, v.z, v.w);
+        if constexpr (kLast)
+          store4(a.dx + static_cast<int64_t>(dst_row[i]) * a.d + d0 + 4 * chunk, v.x, v.y, v.z, v.w);
         else
-          *reinterpret_cast<float4*>(a.acc_buf + off) = v;
+          *reinterpret_cast<float4*>(a.acc_buf + tok * a.d + d0 + 4 * chunk) = v;
       }
     }
     __syncthreads();
@@ -675,8 +738,9 @@ __global__ __launch_bounds__(256) void k_db(const T* __restrict__ gt, int64_t ld
   if (v >= slice_len) return;
   const int lane = threadIdx.x & 63;
   const T* row = gt + v * ldt;
+  const int64_t nv = ctl->n_valid < n ? ctl->n_valid : n;
   float s = 0.f;
-  for (int64_t i = lane; i < n; i += 64) s += ld_elem(row, i);
+  for (int64_t i = lane; i < nv; i += 64) s += ld_elem(row, i);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
   if (lane == 0) db[v0 + v] = ctl->scale * s;

@@ -73,7 +73,9 @@ def test_workspace_never_holds_the_logits():
     assert round(4 * n * v / 1e9, 1) == g["logits_fp32_gb"]
     p = _lib.make_params(n, d, v, _lib.DTYPE_BF16)
     ws = _lib.workspace_size(p, True)
-    assert 0 < ws < 2 * n * v / 4          # under a quarter of one bf16 copy of the logits
+    # under a third of one bf16 copy of the logits (the workspace holds one G
+    # slice in both orientations, X^T, the fp32 dX sum and the packed valid rows of X)
+    assert 0 < ws < 2 * n * v / 3
     assert _lib.workspace_size(p, False) < ws
 
 
