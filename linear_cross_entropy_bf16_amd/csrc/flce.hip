@@ -185,9 +185,9 @@ void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
     m.chunk_base = 0;
     m.n_chunks = L.main_chunks;
     m.tiles_per_chunk = L.tiles_per_chunk;
-    m.grid = grid8(L.n_tiles * m.n_chunks);
     hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, false>),
-                       dim3(static_cast<unsigned>(m.grid)), dim3(tile::kThreads), 0, s, m);
+                       dim3(static_cast<unsigned>(grid8(L.n_tiles * m.n_chunks))),
+                       dim3(tile::kThreads), 0, s, m);
   }
   if (L.v_full < L.v_tiles) {
     flce::FwdArgs<T> t = a;
@@ -196,9 +196,8 @@ void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
     t.chunk_base = L.main_chunks;
     t.n_chunks = 1;
     t.tiles_per_chunk = 1;
-    t.grid = grid8(L.n_tiles);
     hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, true>),
-                       dim3(static_cast<unsigned>(t.grid)), dim3(tile::kThreads), 0, s, t);
+                       dim3(static_cast<unsigned>(grid8(L.n_tiles))), dim3(tile::kThreads), 0, s, t);
   }
 }
 
@@ -231,7 +230,6 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.v = p.v;
   a.softcap = p.softcap;
   a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
-  a.n_tiles = L.n_tiles;
   a.group = kRasterGroup;
   a.part_m = reinterpret_cast<float*>(at(ws, L.part_m));
   a.part_d = reinterpret_cast<float*>(at(ws, L.part_d));
@@ -277,8 +275,8 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
 
 // ----------------------------------------------------------------- backward
 template <typename T, bool kBias, bool kSoftcap>
-void launch_g(const flce::GArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((flce::k_bwd_g<T, kBias, kSoftcap>), dim3(static_cast<unsigned>(a.grid)),
+void launch_g(const flce::GArgs<T>& a, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((flce::k_bwd_g<T, kBias, kSoftcap>), dim3(static_cast<unsigned>(grid)),
                      dim3(tile::kThreads), 0, s, a);
 }
 
@@ -350,16 +348,15 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
       ga.ldt = L.ldt;
       ga.g = g;
       ga.gt = gt;
-      ga.n_tiles = L.n_tiles;
       ga.s_tiles = s_tiles;
-      ga.grid = grid8(L.n_tiles * s_tiles);
+      const int64_t g_grid = grid8(L.n_tiles * s_tiles);   // upper bound: all rows valid
       ga.group = kRasterGroup;
       const int key = (has_bias ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
       switch (key) {
-        case 0: launch_g<T, false, false>(ga, s); break;
-        case 1: launch_g<T, true, false>(ga, s); break;
-        case 2: launch_g<T, false, true>(ga, s); break;
-        default: launch_g<T, true, true>(ga, s); break;
+        case 0: launch_g<T, false, false>(ga, g_grid, s); break;
+        case 1: launch_g<T, true, false>(ga, g_grid, s); break;
+        case 2: launch_g<T, false, true>(ga, g_grid, s); break;
+        default: launch_g<T, true, true>(ga, g_grid, s); break;
       }
     }
     flce::DwArgs<T> wa{};
@@ -391,13 +388,12 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
       xa.dx = static_cast<T*>(dx);
       xa.first = si == 0;
       xa.d_tiles = d_tiles;
-      xa.n_tiles = L.n_tiles;
-      xa.grid = grid8(d_tiles * L.n_tiles);
+      const int64_t x_grid = grid8(d_tiles * L.n_tiles);   // upper bound: all rows valid
       if (si + 1 == n_slices)
-        hipLaunchKernelGGL((flce::k_dx<T, true>), dim3(static_cast<unsigned>(xa.grid)),
+        hipLaunchKernelGGL((flce::k_dx<T, true>), dim3(static_cast<unsigned>(x_grid)),
                            dim3(tile::kThreads), 0, s, xa);
       else
-        hipLaunchKernelGGL((flce::k_dx<T, false>), dim3(static_cast<unsigned>(xa.grid)),
+        hipLaunchKernelGGL((flce::k_dx<T, false>), dim3(static_cast<unsigned>(x_grid)),
                            dim3(tile::kThreads), 0, s, xa);
     }
     if (has_bias)

@@ -154,7 +154,7 @@ struct FwdArgs {
   const int32_t* targets;  // packed like x
   int64_t n, d, v;
   float softcap, inv_softcap;
-  int64_t n_tiles, n_chunks, tiles_per_chunk, grid, group;
+  int64_t n_chunks, tiles_per_chunk, group;   // chunks of this launch; tiles per chunk
   int64_t vt_base, vt_end;   // vocabulary tiles [vt_base, vt_end) of this launch
   int64_t chunk_base;        // partials row of this launch's first chunk
   float* part_m;          // [n_chunks, n] running max, log2 units
@@ -429,7 +429,7 @@ struct GArgs {
   int64_t v0, slice_len, ldg, ldt;
   T* g;                 // [n, ldg]       G slice, columns >= slice_len written as 0
   T* gt;                // [gcols, ldt]   the same slice transposed, tokens >= n_valid as 0
-  int64_t n_tiles, s_tiles, grid, group;
+  int64_t s_tiles, group;   // vocabulary tiles of the slice; raster group
   const int32_t* rows;  // packed row -> row (lse is stored by row)
   const Ctl* ctl;
 };
@@ -648,7 +648,7 @@ struct DxArgs {
   float* acc_buf;       // [n, d] fp32 running sum over slices, by packed row
   T* dx;                // [n, d]
   int32_t first;
-  int64_t d_tiles, n_tiles, grid;
+  int64_t d_tiles;
   const int32_t* rows;  // packed row -> row
 };
 
