@@ -15,7 +15,9 @@
  *
  * Rows with t_n == ignore_index are not valid: their loss and lse are 0 and
  * their gradient rows are 0 (page "Cutting LLM Memory by 84%", "Kernel
- * Implementation", step 1).  The backward recomputes softmax tiles from the
+ * Implementation", step 1).  They take no part in any contraction: the valid
+ * rows are packed (in order) into the workspace first and every GEMM runs on
+ * those only.  The backward recomputes softmax tiles from the
  * saved LSE and forms G = [softmax(z)(1 + 2 s lse) - (1-eps) onehot - eps/V]
  * (times 1 - (z/c)^2 under the softcap), then dX = scale G W and
  * dW = scale G^T X, db = scale sum_n G, with scale = g / n_valid ('mean') or g
@@ -93,7 +95,9 @@ typedef struct flce_params {
 /* Bytes of workspace the calls need for these parameters.  with_backward = 0
  * sizes flce_forward only; 1 sizes flce_backward and flce_fused_fwd_bwd (and
  * also covers flce_forward).  Returns 0 for invalid parameters.  The size is
- * O(N (V/1024 + D) + N * vocab_slice), far below the N x V logits. */
+ * O(N (V/1024 + D) + N * vocab_slice), far below the N x V logits: the packed
+ * valid rows of X, per-row forward partials, and for the backward one G slice
+ * in both orientations, X^T and an fp32 dX accumulator. */
 size_t flce_workspace_size(const flce_params* params, int with_backward);
 
 /* Forward: loss and per-row LSE.
