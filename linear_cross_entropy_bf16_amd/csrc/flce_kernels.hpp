@@ -76,39 +76,46 @@ __global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targe
                                                const float* __restrict__ grad_output,
                                                int32_t reduction_mean, Ctl* __restrict__ ctl,
                                                int32_t* __restrict__ rows) {
-  // thread t owns rows [t * per, (t + 1) * per); an inclusive scan of the
-  // per-thread counts places each thread's valid rows, in order, in `rows`
-  __shared__ int32_t s_cnt[1024];
-  __shared__ int32_t s_bad[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t lo = tid * per, hi = lo + per < n ? lo + per : n;
+  // Wave w owns the contiguous rows [w * per, (w + 1) * per) and walks them 64
+  // at a time (coalesced); a ballot gives each valid row its place, so the
+  // valid rows land in `rows` in row order.
+  __shared__ int32_t s_cnt[16];
+  __shared__ int32_t s_bad[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t per = ((n + 15) / 16 + 63) / 64 * 64;
+  const int64_t lo = wave * per, hi = lo + per < n ? lo + per : n;
   int32_t cnt = 0, bad = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    const int32_t t = targets[i];
-    const bool ign = t == ignore_index;
-    cnt += ign ? 0 : 1;
-    bad |= (!ign && (t < 0 || static_cast<int64_t>(t) >= v)) ? 1 : 0;
+  for (int64_t i0 = lo; i0 < hi; i0 += 64) {
+    const int64_t i = i0 + lane;
+    const int32_t t = i < hi ? targets[i] : ignore_index;
+    const bool ok = t != ignore_index;
+    cnt += __popcll(__ballot(ok));
+    bad |= (ok && (t < 0 || static_cast<int64_t>(t) >= v)) ? 1 : 0;
   }
-  s_cnt[tid] = cnt;
-  s_bad[tid] = bad;
+  bad = __ballot(bad) != 0 ? 1 : 0;
+  if (lane == 0) {
+    s_cnt[wave] = cnt;
+    s_bad[wave] = bad;
+  }
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t c = tid >= off ? s_cnt[tid - off] : 0;
-    const int32_t e = tid >= off ? s_bad[tid - off] : 0;
-    __syncthreads();
-    s_cnt[tid] += c;
-    s_bad[tid] |= e;
-    __syncthreads();
+  int32_t k = 0, nv = 0, any_bad = 0;
+  for (int w = 0; w < 16; ++w) {
+    k += w < wave ? s_cnt[w] : 0;
+    nv += s_cnt[w];
+    any_bad |= s_bad[w];
   }
-  int32_t k = s_cnt[tid] - cnt;
-  for (int64_t i = lo; i < hi; ++i)
-    if (targets[i] != ignore_index) rows[k++] = static_cast<int32_t>(i);
-  if (tid == 1023) {
-    const int32_t nv = s_cnt[1023];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes under this one
+  for (int64_t i0 = lo; i0 < hi; i0 += 64) {
+    const int64_t i = i0 + lane;
+    const bool ok = i < hi && targets[i] != ignore_index;
+    const uint64_t m = __ballot(ok);
+    if (ok) rows[k + __popcll(m & below)] = static_cast<int32_t>(i);
+    k += __popcll(m);
+  }
+  if (threadIdx.x == 0) {
     const float g = grad_output ? grad_output[0] : 1.0f;
     ctl->n_valid = nv;
-    ctl->status = s_bad[1023];
+    ctl->status = any_bad;
     ctl->scale = reduction_mean ? (nv > 0 ? g / static_cast<float>(nv) : 0.0f) : g;
     ctl->pad = 0.0f;
   }
