@@ -50,7 +50,7 @@ struct Layout {
   // byte offsets from the workspace base
   int64_t ctl, rows, tc, xc;   // shared by forward and backward
   int64_t zt, part_m, part_d, part_s, block_sums, fwd_end;
-  int64_t g, gt, xt, wt, dx_acc, bwd_end;
+  int64_t g, gt, xt, wt, dx_acc, lsep, bwd_end;
 };
 
 Layout make_layout(const flce_params& p) {
@@ -105,6 +105,7 @@ Layout make_layout(const flce_params& p) {
   const bool multi_slice = L.slice < p.v;
   L.dx_acc = off;
   if (multi_slice) off = round_up(off + 4 * p.n * p.d, kAlign);   // by packed row
+  L.lsep = off;        off = round_up(off + 4 * p.n, kAlign);
   L.bwd_end = off;
   return L;
 }
@@ -311,6 +312,10 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
   T* xt = reinterpret_cast<T*>(at(ws, L.xt));
   T* wt = reinterpret_cast<T*>(at(ws, L.wt));
   float* dx_acc = reinterpret_cast<float*>(at(ws, L.dx_acc));
+  float* lsep = reinterpret_cast<float*>(at(ws, L.lsep));
+  if (p.n > 0)
+    hipLaunchKernelGGL(flce::k_pack_lse, dim3(static_cast<unsigned>(cdiv(p.n, 256))), dim3(256), 0, s,
+                       lse, static_cast<const int32_t*>(rows), static_cast<const Ctl*>(ctl), lsep);
   const T* W = static_cast<const T*>(w);
   // X^T of the packed valid rows [d][ldt], tokens >= n_valid zero
   transpose<T>(xc, p.n, p.d, p.d, xt, p.d, round_up(p.n, tile::kN), L.ldt, s, ctl);
@@ -330,9 +335,8 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
       ga.w = W;
       ga.bias = static_cast<const T*>(bias);
       ga.targets = tc;
-      ga.rows = rows;
       ga.ctl = ctl;
-      ga.lse = lse;
+      ga.lsep = lsep;
       ga.n = p.n;
       ga.d = p.d;
       ga.v = p.v;

@@ -7,6 +7,7 @@
 //   k_merge       partials -> lse, per-row loss, per-block loss sums
 //   k_loss_final  fixed-order sum of the block sums -> scalar loss
 //   k_transpose   X^T once per backward, W^T once per vocabulary slice
+//   k_pack_lse    lse of the valid rows, in packed-row order
 //   k_bwd_g       recomputed logits of one vocabulary slice -> G slice, in
 //                 both orientations
 //   k_dw          dW[slice] = scale G_slice^T X   (K = N, written once)
@@ -40,9 +41,11 @@ __device__ __forceinline__ float ld_elem(const uint16_t* p, int64_t i) {
 }
 __device__ __forceinline__ float ld_elem(const float* p, int64_t i) { return p[i]; }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (round to nearest even) in one dword, a in the low half
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 __device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
   *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
@@ -138,6 +141,16 @@ __global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ x, in
   const int64_t vecs = d * static_cast<int64_t>(sizeof(T)) / 16;
   for (int64_t i = threadIdx.x; i < vecs; i += 256) dst[i] = src[i];
   if (threadIdx.x == 0) tc[j] = targets[r];
+}
+
+// lse of each valid row in packed-row order, so the backward's per-token loads
+// are independent of the row map.
+__global__ __launch_bounds__(256) void k_pack_lse(const float* __restrict__ lse,
+                                                  const int32_t* __restrict__ rows,
+                                                  const Ctl* __restrict__ ctl,
+                                                  float* __restrict__ lsep) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j < ctl->n_valid) lsep[j] = lse[rows[j]];
 }
 
 // Rows of dX whose target is ignore_index are zero.
@@ -426,7 +439,7 @@ struct GArgs {
   const T* w;
   const T* bias;
   const int32_t* targets;
-  const float* lse;
+  const float* lsep;    // lse by packed row
   int64_t n, d, v;
   int32_t ignore_index;
   float softcap, inv_softcap;
@@ -437,7 +450,6 @@ struct GArgs {
   T* g;                 // [n, ldg]       G slice, columns >= slice_len written as 0
   T* gt;                // [gcols, ldt]   the same slice transposed, tokens >= n_valid as 0
   int64_t s_tiles, group;   // vocabulary tiles of the slice; raster group
-  const int32_t* rows;  // packed row -> row (lse is stored by row)
   const Ctl* ctl;
 };
 
@@ -452,22 +464,29 @@ __device__ __forceinline__ void store1(float* p, float a) { *p = a; }
 constexpr int kStagePitch = 264;   // bf16 elements per staged row (256 + 8)
 static_assert(256 * kStagePitch * 2 <= tile::kLdsBytes, "staged G tile exceeds LDS");
 
+// G tile held as bf16 pairs -> G [n, ldg] and G^T [gcols, ldt] through LDS
+// (free again once gemm_tile returns): the tile is staged once per
+// orientation with rows padded to 528 bytes, then every row leaves as 32
+// coalesced 16-byte stores.  gp[nb][mb][2q + h] holds tile rows
+// vw + mb*32 + 8q + 2h and the next one, for token column nb.
 template <typename T>
-__device__ __forceinline__ void store_g_staged(const GArgs<T>& a, const f32x16 (&acc)[4][4],
+__device__ __forceinline__ void store_g_staged(const GArgs<T>& a, const uint32_t (&gp)[4][4][8],
                                                char* lds, int64_t n0, int64_t vl0, int vw, int wn,
                                                int lane, int tid, int64_t nv) {
   uint16_t* sm = reinterpret_cast<uint16_t*>(lds);
   const int tcol = wn * 128 + (lane & 31);        // tile-local token of (nb = 0)
-  // G^T: staged row = vocabulary, 256 tokens per row
+  // G^T: staged row = vocabulary, 256 tokens per row; the two halves of a
+  // pair go to consecutive rows
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
-        sm[vl * kStagePitch + tcol + nb * 32] =
-            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[mb][nb][r]));
+      for (int i = 0; i < 8; ++i) {
+        const int vl = vw + mb * 32 + 8 * (i >> 1) + 2 * (i & 1);
+        const uint32_t w = gp[nb][mb][i];
+        sm[vl * kStagePitch + tcol + nb * 32] = static_cast<uint16_t>(w);
+        sm[(vl + 1) * kStagePitch + tcol + nb * 32] = static_cast<uint16_t>(w >> 16);
       }
   __syncthreads();
   const int chunk = tid & 31, row0 = tid >> 5;
@@ -485,8 +504,8 @@ __device__ __forceinline__ void store_g_staged(const GArgs<T>& a, const f32x16 (
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        store4(sm + (tcol + nb * 32) * kStagePitch + vw + mb * 32 + 8 * q, acc[mb][nb][4 * q],
-               acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+        *reinterpret_cast<uint2*>(sm + (tcol + nb * 32) * kStagePitch + vw + mb * 32 + 8 * q) =
+            uint2{gp[nb][mb][2 * q], gp[nb][mb][2 * q + 1]};
   __syncthreads();
 #pragma unroll 4
   for (int i = 0; i < 32; ++i) {
@@ -522,6 +541,62 @@ __device__ __forceinline__ void store_g_direct(const GArgs<T>& a, const f32x16 (
   }
 }
 
+// One element of G from its logit before bias and softcap; is_t marks the
+// target column.
+template <bool kBias, bool kSoftcap, typename T>
+__device__ __forceinline__ float g_elem(const GArgs<T>& a, float z, float bv, float lse2, float zfac,
+                                        bool is_t) {
+  if (kBias) z += bv;
+  float dz = 1.0f;
+  if (kSoftcap) {
+    const float th = fast_tanh(z * a.inv_softcap);
+    z = a.softcap * th;
+    dz = 1.0f - th * th;
+  }
+  const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2));
+  const float sub = is_t ? a.eps_over_v + a.keep_target : a.eps_over_v;
+  float g = __builtin_fmaf(p, zfac, -sub);
+  if (kSoftcap) g *= dz;
+  return g;
+}
+
+// bf16 G of one tile, straight from the accumulators into bf16 pairs, then
+// staged out.  kEdge: the tile reaches past n_valid or past the slice, whose
+// entries are 0.
+template <typename T, bool kBias, bool kSoftcap, bool kEdge>
+__device__ __forceinline__ void g_tile_bf16(const GArgs<T>& a, const f32x16 (&acc)[4][4], char* lds,
+                                            int64_t n0, int64_t vl0, int vw, int wn, int lane, int tid,
+                                            int64_t nv, int vlim, const float (&lse2)[4],
+                                            const float (&zfac)[4], const int (&hit)[4],
+                                            const bool (&valid)[4]) {
+  uint32_t gp[4][4][8];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 2 * i;                                   // rows r, r + 1 of the 32 x 32 block
+      const int vl = vw + mb * 32 + 8 * (i >> 1) + 2 * (i & 1);
+      const bool in0 = !kEdge || vl < vlim, in1 = !kEdge || vl + 1 < vlim;
+      float bv0 = 0.f, bv1 = 0.f;
+      if (kBias) {
+        bv0 = in0 ? ld_elem(a.bias, a.v0 + vl0 + vl) : 0.f;
+        bv1 = in1 ? ld_elem(a.bias, a.v0 + vl0 + vl + 1) : 0.f;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        float g0 = g_elem<kBias, kSoftcap>(a, acc[mb][nb][r], bv0, lse2[nb], zfac[nb], mb * 16 + r == hit[nb]);
+        float g1 = g_elem<kBias, kSoftcap>(a, acc[mb][nb][r + 1], bv1, lse2[nb], zfac[nb],
+                                           mb * 16 + r + 1 == hit[nb]);
+        if (kEdge) {
+          g0 = (valid[nb] && in0) ? g0 : 0.f;
+          g1 = (valid[nb] && in1) ? g1 : 0.f;
+        }
+        gp[nb][mb][i] = pack_bf16x2(g0, g1);
+      }
+    }
+  store_g_staged(a, gp, lds, n0, vl0, vw, wn, lane, tid, nv);
+}
+
 // Recompute one 256 x 256 logits tile of the slice and turn it into
 // G = [p (1 + 2 s lse) - (1-eps) onehot - eps/V] (1 - (z/c)^2), p = exp(z - lse)
 // (page "Cutting LLM Memory by 84%", "Kernel Implementation", backward:
@@ -540,6 +615,18 @@ void k_bwd_g(GArgs<T> a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t n0 = nt * tile::kN, vl0 = st * tile::kM;
 
+  // Per-token inputs are requested before the mainloop, which hides their
+  // latency; rows past n_valid read row n_valid - 1 and are masked below.
+  int32_t tgt[4];
+  float lse_t[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
+    const int64_t j = tok < nv ? tok : nv - 1;
+    tgt[nb] = a.targets[j];
+    lse_t[nb] = a.lsep[j];
+  }
+
   const Operand<T> A{a.w + a.v0 * a.d, a.d, a.v - a.v0, a.d};
   const Operand<T> B{a.x, a.d, nv, a.d};       // packed valid rows
   f32x16 acc[4][4];
@@ -547,19 +634,17 @@ void k_bwd_g(GArgs<T> a) {
 
   const int vw = wm * 128 + 4 * (lane >> 5);              // tile-local v of (mb = 0, r = 0)
   const int vlim = a.slice_len - vl0 < tile::kM ? static_cast<int>(a.slice_len - vl0) : tile::kM;
-  // G replaces the logits in the accumulators; rows past the slice and
-  // ignored or missing tokens hold 0.  Per-token terms first, then one
-  // vocabulary row (and its bias) at a time across the four token blocks.
+  // Rows past the slice and missing tokens get 0.  Per-token terms first,
+  // then one vocabulary row (and its bias) at a time across the token blocks.
   float lse2[4], zfac[4];
   int hit[4];
   bool valid[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
-    const bool tin = tok < nv;
-    const int32_t t = tin ? a.targets[tok] : a.ignore_index;
-    valid[nb] = tin && t != a.ignore_index;
-    const float l = valid[nb] ? a.lse[a.rows[tok]] : 0.f;
+    const int32_t t = tgt[nb];
+    valid[nb] = tok < nv;          // packed rows all have a target
+    const float l = valid[nb] ? lse_t[nb] : 0.f;
     lse2[nb] = l * kLog2e;
     zfac[nb] = 1.0f + a.two_s * l;
     const int64_t rel64 = static_cast<int64_t>(t) - a.v0 - vl0 - vw;
@@ -567,33 +652,31 @@ void k_bwd_g(GArgs<T> a) {
                   ? static_cast<int>((rel64 >> 5) * 16 + ((rel64 >> 3) & 3) * 4 + (rel64 & 3))
                   : -1;
   }
+  if constexpr (sizeof(T) == 2) {
+    if (n0 + tile::kN <= nv && vlim == tile::kM)
+      g_tile_bf16<T, kBias, kSoftcap, false>(a, acc, lds, n0, vl0, vw, wn, lane, tid, nv, vlim, lse2,
+                                             zfac, hit, valid);
+    else
+      g_tile_bf16<T, kBias, kSoftcap, true>(a, acc, lds, n0, vl0, vw, wn, lane, tid, nv, vlim, lse2,
+                                            zfac, hit, valid);
+  } else {
+    // fp32: G replaces the logits in the accumulators, then leaves directly
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
-      const bool vin = vl < vlim;
-      const float bv = (kBias && vin) ? ld_elem(a.bias, a.v0 + vl0 + vl) : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
+        const bool vin = vl < vlim;
+        const float bv = (kBias && vin) ? ld_elem(a.bias, a.v0 + vl0 + vl) : 0.f;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        float z = acc[mb][nb][r] + bv;
-        float dz = 1.0f;
-        if (kSoftcap) {
-          const float th = fast_tanh(z * a.inv_softcap);
-          z = a.softcap * th;
-          dz = 1.0f - th * th;
+        for (int nb = 0; nb < 4; ++nb) {
+          const float g = g_elem<kBias, kSoftcap>(a, acc[mb][nb][r], bv, lse2[nb], zfac[nb],
+                                                  mb * 16 + r == hit[nb]);
+          acc[mb][nb][r] = (valid[nb] && vin) ? g : 0.f;
         }
-        const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2[nb]));
-        const float sub = (mb * 16 + r == hit[nb]) ? a.eps_over_v + a.keep_target : a.eps_over_v;
-        float g = __builtin_fmaf(p, zfac[nb], -sub);
-        if (kSoftcap) g *= dz;
-        acc[mb][nb][r] = (valid[nb] && vin) ? g : 0.f;
       }
-    }
-  if constexpr (sizeof(T) == 2)
-    store_g_staged(a, acc, lds, n0, vl0, vw, wn, lane, tid, nv);
-  else
     store_g_direct(a, acc, n0, vl0, vw, wn, lane, nv);
+  }
 }
 
 template <typename T>
