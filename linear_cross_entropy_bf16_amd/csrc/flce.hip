@@ -103,8 +103,8 @@ Layout make_layout(const flce_params& p) {
   L.xt = off;          off = round_up(off + L.elem * p.d * L.ldt, kAlign);
   L.wt = off;          off = round_up(off + L.elem * p.d * L.ldg, kAlign);
   const bool multi_slice = L.slice < p.v;
-  L.dx_acc = off;
-  if (multi_slice) off = round_up(off + 4 * p.n * p.d, kAlign);   // by packed row
+  L.dx_acc = off;   // one fp32 256 x 256 block per (token tile, d tile), in accumulator order
+  if (multi_slice) off = round_up(off + 4 * round_up(p.n, tile::kN) * round_up(p.d, tile::kM), kAlign);
   L.lsep = off;        off = round_up(off + 4 * p.n, kAlign);
   L.bwd_end = off;
   return L;
@@ -375,9 +375,8 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
     wa.dw = dw;
     wa.d_tiles = d_tiles;
     wa.s_tiles = s_tiles;
-    wa.grid = grid8(d_tiles * s_tiles);
-    hipLaunchKernelGGL((flce::k_dw<T>), dim3(static_cast<unsigned>(wa.grid)), dim3(tile::kThreads), 0,
-                       s, wa);
+    hipLaunchKernelGGL((flce::k_dw<T>), dim3(static_cast<unsigned>(grid8(d_tiles * s_tiles))),
+                       dim3(tile::kThreads), 0, s, wa);
     if (p.n > 0) {
       flce::DxArgs<T> xa{};
       xa.wt = wt;

@@ -282,6 +282,25 @@ __device__ __forceinline__ void interleave() {
 
 }  // namespace dma
 
+// First four slabs of a tile's stream (A0 B0 A1 B1 into slots 0..3).  Issued
+// by gemm_tile_dma itself, or ahead of it (kPrefetched) while the previous
+// tile's epilogue runs; either way the ring must be idle (no loads in flight,
+// no reads pending), which the end of gemm_tile_dma guarantees.
+__device__ __forceinline__ void gemm_prologue_dma(const Operand<uint16_t>& A,
+                                                  const Operand<uint16_t>& B, int64_t m0,
+                                                  int64_t n0, char* lds) {
+  using namespace dma;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const SlabStream sa = slab_stream(A, m0, wave, lane), sb = slab_stream(B, n0, wave, lane);
+  issue_slab(sa, 0, lds, wave);
+  issue_slab(sb, 0, lds + kOpBytes, wave);
+  issue_slab(sa, kBK, lds + 2 * kOpBytes, wave);
+  issue_slab(sb, kBK, lds + 3 * kOpBytes, wave);
+}
+
+template <bool kPrefetched = false>
 __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
                                               const Operand<uint16_t>& B, int64_t m0,
                                               int64_t n0, int64_t K, char* lds,
@@ -320,11 +339,11 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
 
   // Slabs past the end of K are all out of range and land as zeros.
   const SlabStream sa = slab_stream(A, m0, wave, lane), sb = slab_stream(B, n0, wave, lane);
-  issue_slab(sa, 0, slot(0), wave);
-  issue_slab(sb, 0, slot(1), wave);
-  issue_slab(sa, kBK, slot(2), wave);
-  issue_slab(sb, kBK, slot(3), wave);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 15));   // A0, B0 landed
+  if constexpr (!kPrefetched) gemm_prologue_dma(A, B, m0, n0, lds);
+  // A0, B0 landed: the first 16 of this wave's loads since the ring went idle
+  // (loads complete in issue order; any stores issued in between only make the
+  // count stricter)
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 15));
   __builtin_amdgcn_s_barrier();
   u32x4 a0[4], b0[4], a1[4], b1[4];
   load_frags(a0, b0, 0, 0);
@@ -355,13 +374,25 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
 
 // One 256 x 256 output tile at (m0, n0), K = [0, K).  All 256 threads must
 // call it; it ends with a barrier, so `lds` is free again on return.
-template <typename T>
+// kPrefetched (bf16 only): gemm_prefetch has already issued this tile's first
+// slabs.
+template <typename T, bool kPrefetched = false>
 __device__ __forceinline__ void gemm_tile(const Operand<T>& A, const Operand<T>& B, int64_t m0,
                                           int64_t n0, int64_t K, char* lds, f32x16 (&acc)[4][4]) {
   if constexpr (sizeof(T) == 2)
-    gemm_tile_dma(A, B, m0, n0, K, lds, acc);
+    gemm_tile_dma<kPrefetched>(A, B, m0, n0, K, lds, acc);
   else
     gemm_tile_regs<T>(A, B, m0, n0, K, lds, acc);
+}
+
+// Start the slab stream of the next tile while the caller still works on the
+// previous one in registers (bf16; a no-op for fp32, whose mainloop starts its
+// own stream).  Only after gemm_tile has returned, and the caller must not
+// touch `lds` until the matching gemm_tile<T, true> call.
+template <typename T>
+__device__ __forceinline__ void gemm_prefetch(const Operand<T>& A, const Operand<T>& B, int64_t m0,
+                                              int64_t n0, char* lds) {
+  if constexpr (sizeof(T) == 2) gemm_prologue_dma(A, B, m0, n0, lds);
 }
 
 // ---------------------------------------------------------------- tile order

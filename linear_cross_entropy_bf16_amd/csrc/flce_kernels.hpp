@@ -11,7 +11,7 @@
 //   k_bwd_g       recomputed logits of one vocabulary slice -> G slice, in
 //                 both orientations
 //   k_dw          dW[slice] = scale G_slice^T X   (K = N, written once)
-//   k_dx          dX (+)= scale G_slice W_slice   (K = slice width)
+//   k_dx          dX (+)= G_slice W_slice, scaled at the last slice (K = slice width)
 //   k_db          db[slice] = scale sum_n G_slice
 //
 // Every reduction has a fixed order and no kernel uses global atomics, so
@@ -193,13 +193,18 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
                                                   const int32_t (&tgt)[4], int64_t n0, int wn,
                                                   int lane, float (&m_run)[4], float (&d_run)[4],
                                                   float (&s_run)[4]) {
+  // 32-bit throughout: targets and vocabulary offsets are below 2^31
+  const int v0i = static_cast<int>(v0);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    const int64_t rel64 = static_cast<int64_t>(tgt[nb]) - v0 - vw;
-    const bool hit_col = rel64 >= 0 && rel64 < 128 && (rel64 & 4) == 0;
-    const int rel = hit_col ? static_cast<int>(rel64) : -1;
+    const int rel32 = tgt[nb] - v0i - vw;
+    const bool hit_col = rel32 >= 0 && rel32 < 128 && (rel32 & 4) == 0;
+    const int rel = hit_col ? rel32 : -1;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
+      // one 32 x 32 block at a time: keeps the 16 logits of a block, not the
+      // whole tile, in VGPRs
+      __builtin_amdgcn_sched_barrier(0);
       float z[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -278,10 +283,14 @@ void k_fwd(FwdArgs<T> a) {
   const int64_t vt_first = a.vt_base + ch * a.tiles_per_chunk;
   const int64_t vt_end = vt_first + a.tiles_per_chunk < a.vt_end ? vt_first + a.tiles_per_chunk
                                                                  : a.vt_end;
+  // The slab stream of the next vocabulary tile starts before this tile's
+  // epilogue, which works in registers only, so its load latency is hidden.
+  if (vt_first < vt_end) gemm_prefetch(A, B, vt_first * tile::kM, n0, lds);
   for (int64_t vt = vt_first; vt < vt_end; ++vt) {
     const int64_t v0 = vt * tile::kM;
     f32x16 acc[4][4];
-    gemm_tile(A, B, v0, n0, a.d, lds, acc);
+    gemm_tile<T, true>(A, B, v0, n0, a.d, lds, acc);
+    if (vt + 1 < vt_end) gemm_prefetch(A, B, v0 + tile::kM, n0, lds);
     // tile-local vocabulary row of (mb, r) = vw + mb*32 + 8(r/4) + r%4
     const int vw = wm * 128 + 4 * (lane >> 5);
     const int vlim = a.v - v0 < tile::kM ? static_cast<int>(a.v - v0) : tile::kM;
@@ -686,7 +695,7 @@ struct DwArgs {
   int64_t d, v0, slice_len, ldt, gcols;
   const Ctl* ctl;
   float* dw;            // [v, d]
-  int64_t d_tiles, s_tiles, grid;
+  int64_t d_tiles, s_tiles;
 };
 
 // dW[v0 + v, :] = scale sum_n G[n, v] X[n, :]: one dedicated contraction over
@@ -695,11 +704,7 @@ struct DwArgs {
 // and iterate over the batch).  Computed as C[d, v] so each lane stores four
 // consecutive d.
 template <typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_dw(DwArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
-  const int64_t L = xcd_logical(blockIdx.x, a.grid);
-  if (L >= a.d_tiles * a.s_tiles) return;
+__device__ __forceinline__ void dw_tile(const DwArgs<T>& a, int64_t L, char* lds) {
   int64_t dt, st;
   grouped(L, a.d_tiles, a.s_tiles, kGroup, dt, st);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -735,27 +740,26 @@ struct DxArgs {
   const T* g;           // [n, ldg]  packed rows
   int64_t n, d, kdim, ldg;
   const Ctl* ctl;
-  float* acc_buf;       // [n, d] fp32 running sum over slices, by packed row
+  float* acc_buf;       // running sum over slices, one 256 x 256 block per output tile (see k_dx)
   T* dx;                // [n, d]
   int32_t first;
   int64_t d_tiles;
   const int32_t* rows;  // packed row -> row
 };
 
-// dX (+)= scale G_slice W_slice, computed as C[d, n]; the running fp32 sum
-// over slices is read-modified-written row by row, and the last slice writes
-// dX in its own dtype.
+// dX (+)= G_slice W_slice, computed as C[d, n] tile by tile.  The running
+// fp32 sum over slices lives in the workspace in the accumulators' own
+// layout: output tile (token tile nt, d tile dt) owns 64 Ki floats at
+// ((nt * d_tiles + dt) * 4 + wave) * 16384, and register group i = (mb, nb, q)
+// of a wave is the 1 KiB at i * 256 floats, lane l's four values at 4 l.  Every
+// load and store of the sum is one contiguous 1 KiB wave access and no staging
+// is needed; only the last slice applies the gradient scale and writes dX rows.
 constexpr int kDxPitch = 260;   // fp32 per staged token row (256 + 4)
 static_assert(128 * kDxPitch * 4 <= tile::kLdsBytes, "staged dX half tile exceeds LDS");
 // kLast: the last slice, which scatters the finished rows to dX.
 template <typename T, bool kLast>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_dx(DxArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
-  const int64_t nv = a.ctl->n_valid;
-  const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;   // valid rows only
-  int64_t L;
-  if (!xcd_logical_n(blockIdx.x, a.d_tiles * n_tiles, L)) return;
+__device__ __forceinline__ void dx_tile(const DxArgs<T>& a, int64_t L, int64_t nv, int64_t n_tiles,
+                                        char* lds) {
   int64_t nt, dt;
   grouped(L, n_tiles, a.d_tiles, kGroup, nt, dt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -765,57 +769,105 @@ void k_dx(DxArgs<T> a) {
   f32x16 acc[4][4];
   gemm_tile(A, B, dt * tile::kM, nt * tile::kN, a.kdim, lds, acc);
 
-  // The tile goes through LDS (free again once gemm_tile returns) in two
-  // halves of 128 tokens, so the running sum is read-modified-written as whole
-  // 1 KiB rows of 256 fp32 instead of 32-byte pieces of 32 rows.
-  const float scale = a.ctl->scale;
-  float* sm = reinterpret_cast<float*>(lds);
-  const int64_t tok0 = nt * tile::kN, d0 = dt * tile::kM;
-  const int chunk = tid & 63, row0 = tid >> 6;
-  const bool cols_ok = d0 + 4 * chunk < a.d;          // d is a multiple of 8
+  float4* sum = reinterpret_cast<float4*>(a.acc_buf) +
+                ((nt * a.d_tiles + dt) * 4 + wave) * 4096 + lane;
+  if (!a.first) {
+    // previous slices' sum, 16 groups at a time
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    // this half's previous sums are requested first and land while the
-    // tile is being staged
-    float4 prev[32];
-    int32_t dst_row[kLast ? 32 : 1];   // the row of dX each packed row goes to
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int64_t tok = tok0 + h * 128 + row0 + 4 * i;
-      prev[i] = float4{0.f, 0.f, 0.f, 0.f};
-      if (!a.first && tok < nv && cols_ok)
-        prev[i] = *reinterpret_cast<const float4*>(a.acc_buf + tok * a.d + d0 + 4 * chunk);
-      if constexpr (kLast) dst_row[i] = tok < nv ? a.rows[tok] : 0;
-    }
-    if (wn == h) {
+    for (int mb = 0; mb < 4; ++mb) {
+      float4 prev[16];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int q = 0; q < 4; ++q) prev[nb * 4 + q] = sum[((mb * 4 + nb) * 4 + q) * 64];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int dl = wm * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
-            *reinterpret_cast<float4*>(sm + (nb * 32 + (lane & 31)) * kDxPitch + dl) =
-                float4{scale * acc[mb][nb][4 * q], scale * acc[mb][nb][4 * q + 1],
-                       scale * acc[mb][nb][4 * q + 2], scale * acc[mb][nb][4 * q + 3]};
-          }
-    }
-    __syncthreads();
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int row = row0 + 4 * i;
-      const int64_t tok = tok0 + h * 128 + row;
-      if (tok < nv && cols_ok) {
-        float4 v = *reinterpret_cast<const float4*>(sm + row * kDxPitch + 4 * chunk);
-        v.x += prev[i].x; v.y += prev[i].y; v.z += prev[i].z; v.w += prev[i].w;
-        if constexpr (kLast)
-          store4(a.dx + static_cast<int64_t>(dst_row[i]) * a.d + d0 + 4 * chunk, v.x, v.y, v.z, v.w);
-        else
-          *reinterpret_cast<float4*>(a.acc_buf + tok * a.d + d0 + 4 * chunk) = v;
-      }
+        for (int q = 0; q < 4; ++q) {
+          const float4 p = prev[nb * 4 + q];
+          acc[mb][nb][4 * q] += p.x;
+          acc[mb][nb][4 * q + 1] += p.y;
+          acc[mb][nb][4 * q + 2] += p.z;
+          acc[mb][nb][4 * q + 3] += p.w;
+        }
     }
-    __syncthreads();
   }
+  if constexpr (!kLast) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          sum[((mb * 4 + nb) * 4 + q) * 64] = float4{acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
+                                                     acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
+  } else {
+    // The finished tile goes through LDS (free again once gemm_tile returns)
+    // in two halves of 128 tokens, so each dX row leaves in whole 512-byte
+    // (bf16) pieces, scattered back to the row it was packed from.
+    const float scale = a.ctl->scale;
+    float* sm = reinterpret_cast<float*>(lds);
+    const int64_t tok0 = nt * tile::kN, d0 = dt * tile::kM;
+    const int chunk = tid & 63, row0 = tid >> 6;
+    const bool cols_ok = d0 + 4 * chunk < a.d;          // d is a multiple of 8
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int32_t dst_row[32];   // the row of dX each packed row goes to
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int64_t tok = tok0 + h * 128 + row0 + 4 * i;
+        dst_row[i] = tok < nv ? a.rows[tok] : 0;
+      }
+      if (wn == h) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int dl = wm * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
+              *reinterpret_cast<float4*>(sm + (nb * 32 + (lane & 31)) * kDxPitch + dl) =
+                  float4{scale * acc[mb][nb][4 * q], scale * acc[mb][nb][4 * q + 1],
+                         scale * acc[mb][nb][4 * q + 2], scale * acc[mb][nb][4 * q + 3]};
+            }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int row = row0 + 4 * i;
+        const int64_t tok = tok0 + h * 128 + row;
+        if (tok < nv && cols_ok) {
+          const float4 v = *reinterpret_cast<const float4*>(sm + row * kDxPitch + 4 * chunk);
+          store4(a.dx + static_cast<int64_t>(dst_row[i]) * a.d + d0 + 4 * chunk, v.x, v.y, v.z, v.w);
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Each XCD walks a contiguous range of dW tiles; all 16 x 32 tiles of a slice
+// at the headline shape run as two lock-step rounds whose concurrent tiles
+// share their K = N operand panels in L2 (interleaving them with dX tiles in
+// one launch desynchronised them and made the slice 1.8x slower).
+template <typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_dw(DwArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
+  int64_t L;
+  if (!xcd_logical_n(blockIdx.x, a.d_tiles * a.s_tiles, L)) return;
+  dw_tile(a, L, lds);
+}
+
+template <typename T, bool kLast>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_dx(DxArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
+  const int64_t nv = a.ctl->n_valid;
+  const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;   // valid rows only
+  int64_t L;
+  if (!xcd_logical_n(blockIdx.x, a.d_tiles * n_tiles, L)) return;
+  dx_tile<T, kLast>(a, L, nv, n_tiles, lds);
 }
 
 // db[v0 + v] = scale sum_n G^T[v, n]: one wave per vocabulary row, lanes
