@@ -277,3 +277,51 @@ def dw_blocks(x, w, bias, targets, opts: LossOptions, grad_output: float = 1.0,
     for v0 in range(0, v, vocab_block):
         v1 = min(v, v0 + vocab_block)
         yield v0, v1, g[:, v0:v1].T @ x
+
+
+# ------------------------------------------------- cross-entropy on logits
+
+def cross_entropy_on_logits(r, targets, opts: LossOptions, grad_output: float = 1.0,
+                            n_valid: Optional[int] = None, want_grad: bool = True,
+                            row_block: int = ROW_BLOCK) -> Result:
+    """The same loss on logits given directly (no linear layer): the forward
+    "sum-exp" and "mean-log" passes and the backward of the cross-entropy
+    kernels on materialised logits (page "Add efficient Cross-Entropy by cuda
+    kernel", TransformerEngine PR #995: Changes, and the review of the
+    backward kernel, where smoothing subtracts a uniform term).  ``r`` holds
+    the pre-softcap logits [N, V] (bf16 bit patterns or floats); the result's
+    ``dx`` field carries dL/dr = scale * G.  Same readings as the fused
+    problem; the smoothing eps is the PyTorch one (the Megatron form on that
+    page is eps' = eps V / (V - 1), see ``megatron_smoothing``).  Pinned:
+    equals ``forward_backward`` with X = r and W = identity, torch's
+    cross_entropy with autograd, finite differences, the Megatron form."""
+    r = to_f64(r)
+    targets = np.asarray(targets)
+    n, v = r.shape
+    check_targets(targets, v, opts)
+    valid = valid_rows(targets, opts)
+    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    scale = grad_scale(opts, nv, grad_output) if want_grad else 0.0
+    lse = np.zeros(n)
+    rl = np.zeros(n)
+    grad = np.zeros((n, v)) if want_grad else None
+    for r0 in range(0, n, row_block):
+        sl = slice(r0, min(n, r0 + row_block))
+        z = r[sl]
+        if opts.softcap > 0.0:
+            z = opts.softcap * np.tanh(z / opts.softcap)
+        l = log_sum_exp(z)
+        rl[sl] = row_losses(z, l, targets[sl], opts)
+        lse[sl] = np.where(valid[sl], l, 0.0)
+        if want_grad:
+            grad[sl] = grad_logits(z, l, targets[sl], opts) * scale
+    return Result(reduce_loss(rl, nv, opts), lse, rl, nv, dx=grad)
+
+
+def megatron_smoothing(eps: float, v: int) -> float:
+    """The smoothing factor of the Megatron cross-entropy that the
+    TransformerEngine kernels follow (review of the backward kernel there:
+    smoothing = label_smoothing * V / (V - 1)); with it the target keeps
+    1 - eps and every other class gets eps / (V - 1).  Under this module's
+    convention that is the target distribution of eps' = eps V / (V - 1)."""
+    return eps * v / (v - 1)

@@ -368,10 +368,108 @@ def pin_gaussian_lse_level(O):
     assert abs(r.lse.mean() - (math.log(v) + 0.5)) < 0.05
 
 
+# ------------------------------------------------- cross-entropy on logits
+
+def _logits_problem(n=30, v=47, seed=31, ignore=4, spread=1.5):
+    rng = np.random.default_rng(seed)
+    r = rng.standard_normal((n, v)) * spread
+    t = rng.integers(0, v, n).astype(np.int32)
+    if ignore:
+        t[rng.choice(n, ignore, replace=False)] = IGN
+    return r, t
+
+
+def pin_logits_identity_linear(O):
+    """Cross-entropy on given logits r is the fused problem with X = r and W =
+    the identity (logits X.W^T = r), whose dX = G.W is then dL/dr, for every
+    feature combination; the fused oracle is pinned independently above."""
+    r, t = _logits_problem()
+    eye = np.eye(r.shape[1])
+    for feats in FEATURE_SETS:
+        o = _opts(O, **feats)
+        a = O.cross_entropy_on_logits(r, t, o, grad_output=0.7)
+        b = O.forward_backward(r, eye, None, t, o, grad_output=0.7)
+        assert abs(a.loss - b.loss) <= 1e-13 * max(1.0, abs(b.loss)), feats
+        assert np.allclose(a.lse, b.lse, rtol=0, atol=1e-13), feats
+        assert np.allclose(a.row_loss, b.row_loss, rtol=0, atol=1e-13), feats
+        assert np.allclose(a.dx, b.dx, rtol=0, atol=1e-15), feats
+
+
+def pin_logits_torch(O):
+    """Without softcap and z-loss: torch's cross_entropy on the same logits
+    (mean over non-ignored rows, sum, none; label smoothing) and its autograd
+    gradient, float64 on the CPU."""
+    import torch
+    import torch.nn.functional as F
+
+    r, t = _logits_problem(n=33, v=61, seed=5)
+    for eps in (0.0, 0.15):
+        for red in ("mean", "sum", "none"):
+            o = _opts(O, label_smoothing=eps, reduction=red)
+            rt = torch.tensor(r, requires_grad=True)
+            lt = F.cross_entropy(rt, torch.tensor(t, dtype=torch.long), ignore_index=IGN,
+                                 label_smoothing=eps, reduction=red)
+            if red == "none":
+                a = O.cross_entropy_on_logits(r, t, o, want_grad=False)
+                assert np.allclose(a.loss, lt.detach().numpy(), rtol=0, atol=1e-13)
+                continue
+            lt.backward()
+            a = O.cross_entropy_on_logits(r, t, o)
+            assert abs(a.loss - lt.item()) <= 1e-13 * max(1.0, abs(lt.item()))
+            assert np.allclose(a.dx, rt.grad.numpy(), rtol=0, atol=1e-15)
+
+
+def pin_logits_finite_differences(O, directions=12, seed=8):
+    """Central differences of the loss along random directions of the logits
+    agree with dL/dr to 1e-7 of its norm, for every feature combination (the
+    softcap derivative and the z-loss term included)."""
+    rng = np.random.default_rng(seed)
+    r, t = _logits_problem(n=64, v=300, seed=seed, ignore=6)
+    h = 1e-5
+    for feats in FEATURE_SETS:
+        o = _opts(O, **feats)
+        a = O.cross_entropy_on_logits(r, t, o)
+        gn = np.linalg.norm(a.dx)
+        for _ in range(directions):
+            dv = rng.standard_normal(r.shape)
+            dv /= np.linalg.norm(dv)
+            fp = O.cross_entropy_on_logits(r + h * dv, t, o, want_grad=False).loss
+            fm = O.cross_entropy_on_logits(r - h * dv, t, o, want_grad=False).loss
+            fd = (fp - fm) / (2 * h)
+            an = float((a.dx * dv).sum())
+            assert abs(fd - an) <= 1e-7 * gn + 1e-12, (feats, fd, an, gn)
+
+
+def pin_megatron_smoothing(O):
+    """The Megatron form that the TransformerEngine cross-entropy kernels
+    follow, written out here from its own description: smoothing = eps V / (V-1),
+    loss = (1 - smoothing)(-log p_t) - smoothing mean_v log p_v and gradient
+    softmax - (1 - smoothing) onehot - smoothing / V.  It equals the oracle at
+    eps' = megatron_smoothing(eps, V); its target distribution keeps 1 - eps on
+    the target and eps / (V - 1) on every other class."""
+    r, t = _logits_problem(n=20, v=37, seed=9, ignore=0)
+    n, v = r.shape
+    for eps in (0.05, 0.3):
+        sm = eps * v / (v - 1)
+        assert abs(O.megatron_smoothing(eps, v) - sm) <= 1e-15
+        assert abs((1 - sm + sm / v) - (1 - eps)) <= 1e-15 and abs(sm / v - eps / (v - 1)) <= 1e-15
+        m = r.max(axis=1, keepdims=True)
+        logp = r - m - np.log(np.exp(r - m).sum(axis=1, keepdims=True))
+        rows = -(1 - sm) * logp[np.arange(n), t] - sm * logp.mean(axis=1)
+        grad = np.exp(logp)
+        grad[np.arange(n), t] -= 1 - sm
+        grad -= sm / v
+        a = O.cross_entropy_on_logits(r, t, _opts(O, label_smoothing=O.megatron_smoothing(eps, v),
+                                                  reduction="sum"))
+        assert np.allclose(a.row_loss, rows, rtol=0, atol=1e-13)
+        assert np.allclose(a.dx, grad, rtol=0, atol=1e-15)
+
+
 ALL_PINS = [
     pin_uniform_logits, pin_single_class, pin_two_classes, pin_gradient_row_sums,
     pin_shift_invariance, pin_batch_additivity, pin_vocab_permutation,
     pin_online_merge, pin_no_valid_rows, pin_softcap_limits,
     pin_torch_cross_entropy, pin_finite_differences, pin_brute_force,
-    pin_gaussian_lse_level,
+    pin_gaussian_lse_level, pin_logits_identity_linear, pin_logits_torch,
+    pin_logits_finite_differences, pin_megatron_smoothing,
 ]

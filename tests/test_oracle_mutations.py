@@ -131,9 +131,36 @@ def mut_transposed_dw(m):
     m.forward_backward = forward_backward
 
 
+def mut_logits_ignore_softcap(m):
+    orig = m.cross_entropy_on_logits
+
+    def cross_entropy_on_logits(r, targets, opts, *a, **k):
+        o2 = m.LossOptions(opts.ignore_index, opts.label_smoothing, opts.lse_square_scale, 0.0,
+                           opts.reduction)
+        return orig(r, targets, o2, *a, **k)            # softcap option dropped on this path
+    m.cross_entropy_on_logits = cross_entropy_on_logits
+
+
+def mut_logits_unscaled_grad(m):
+    orig = m.cross_entropy_on_logits
+
+    def cross_entropy_on_logits(r, targets, opts, grad_output=1.0, n_valid=None, want_grad=True,
+                                **k):
+        res = orig(r, targets, opts, grad_output, n_valid, want_grad, **k)
+        if want_grad and res.n_valid and opts.reduction == "mean":
+            res.dx = res.dx * res.n_valid                  # forgot the 1 / n_valid of the mean
+        return res
+    m.cross_entropy_on_logits = cross_entropy_on_logits
+
+
+def mut_megatron_plain_eps(m):
+    m.megatron_smoothing = lambda eps, v: eps               # forgot the V / (V - 1)
+
+
 MUTATIONS = [mut_drop_smoothing_sum, mut_zloss_grad_sign, mut_no_softcap_derivative,
              mut_target_off_by_one, mut_lse_missing_max, mut_mean_over_all_rows,
-             mut_online_no_rescale, mut_smoothing_over_v_minus_1, mut_transposed_dw]
+             mut_online_no_rescale, mut_smoothing_over_v_minus_1, mut_transposed_dw,
+             mut_logits_ignore_softcap, mut_logits_unscaled_grad, mut_megatron_plain_eps]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
