@@ -112,6 +112,8 @@ def main():
     import torch
     from linear_cross_entropy_bf16_amd import api, workloads as W
 
+    if args.workload in W.CE_WORKLOADS:
+        return bench_ce(args, W.CE_WORKLOADS[args.workload])
     wl = W.WORKLOADS[args.workload]
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a ROCm GPU")
@@ -251,6 +253,141 @@ def main():
             "traffic": traffic,
             "fwd_ms": round(fwd_ms, 3),
             "flops_per_launch": fwd_flops,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_ce(wl, inp, max_rows: int):
+    """The fp64 oracle on the first rows of a logits workload (full V)."""
+    from oracle import flce_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    rows = min(max_rows, wl.n)
+    o = O.LossOptions(wl.ignore_index, wl.label_smoothing, wl.lse_square_scale, wl.softcap,
+                      wl.reduction)
+    t0 = time.perf_counter()
+    O.cross_entropy_on_logits(inp["logits"][:rows], inp["targets"][:rows], o)
+    dt = time.perf_counter() - t0
+    return {"value": round(rows / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {rows} of {wl.n} rows of {wl.name} (full V={wl.v}, loss and "
+                      f"dL/dlogits), fp64 numpy, {dt:.1f} s"}
+
+
+def bench_ce(args, wl):
+    """Cross-entropy on given logits: one step is one flce_ce_fused_fwd_bwd
+    (row statistics, loss, dL/dlogits) over the whole synthetic batch, logits
+    resident in HBM.  HBM-bound: the roofline is bytes moved against 8 TB/s."""
+    import numpy as np
+    import torch
+    from linear_cross_entropy_bf16_amd import api, workloads as W
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU")
+    dev = torch.device("cuda:0")
+    log(f"generating {wl}")
+    inp = W.generate_logits(wl)
+    r = torch.from_numpy(inp["logits"])
+    if wl.dtype == "bf16":
+        r = r.view(torch.bfloat16)
+    r = r.to(dev)
+    t = torch.from_numpy(inp["targets"]).to(dev)
+    opts = dict(ignore_index=wl.ignore_index, label_smoothing=wl.label_smoothing,
+                lse_square_scale=wl.lse_square_scale, softcap=wl.softcap, reduction=wl.reduction)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_alloc = torch.cuda.memory_allocated(dev)
+    elem = r.element_size()
+    out = (torch.empty(1, dtype=torch.float32, device=dev),
+           torch.empty(wl.n, dtype=torch.float32, device=dev), torch.empty_like(r))
+    p = api._ce_params(r, **opts)
+    from linear_cross_entropy_bf16_amd import _lib
+    ws = torch.empty(_lib.ce_workspace_size(p), dtype=torch.uint8, device=dev)
+
+    def step():
+        return api.cross_entropy_fused_fwd_bwd(r, t, workspace=ws, out=out, **opts)
+
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(reps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    log(f"warmup {args.warmup}")
+    for _ in range(max(1, args.warmup)):
+        step()
+    log(f"timing {args.steps} steps")
+    wall0 = time.perf_counter()
+    ms = timed(step, args.steps)
+    wall = time.perf_counter() - wall0
+    peak_bytes = torch.cuda.max_memory_allocated(dev)
+    loss = float(out[0].item())
+    log(f"{ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), loss {loss:.6f}")
+
+    # forward alone (flce_ce_forward): reads the valid rows once
+    lse = torch.empty(wl.n, dtype=torch.float32, device=dev)
+    loss1 = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def fwd():
+        st = _lib.ce_forward(p, r.data_ptr(), t.data_ptr(), loss1.data_ptr(), lse.data_ptr(), None,
+                             ws.data_ptr(), ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise _lib.FLCEError(st, "flce_ce_forward")
+
+    fwd()
+    fwd_ms = timed(fwd, max(3, args.steps))
+
+    n_valid = int((inp["targets"] != wl.ignore_index).sum())
+    # must-move bytes: the valid rows read once, the gradient written once
+    # (ignored rows are written as zeros, never read)
+    step_bytes = (n_valid + wl.n) * wl.v * elem
+    fwd_bytes = n_valid * wl.v * elem
+    cpu = cpu_baseline_ce(wl, inp, args.cpu_rows // 8) if args.cpu_rows > 0 else None
+    tokens_per_s = wl.n / (ms * 1e-3)
+    achieved = step_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": f"CE on given logits fwd+bwd tokens/sec at N={wl.n} V={wl.v} ({wl.dtype} logits)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n": wl.n, "v": wl.v, "targets": wl.targets,
+                   "ignore_frac": wl.ignore_frac, "reduction": wl.reduction,
+                   "label_smoothing": wl.label_smoothing, "lse_square_scale": wl.lse_square_scale,
+                   "softcap": wl.softcap, "parallelism": "single GPU"},
+        "n_valid": n_valid,
+        "peak_hbm_bytes": int(peak_bytes),
+        "peak_hbm_bytes_above_inputs": int(peak_bytes - base_alloc),
+        "workspace_bytes": int(ws.numel()),
+        "loss": loss,
+        "roofline": {
+            "kernel": "k_ce_fused (row statistics + dL/dlogits, one workgroup per row)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": step_bytes,
+            "fwd_ms": round(fwd_ms, 4),
+            "fwd_gbs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
         },
         "cpu_baseline": cpu,
     }

@@ -141,6 +141,58 @@ flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const v
                                float* lse, void* dx, float* dw, float* dbias, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Cross-entropy on logits given directly (no linear layer): the workload of
+ * the cross-entropy kernels of the page "Add efficient Cross-Entropy by cuda
+ * kernel" (TransformerEngine PR #995, Changes: a forward that reduces each row
+ * to its maximum and sum of exponentials, and a backward that writes the
+ * softmax minus the one-hot target, less a uniform smoothing term), with the
+ * option set and definitions above applied to r = logits:
+ *
+ *   z = c tanh(r / c) (softcap c > 0) or r;  lse, row_n and loss as above;
+ *   dL/dr = scale [softmax(z)(1 + 2 s lse) - (1-eps) onehot - eps/V] (1 - (z/c)^2)
+ *
+ * eps is the PyTorch smoothing; the Megatron form that page's kernels follow
+ * (smoothing = eps_M V / (V - 1), i.e. 1 - eps_M on the target and
+ * eps_M / (V - 1) on every other class) is eps = eps_M V / (V - 1) here.
+ * params->d and params->vocab_slice are ignored.  The logits are [n, v]
+ * row-major in params->dtype, element-aligned; V is arbitrary (a row that does
+ * not start on 16 bytes is read as an unaligned head, 16-byte vectors and an
+ * unaligned tail).  Streaming kernels, one workgroup per row: the forward
+ * reads the logits once; the backward reads them once and writes dL/dr once.
+ * Rows whose target is ignore_index are not read; their gradient rows are 0.
+ * Targets are range-checked on the device (flce_check_status); an
+ * out-of-range target never causes an out-of-bounds access.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes of the flce_ce_* calls: O(N) (status word, row map, per-row
+ * losses, block sums).  0 for invalid parameters. */
+size_t flce_ce_workspace_size(const flce_params* params);
+
+/* Forward on logits.  loss, lse and row_loss as for flce_forward. */
+flce_status flce_ce_forward(const flce_params* params, const void* logits,
+                            const int32_t* targets, float* loss, float* lse,
+                            float* row_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward on logits from the saved lse.
+ *  grad_output  fp32 [1] device scalar, or NULL for 1.0
+ *  dlogits      [n, v] dtype, overwritten with dL/dr; may be `logits` itself
+ *               (in place), else it must be misaligned to 16 bytes exactly as
+ *               much as `logits` (both 16-byte aligned is the usual case)
+ * reduction NONE returns FLCE_ERR_UNSUPPORTED. */
+flce_status flce_ce_backward(const flce_params* params, const void* logits,
+                             const int32_t* targets, const float* lse,
+                             const float* grad_output, void* dlogits, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* Forward and backward in one pass per row with grad_output = 1.0: each row
+ * is reduced to its lse, then its gradient is written (dlogits may be
+ * `logits`, as for flce_ce_backward).  reduction NONE returns
+ * FLCE_ERR_UNSUPPORTED. */
+flce_status flce_ce_fused_fwd_bwd(const flce_params* params, const void* logits,
+                                  const int32_t* targets, float* loss, float* lse,
+                                  void* dlogits, void* ws, size_t ws_bytes, void* stream);
+
 /* Synchronises `stream`, then reports the device-side target check of the
  * last call that used this workspace: FLCE_OK or FLCE_ERR_TARGET_OUT_OF_RANGE
  * (FLCE_ERR_DEVICE if the synchronisation or copy fails).  When it reports an

@@ -23,6 +23,7 @@ DTYPE_F32 = 1
 REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_fused_fwd_bwd",
+           "flce_ce_workspace_size", "flce_ce_forward", "flce_ce_backward", "flce_ce_fused_fwd_bwd",
            "flce_check_status", "flce_status_string", "flce_version")
 
 
@@ -69,6 +70,14 @@ def load():
     lib.flce_backward.restype = ctypes.c_int
     lib.flce_fused_fwd_bwd.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.flce_fused_fwd_bwd.restype = ctypes.c_int
+    lib.flce_ce_workspace_size.argtypes = [pp]
+    lib.flce_ce_workspace_size.restype = ctypes.c_size_t
+    lib.flce_ce_forward.argtypes = [pp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.flce_ce_forward.restype = ctypes.c_int
+    lib.flce_ce_backward.argtypes = [pp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.flce_ce_backward.restype = ctypes.c_int
+    lib.flce_ce_fused_fwd_bwd.argtypes = [pp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.flce_ce_fused_fwd_bwd.restype = ctypes.c_int
     lib.flce_check_status.argtypes = [_P, _P]
     lib.flce_check_status.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
@@ -114,6 +123,25 @@ def backward(params, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, w
 def fused_fwd_bwd(params, x, w, bias, targets, loss, lse, dx, dw, dbias, ws, ws_bytes, stream) -> int:
     return load().flce_fused_fwd_bwd(ctypes.byref(params), x, w, bias, targets, loss, lse, dx, dw,
                                      dbias, ws, ws_bytes, stream)
+
+
+def ce_workspace_size(params: Params) -> int:
+    return int(load().flce_ce_workspace_size(ctypes.byref(params)))
+
+
+def ce_forward(params, logits, targets, loss, lse, row_loss, ws, ws_bytes, stream) -> int:
+    return load().flce_ce_forward(ctypes.byref(params), logits, targets, loss, lse, row_loss, ws,
+                                  ws_bytes, stream)
+
+
+def ce_backward(params, logits, targets, lse, grad_output, dlogits, ws, ws_bytes, stream) -> int:
+    return load().flce_ce_backward(ctypes.byref(params), logits, targets, lse, grad_output, dlogits,
+                                   ws, ws_bytes, stream)
+
+
+def ce_fused_fwd_bwd(params, logits, targets, loss, lse, dlogits, ws, ws_bytes, stream) -> int:
+    return load().flce_ce_fused_fwd_bwd(ctypes.byref(params), logits, targets, loss, lse, dlogits, ws,
+                                        ws_bytes, stream)
 
 
 def check_status(ws, stream) -> int:

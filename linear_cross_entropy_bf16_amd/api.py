@@ -192,3 +192,134 @@ def linear_cross_entropy(x, weight, target, bias=None, ignore_index=-100, label_
     and bias (reduction 'mean' or 'sum'; 'none' is forward-only)."""
     return LinearCrossEntropyFunction.apply(x, weight, target, bias, ignore_index, label_smoothing,
                                             lse_square_scale, softcap, reduction)
+
+
+# ------------------------------------------------- cross-entropy on logits
+
+def _prepare_logits(logits, target):
+    if not isinstance(logits, torch.Tensor) or logits.device.type != "cuda":
+        raise ValueError("logits must be a tensor on a ROCm GPU (device 'cuda')")
+    if logits.dtype not in _DTYPES:
+        raise TypeError(f"logits must be bfloat16 or float32, got {logits.dtype}")
+    if target.device != logits.device:
+        raise ValueError(f"target is on {target.device}, logits on {logits.device}")
+    v = logits.shape[-1]
+    r2 = logits.reshape(-1, v).contiguous()
+    if r2.data_ptr() % 16:
+        r2 = r2.clone()                      # a fresh allocation is 16-byte aligned
+    t2 = target.reshape(-1)
+    if t2.numel() != r2.shape[0]:
+        raise ValueError("target must have one entry per row of logits")
+    return r2, t2.to(torch.int32).contiguous()
+
+
+def _ce_params(r2, ignore_index, label_smoothing, lse_square_scale, softcap, reduction):
+    n, v = r2.shape
+    return make_params(n, 8, v, r2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
+                       reduction)
+
+
+def _ce_workspace(p, device):
+    nbytes = _lib.ce_workspace_size(p)
+    if nbytes == 0:
+        raise _lib.FLCEError(_lib.FLCE_ERR_INVALID_ARGUMENT, "workspace size")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def cross_entropy_forward(logits, target, *, ignore_index=-100, label_smoothing=0.0,
+                          lse_square_scale=0.0, softcap=0.0, reduction="mean", check_targets=False):
+    """Cross-entropy on given logits [..., V]: returns (loss, lse, row_loss)
+    like ``forward``."""
+    r2, t2 = _prepare_logits(logits, target)
+    p = _ce_params(r2, ignore_index, label_smoothing, lse_square_scale, softcap, reduction)
+    n = r2.shape[0]
+    dev = r2.device
+    ws, nbytes = _ce_workspace(p, dev)
+    loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(n, dtype=torch.float32, device=dev)
+    st = _stream(dev)
+    _check(_lib.ce_forward(p, _ptr(r2), _ptr(t2), _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(ws),
+                           nbytes, st), "flce_ce_forward")
+    if check_targets:
+        _check(_lib.check_status(_ptr(ws), st), "target check")
+    return (loss if reduction == "none" else loss[0]), lse, row_loss
+
+
+def cross_entropy_backward(logits, target, lse, grad_output=None, *, ignore_index=-100,
+                           label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0,
+                           reduction="mean", inplace=False):
+    """dL/dlogits in the logits' dtype and shape; ``inplace`` overwrites the
+    logits (when they are already a contiguous, 16-byte aligned tensor)."""
+    r2, t2 = _prepare_logits(logits, target)
+    p = _ce_params(r2, ignore_index, label_smoothing, lse_square_scale, softcap, reduction)
+    dev = r2.device
+    ws, nbytes = _ce_workspace(p, dev)
+    g = None
+    if grad_output is not None:
+        g = grad_output.detach().reshape(1).to(device=dev, dtype=torch.float32).contiguous()
+    lse = lse.detach().to(torch.float32).contiguous()
+    out = r2 if inplace else torch.empty_like(r2)
+    _check(_lib.ce_backward(p, _ptr(r2), _ptr(t2), _ptr(lse), _ptr(g), _ptr(out), _ptr(ws), nbytes,
+                            _stream(dev)), "flce_ce_backward")
+    return out.reshape(logits.shape)
+
+
+def cross_entropy_fused_fwd_bwd(logits, target, *, ignore_index=-100, label_smoothing=0.0,
+                                lse_square_scale=0.0, softcap=0.0, reduction="mean", inplace=False,
+                                workspace: Optional[torch.Tensor] = None, out=None):
+    """(loss, lse, dlogits) in one pass per row, grad_output = 1.  ``out`` is
+    an optional (loss [1], lse [N], dlogits) tuple to reuse."""
+    r2, t2 = _prepare_logits(logits, target)
+    p = _ce_params(r2, ignore_index, label_smoothing, lse_square_scale, softcap, reduction)
+    n = r2.shape[0]
+    dev = r2.device
+    nbytes = _lib.ce_workspace_size(p)
+    if workspace is None:
+        workspace, nbytes = _ce_workspace(p, dev)
+    elif workspace.numel() < nbytes:
+        raise _lib.FLCEError(_lib.FLCE_ERR_WORKSPACE_TOO_SMALL, "cross_entropy_fused_fwd_bwd")
+    else:
+        nbytes = workspace.numel()
+    if out is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lse = torch.empty(n, dtype=torch.float32, device=dev)
+        grad = r2 if inplace else torch.empty_like(r2)
+    else:
+        loss, lse, grad = out
+    _check(_lib.ce_fused_fwd_bwd(p, _ptr(r2), _ptr(t2), _ptr(loss), _ptr(lse), _ptr(grad),
+                                 _ptr(workspace), nbytes, _stream(dev)), "flce_ce_fused_fwd_bwd")
+    return loss[0], lse, grad.reshape(logits.shape)
+
+
+class CrossEntropyFunction(torch.autograd.Function):
+    """Autograd wrapper of the logits path: keeps only the per-row LSE."""
+
+    @staticmethod
+    def forward(ctx, logits, target, ignore_index, label_smoothing, lse_square_scale, softcap,
+                reduction):
+        loss, lse, _ = cross_entropy_forward(logits, target, ignore_index=ignore_index,
+                                             label_smoothing=label_smoothing,
+                                             lse_square_scale=lse_square_scale, softcap=softcap,
+                                             reduction=reduction)
+        ctx.save_for_backward(logits, target, lse)
+        ctx.opts = dict(ignore_index=ignore_index, label_smoothing=label_smoothing,
+                        lse_square_scale=lse_square_scale, softcap=softcap, reduction=reduction)
+        ctx.mark_non_differentiable(lse)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        logits, target, lse = ctx.saved_tensors
+        if ctx.opts["reduction"] == "none":
+            raise RuntimeError("reduction='none' is forward-only; use 'mean' or 'sum'")
+        g = cross_entropy_backward(logits, target, lse, grad_output=grad_loss, **ctx.opts)
+        return g, None, None, None, None, None, None
+
+
+def cross_entropy(logits, target, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0,
+                  softcap=0.0, reduction="mean"):
+    """Cross-entropy of given logits [..., V]; differentiable in the logits
+    (reduction 'mean' or 'sum'; 'none' is forward-only)."""
+    return CrossEntropyFunction.apply(logits, target, ignore_index, label_smoothing,
+                                      lse_square_scale, softcap, reduction)

@@ -13,6 +13,7 @@
 
 #include "flce.h"
 #include "flce_kernels.hpp"
+#include "flce_ce.hpp"
 
 namespace {
 
@@ -411,6 +412,144 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
   return launched();
 }
 
+// ------------------------------------------------- cross-entropy on logits
+struct CeLayout {
+  int64_t elem;
+  int64_t ctl, rows, row_loss, block_sums, end;
+  int64_t n_blocks;
+};
+
+CeLayout make_ce_layout(const flce_params& p) {
+  CeLayout L{};
+  L.elem = p.dtype == FLCE_DTYPE_BF16 ? 2 : 4;
+  L.n_blocks = cdiv(p.n, 256);
+  int64_t off = 0;
+  L.ctl = off;         off += kAlign;
+  L.rows = off;        off = round_up(off + 4 * p.n, kAlign);
+  L.row_loss = off;    off = round_up(off + 4 * p.n, kAlign);
+  L.block_sums = off;  off = round_up(off + 8 * L.n_blocks, kAlign);
+  L.end = off;
+  return L;
+}
+
+// flce_params without the hidden size: d and vocab_slice are ignored.
+flce_status check_ce_params(const flce_params* p) {
+  if (!p) return FLCE_ERR_INVALID_ARGUMENT;
+  flce_params q = *p;
+  q.d = 8;
+  q.vocab_slice = 0;
+  const flce_status st = check_params(&q);
+  if (st != FLCE_OK) return st;
+  if (static_cast<double>(p->n) * static_cast<double>(p->v) > 1e17) return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+// logits and the gradient: element-aligned, and equally misaligned to 16
+// bytes so both split every row the same way
+flce_status check_ce_ptrs(const flce_params& p, const void* logits, const int32_t* targets,
+                          const void* grad) {
+  const uintptr_t e = p.dtype == FLCE_DTYPE_BF16 ? 2 : 4;
+  if (p.n == 0) return FLCE_OK;
+  if (!logits || !aligned(logits, e) || !targets || !aligned(targets, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (grad && (!aligned(grad, e) || ((reinterpret_cast<uintptr_t>(grad) -
+                                      reinterpret_cast<uintptr_t>(logits)) & 15u) != 0))
+    return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+template <typename T>
+flce::CeArgs<T> ce_args(const flce_params& p, const CeLayout& L, const void* logits,
+                        const int32_t* targets, void* ws) {
+  flce::CeArgs<T> a{};
+  a.logits = static_cast<const T*>(logits);
+  a.targets = targets;
+  a.n = p.n;
+  a.v = p.v;
+  a.ignore_index = p.ignore_index;
+  a.softcap = p.softcap;
+  a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
+  a.keep_target = 1.0f - p.label_smoothing;
+  a.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
+  a.zloss = p.lse_square_scale;
+  a.two_s = 2.0f * p.lse_square_scale;
+  a.ctl = reinterpret_cast<const Ctl*>(at(ws, L.ctl));
+  a.row_loss_ws = reinterpret_cast<float*>(at(ws, L.row_loss));
+  return a;
+}
+
+void ce_prep(const flce_params& p, const CeLayout& L, const int32_t* targets,
+             const float* grad_output, void* ws, hipStream_t s) {
+  hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
+                     grad_output, p.reduction == FLCE_REDUCTION_MEAN ? 1 : 0,
+                     reinterpret_cast<Ctl*>(at(ws, L.ctl)), reinterpret_cast<int32_t*>(at(ws, L.rows)));
+}
+
+void ce_reduce(const flce_params& p, const CeLayout& L, float* loss, void* ws, hipStream_t s) {
+  if (p.reduction == FLCE_REDUCTION_NONE) return;
+  double* sums = reinterpret_cast<double*>(at(ws, L.block_sums));
+  if (L.n_blocks > 0)
+    hipLaunchKernelGGL(flce::k_ce_block_sums, dim3(static_cast<unsigned>(L.n_blocks)), dim3(256), 0, s,
+                       static_cast<const float*>(reinterpret_cast<float*>(at(ws, L.row_loss))), p.n, sums);
+  hipLaunchKernelGGL(flce::k_loss_final, dim3(1), dim3(256), 0, s, static_cast<const double*>(sums),
+                     L.n_blocks, reinterpret_cast<const Ctl*>(at(ws, L.ctl)),
+                     p.reduction == FLCE_REDUCTION_MEAN ? 1 : 0, loss);
+}
+
+template <typename T, bool kSoftcap, bool kSumZ>
+void launch_ce_fwd(const flce::CeArgs<T>& a, hipStream_t s) {
+  hipLaunchKernelGGL((flce::k_ce_fwd<T, kSoftcap, kSumZ>), dim3(static_cast<unsigned>(a.n)), dim3(256), 0,
+                     s, a);
+}
+template <typename T, bool kSoftcap, bool kSumZ>
+void launch_ce_fused(const flce::CeArgs<T>& a, hipStream_t s) {
+  hipLaunchKernelGGL((flce::k_ce_fused<T, kSoftcap, kSumZ>), dim3(static_cast<unsigned>(a.n)), dim3(256),
+                     0, s, a);
+}
+
+template <typename T>
+flce_status run_ce(const flce_params& p, const CeLayout& L, const void* logits, const int32_t* targets,
+                   float* loss, float* lse, float* row_loss, const float* lse_in,
+                   const float* grad_output, void* grad, void* ws, hipStream_t s, int mode) {
+  // mode 0: forward, 1: backward, 2: fused
+  ce_prep(p, L, targets, grad_output, ws, s);
+  flce::CeArgs<T> a = ce_args<T>(p, L, logits, targets, ws);
+  a.lse = lse;
+  a.lse_in = lse_in;
+  a.row_loss = row_loss;
+  a.loss_rows = (mode == 0 && p.reduction == FLCE_REDUCTION_NONE) ? loss : nullptr;
+  a.grad = static_cast<T*>(grad);
+  const bool c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
+  if (p.n > 0) {
+    if (mode == 1) {
+      if (c)
+        hipLaunchKernelGGL((flce::k_ce_bwd<T, true>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((flce::k_ce_bwd<T, false>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s, a);
+      return launched();
+    }
+    const int key = (c ? 1 : 0) | (z ? 2 : 0);
+    if (mode == 0) {
+      switch (key) {
+        case 0: launch_ce_fwd<T, false, false>(a, s); break;
+        case 1: launch_ce_fwd<T, true, false>(a, s); break;
+        case 2: launch_ce_fwd<T, false, true>(a, s); break;
+        default: launch_ce_fwd<T, true, true>(a, s); break;
+      }
+    } else {
+      switch (key) {
+        case 0: launch_ce_fused<T, false, false>(a, s); break;
+        case 1: launch_ce_fused<T, true, false>(a, s); break;
+        case 2: launch_ce_fused<T, false, true>(a, s); break;
+        default: launch_ce_fused<T, true, true>(a, s); break;
+      }
+    }
+  } else if (mode == 1) {
+    return launched();
+  }
+  ce_reduce(p, L, loss, ws, s);
+  return launched();
+}
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -501,6 +640,71 @@ flce_status flce_check_status(const void* ws, void* stream) {
   Ctl host{};
   if (hipMemcpy(&host, ws, sizeof(Ctl), hipMemcpyDeviceToHost) != hipSuccess) return FLCE_ERR_DEVICE;
   return host.status ? FLCE_ERR_TARGET_OUT_OF_RANGE : FLCE_OK;
+}
+
+size_t flce_ce_workspace_size(const flce_params* params) {
+  if (check_ce_params(params) != FLCE_OK) return 0;
+  return static_cast<size_t>(make_ce_layout(*params).end);
+}
+
+flce_status flce_ce_forward(const flce_params* params, const void* logits, const int32_t* targets,
+                            float* loss, float* lse, float* row_loss, void* ws, size_t ws_bytes,
+                            void* stream) {
+  flce_status st = check_ce_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if ((st = check_ce_ptrs(p, logits, targets, nullptr)) != FLCE_OK) return st;
+  if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p.n > 0 && (!lse || !aligned(lse, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (row_loss && !aligned(row_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  const CeLayout L = make_ce_layout(p);
+  if ((st = check_ws(ws, ws_bytes, L.end)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16)
+    return run_ce<uint16_t>(p, L, logits, targets, loss, lse, row_loss, nullptr, nullptr, nullptr, ws, s, 0);
+  return run_ce<float>(p, L, logits, targets, loss, lse, row_loss, nullptr, nullptr, nullptr, ws, s, 0);
+}
+
+flce_status flce_ce_backward(const flce_params* params, const void* logits, const int32_t* targets,
+                             const float* lse, const float* grad_output, void* dlogits, void* ws,
+                             size_t ws_bytes, void* stream) {
+  flce_status st = check_ce_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if (p.reduction == FLCE_REDUCTION_NONE) return FLCE_ERR_UNSUPPORTED;
+  if (p.n > 0 && !dlogits) return FLCE_ERR_INVALID_ARGUMENT;
+  if ((st = check_ce_ptrs(p, logits, targets, dlogits)) != FLCE_OK) return st;
+  if (p.n > 0 && (!lse || !aligned(lse, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (grad_output && !aligned(grad_output, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  const CeLayout L = make_ce_layout(p);
+  if ((st = check_ws(ws, ws_bytes, L.end)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16)
+    return run_ce<uint16_t>(p, L, logits, targets, nullptr, nullptr, nullptr, lse, grad_output, dlogits, ws,
+                            s, 1);
+  return run_ce<float>(p, L, logits, targets, nullptr, nullptr, nullptr, lse, grad_output, dlogits, ws, s, 1);
+}
+
+flce_status flce_ce_fused_fwd_bwd(const flce_params* params, const void* logits, const int32_t* targets,
+                                  float* loss, float* lse, void* dlogits, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  flce_status st = check_ce_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if (p.reduction == FLCE_REDUCTION_NONE) return FLCE_ERR_UNSUPPORTED;
+  if (p.n > 0 && !dlogits) return FLCE_ERR_INVALID_ARGUMENT;
+  if ((st = check_ce_ptrs(p, logits, targets, dlogits)) != FLCE_OK) return st;
+  if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p.n > 0 && (!lse || !aligned(lse, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  const CeLayout L = make_ce_layout(p);
+  if ((st = check_ws(ws, ws_bytes, L.end)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16)
+    return run_ce<uint16_t>(p, L, logits, targets, loss, lse, nullptr, nullptr, nullptr, dlogits, ws, s, 2);
+  return run_ce<float>(p, L, logits, targets, loss, lse, nullptr, nullptr, nullptr, dlogits, ws, s, 2);
 }
 
 const char* flce_status_string(flce_status status) {

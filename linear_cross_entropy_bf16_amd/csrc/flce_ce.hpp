@@ -1,0 +1,347 @@
+// Cross-entropy on logits given directly, [N, V] row-major in bf16 or fp32:
+// the workload of the cross-entropy kernels of "Add efficient Cross-Entropy by
+// cuda kernel" (TransformerEngine PR #995, Changes: a forward that reduces each
+// row to its maximum and sum of exponentials, and a backward that writes
+// softmax - onehot with the smoothing term), with the option set of the fused
+// path (ignore_index, label smoothing, z-loss, softcap, mean / sum / none).
+//
+//   k_ce_fwd       one workgroup per row: online (max, sum-exp, sum-z) over the
+//                  row in 16-byte vectors, lse, row loss
+//   k_ce_bwd       one workgroup per row: dL/dr from the saved lse, written in
+//                  the logits' dtype (in place allowed)
+//   k_ce_fused     both in one kernel: the second pass re-reads the row the
+//                  first pass has just streamed
+//   k_ce_block_sums  fixed-order partial sums of the row losses
+//
+// Streaming and HBM-bound: each element is read once per pass and the
+// gradient written once; nothing is staged.  A row whose base address is not
+// 16-byte aligned (V * sizeof(T) not a multiple of 16) is split into a short
+// unaligned head, a vectorised body and a short tail, so any V works.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "flce_kernels.hpp"
+
+namespace flce {
+
+template <typename T>
+struct CeArgs {
+  const T* logits;          // [n, v] pre-softcap logits
+  const int32_t* targets;   // [n]
+  int64_t n, v;
+  int32_t ignore_index;
+  float softcap, inv_softcap;
+  float keep_target;        // 1 - eps
+  float eps_over_v;         // eps / V
+  float zloss;              // s
+  float two_s;              // 2 s
+  const Ctl* ctl;           // n_valid and the gradient scale (k_prep)
+  float* lse;               // [n] out (forward), 0 on ignored rows
+  const float* lse_in;      // [n] in (backward)
+  float* row_loss_ws;       // [n] per-row losses for the fixed-order reduction
+  float* row_loss;          // [n] or null: per-row losses for the caller
+  float* loss_rows;         // [n] or null: reduction 'none'
+  T* grad;                  // [n, v] dL/dr (may be `logits`)
+};
+
+// 16 bytes of a row as floats, and back (bf16 with round to nearest even).
+template <typename T> struct CeVec;
+template <> struct CeVec<uint16_t> {
+  static constexpr int n = 8;
+  static __device__ __forceinline__ void load(const uint16_t* p, float (&z)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[2 * i] = __uint_as_float(w[i] << 16);
+      z[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float (&g)[8]) {
+    *reinterpret_cast<uint4*>(p) = uint4{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
+                                         pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
+  }
+};
+template <> struct CeVec<float> {
+  static constexpr int n = 4;
+  static __device__ __forceinline__ void load(const float* p, float (&z)[4]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    z[0] = u.x; z[1] = u.y; z[2] = u.z; z[3] = u.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float (&g)[4]) {
+    *reinterpret_cast<float4*>(p) = float4{g[0], g[1], g[2], g[3]};
+  }
+};
+
+// Split of row r into [0, head) unaligned, [head, body_end) whole 16-byte
+// vectors, [body_end, v) unaligned (head and tail each shorter than a vector).
+template <typename T>
+struct RowSplit {
+  int64_t head, body_end;
+  int n_scalar;             // head + tail elements
+};
+template <typename T>
+__device__ __forceinline__ RowSplit<T> row_split(const T* row, int64_t v) {
+  constexpr int kVec = CeVec<T>::n;
+  const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
+  int64_t head = mis ? static_cast<int64_t>((16u - mis) / sizeof(T)) : 0;
+  head = head < v ? head : v;
+  const int64_t body_end = head + (v - head) / kVec * kVec;
+  return RowSplit<T>{head, body_end, static_cast<int>(head + (v - body_end))};
+}
+// element index of scalar slot i (0 <= i < n_scalar)
+template <typename T>
+__device__ __forceinline__ int64_t scalar_index(const RowSplit<T>& sp, int i) {
+  return i < sp.head ? i : sp.body_end + (i - sp.head);
+}
+
+__device__ __forceinline__ float softcapped(float r, float c, float inv_c, bool on) {
+  return on ? c * fast_tanh(r * inv_c) : r;
+}
+
+// Running row statistics of one thread: m = max z in log2 units, d = sum of
+// 2^(z log2e - m), s = sum z (online-softmax recurrence, page "Cutting LLM
+// Memory by 84%", "Definition and Forward Pass").
+struct RowStats {
+  float m, d, s;
+};
+
+template <int N, bool kSumZ>
+__device__ __forceinline__ void stats_add(RowStats& st, const float (&z)[N]) {
+  float mx = z[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) mx = fmax_fast(mx, z[i]);
+  if (kSumZ) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) st.s += z[i];
+  }
+  if (mx == -INFINITY) return;          // only masked (-inf) logits here
+  const float m_new = fmax_fast(st.m, mx * kLog2e);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) sum += fast_exp2(__builtin_fmaf(z[i], kLog2e, -m_new));
+  st.d = st.d * fast_exp2(st.m - m_new) + sum;   // st.m = -inf: the old sum is 0
+  st.m = m_new;
+}
+
+// Whole-workgroup merge of the per-thread statistics in a fixed order; every
+// thread gets the row's result.  `sm` holds 12 floats of LDS.
+__device__ __forceinline__ RowStats block_stats(RowStats st, float* sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(st.m, off), d2 = __shfl_xor(st.d, off), s2 = __shfl_xor(st.s, off);
+    lse_merge(st.m, st.d, m2, d2);
+    st.s += s2;
+  }
+  if (lane == 0) {
+    sm[wave] = st.m;
+    sm[4 + wave] = st.d;
+    sm[8 + wave] = st.s;
+  }
+  __syncthreads();
+  RowStats r{-INFINITY, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    lse_merge(r.m, r.d, sm[w], sm[4 + w]);
+    r.s += sm[8 + w];
+  }
+  return r;
+}
+
+// Statistics of row `row` (all 256 threads); returns the merged result.
+template <typename T, bool kSoftcap, bool kSumZ>
+__device__ __forceinline__ RowStats row_stats(const CeArgs<T>& a, const T* row, const RowSplit<T>& sp,
+                                              float* sm) {
+  constexpr int kVec = CeVec<T>::n;
+  constexpr int kUnroll = 4;
+  const int tid = threadIdx.x;
+  RowStats st{-INFINITY, 0.f, 0.f};
+  if (tid < sp.n_scalar) {
+    float z[1] = {softcapped(ld_elem(row, scalar_index(sp, tid)), a.softcap, a.inv_softcap, kSoftcap)};
+    stats_add<1, kSumZ>(st, z);
+  }
+  const int64_t nvec = (sp.body_end - sp.head) / kVec;
+  const T* body = row + sp.head;
+  int64_t j = tid;
+  // kUnroll vectors in flight per thread
+  for (; j + (kUnroll - 1) * 256 < nvec; j += kUnroll * 256) {
+    float z[kUnroll][kVec];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) CeVec<T>::load(body + (j + u * 256) * kVec, z[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (kSoftcap) {
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) z[u][i] = softcapped(z[u][i], a.softcap, a.inv_softcap, true);
+      }
+      stats_add<kVec, kSumZ>(st, z[u]);
+    }
+  }
+  for (; j < nvec; j += 256) {
+    float z[kVec];
+    CeVec<T>::load(body + j * kVec, z);
+    if (kSoftcap) {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) z[i] = softcapped(z[i], a.softcap, a.inv_softcap, true);
+    }
+    stats_add<kVec, kSumZ>(st, z);
+  }
+  return block_stats(st, sm);
+}
+
+// dL/dr of one logit: scale [p (1 + 2 s lse) - (1-eps) [v = t] - eps/V] (1 - (z/c)^2)
+template <bool kSoftcap>
+__device__ __forceinline__ float ce_grad(float r, bool is_t, float lse2, float zfac, float scale,
+                                         float keep, float eps_v, float c, float inv_c) {
+  float z = r, dz = 1.f;
+  if (kSoftcap) {
+    const float th = fast_tanh(r * inv_c);
+    z = c * th;
+    dz = 1.f - th * th;
+  }
+  const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2));
+  float g = __builtin_fmaf(p, zfac, -(is_t ? keep + eps_v : eps_v));
+  if (kSoftcap) g *= dz;
+  return scale * g;
+}
+
+// Gradient pass over row `row` given its lse; `t` < 0 writes zeros.
+template <typename T, bool kSoftcap>
+__device__ __forceinline__ void row_grad(const CeArgs<T>& a, const T* row, T* grow,
+                                         const RowSplit<T>& sp, int64_t t, float lse, float scale) {
+  constexpr int kVec = CeVec<T>::n;
+  constexpr int kUnroll = 4;
+  const int tid = threadIdx.x;
+  const bool live = t >= 0;
+  const float lse2 = lse * kLog2e, zfac = 1.f + a.two_s * lse;
+  const float sc = live ? scale : 0.f;
+  if (tid < sp.n_scalar) {
+    const int64_t e = scalar_index(sp, tid);
+    const float g = live ? ce_grad<kSoftcap>(ld_elem(row, e), e == t, lse2, zfac, sc, a.keep_target,
+                                             a.eps_over_v, a.softcap, a.inv_softcap)
+                         : 0.f;
+    store1(grow + e, g);
+  }
+  const int64_t nvec = (sp.body_end - sp.head) / kVec;
+  const T* body = row + sp.head;
+  T* gbody = grow + sp.head;
+  const int64_t t_rel = t - sp.head;      // target position within the body
+  int64_t j = tid;
+  for (; j + (kUnroll - 1) * 256 < nvec; j += kUnroll * 256) {
+    float z[kUnroll][kVec];
+    if (live) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) CeVec<T>::load(body + (j + u * 256) * kVec, z[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t e0 = (j + u * 256) * kVec;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i)
+        z[u][i] = live ? ce_grad<kSoftcap>(z[u][i], e0 + i == t_rel, lse2, zfac, sc, a.keep_target,
+                                           a.eps_over_v, a.softcap, a.inv_softcap)
+                       : 0.f;
+      CeVec<T>::store(gbody + e0, z[u]);
+    }
+  }
+  for (; j < nvec; j += 256) {
+    float z[kVec];
+    const int64_t e0 = j * kVec;
+    if (live) CeVec<T>::load(body + e0, z);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i)
+      z[i] = live ? ce_grad<kSoftcap>(z[i], e0 + i == t_rel, lse2, zfac, sc, a.keep_target,
+                                      a.eps_over_v, a.softcap, a.inv_softcap)
+                  : 0.f;
+    CeVec<T>::store(gbody + e0, z);
+  }
+}
+
+// Per-row forward results from the merged statistics (thread 0 only).
+template <typename T, bool kSoftcap>
+__device__ __forceinline__ float row_finish(const CeArgs<T>& a, const T* row, int64_t r, int64_t t,
+                                            const RowStats& st) {
+  const float lse = (st.m + log2f(st.d)) * kLn2;
+  // a target outside [0, V) is reported by the status word; never read past the row
+  const float zt = (t >= 0 && t < a.v) ? softcapped(ld_elem(row, t), a.softcap, a.inv_softcap, kSoftcap)
+                                       : 0.f;
+  const float rl = lse - a.keep_target * zt - a.eps_over_v * st.s + a.zloss * lse * lse;
+  a.lse[r] = lse;
+  a.row_loss_ws[r] = rl;
+  if (a.row_loss) a.row_loss[r] = rl;
+  if (a.loss_rows) a.loss_rows[r] = rl;
+  return lse;
+}
+
+template <typename T>
+__device__ __forceinline__ void row_ignored(const CeArgs<T>& a, int64_t r) {
+  a.lse[r] = 0.f;
+  a.row_loss_ws[r] = 0.f;
+  if (a.row_loss) a.row_loss[r] = 0.f;
+  if (a.loss_rows) a.loss_rows[r] = 0.f;
+}
+
+template <typename T, bool kSoftcap, bool kSumZ>
+__global__ __launch_bounds__(256) void k_ce_fwd(CeArgs<T> a) {
+  __shared__ float sm[12];
+  const int64_t r = blockIdx.x;
+  const int32_t t = a.targets[r];
+  if (t == a.ignore_index) {       // zero loss, row never read
+    if (threadIdx.x == 0) row_ignored(a, r);
+    return;
+  }
+  const T* row = a.logits + r * a.v;
+  const RowSplit<T> sp = row_split(row, a.v);
+  const RowStats st = row_stats<T, kSoftcap, kSumZ>(a, row, sp, sm);
+  if (threadIdx.x == 0) row_finish<T, kSoftcap>(a, row, r, t, st);
+}
+
+template <typename T, bool kSoftcap>
+__global__ __launch_bounds__(256) void k_ce_bwd(CeArgs<T> a) {
+  const int64_t r = blockIdx.x;
+  const int32_t t = a.targets[r];
+  const bool live = t != a.ignore_index;
+  const T* row = a.logits + r * a.v;
+  const RowSplit<T> sp = row_split(row, a.v);
+  row_grad<T, kSoftcap>(a, row, a.grad + r * a.v, sp, live ? t : -1, live ? a.lse_in[r] : 0.f,
+                        a.ctl->scale);
+}
+
+template <typename T, bool kSoftcap, bool kSumZ>
+__global__ __launch_bounds__(256) void k_ce_fused(CeArgs<T> a) {
+  __shared__ float sm[13];
+  const int64_t r = blockIdx.x;
+  const int32_t t = a.targets[r];
+  const T* row = a.logits + r * a.v;
+  const RowSplit<T> sp = row_split(row, a.v);
+  if (t == a.ignore_index) {
+    if (threadIdx.x == 0) row_ignored(a, r);
+    row_grad<T, kSoftcap>(a, row, a.grad + r * a.v, sp, -1, 0.f, 0.f);
+    return;
+  }
+  const RowStats st = row_stats<T, kSoftcap, kSumZ>(a, row, sp, sm);
+  if (threadIdx.x == 0) sm[12] = row_finish<T, kSoftcap>(a, row, r, t, st);
+  __syncthreads();
+  // every thread has read its share of the row; with in-place output the
+  // gradient pass overwrites only elements this thread reads first
+  row_grad<T, kSoftcap>(a, row, a.grad + r * a.v, sp, t, sm[12], a.ctl->scale);
+}
+
+// block_sums[b] = sum of rows [256 b, 256 b + 256) in double, fixed order.
+__global__ __launch_bounds__(256) void k_ce_block_sums(const float* __restrict__ rows, int64_t n,
+                                                       double* __restrict__ block_sums) {
+  __shared__ double red[256];
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  red[threadIdx.x] = i < n ? static_cast<double>(rows[i]) : 0.0;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = red[0];
+}
+
+}  // namespace flce

@@ -56,6 +56,7 @@ class Workload:
     softcap: float = 0.0
     reduction: str = "mean"        # "mean", "sum" or "none"
     seed: int = 0
+    kind: str = "flce"             # "flce": X, W (+ bias); "ce_logits": logits [N, V] given directly
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -86,6 +87,23 @@ WORKLOADS: Dict[str, Workload] = {
                                     softcap=30.0, reduction="sum", seed=4),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
+
+# Cross-entropy on logits given directly (the workload of the cross-entropy
+# kernels on materialised logits, TransformerEngine PR #995): logits ~ N(0, 1),
+# the distribution the fused workloads' X W^T has.  d is unused.  A small case,
+# one Llama-3-8B sequence of 128 256-way logits, and an fp32 feature case whose
+# odd V leaves most rows unaligned to 16 bytes.
+CE_WORKLOADS: Dict[str, Workload] = {
+    "ce_logits_small": Workload("ce_logits_small", 4096, 0, 32000, ignore_frac=0.02, seed=11,
+                                kind="ce_logits"),
+    "ce_logits_llama3_8b_seq": Workload("ce_logits_llama3_8b_seq", 8192, 0, 128256,
+                                        targets="zipf", ignore_frac=0.05, seed=12,
+                                        kind="ce_logits"),
+    "ce_logits_features_f32": Workload("ce_logits_features_f32", 2048, 0, 50257, dtype="f32",
+                                       targets="zipf", ignore_frac=0.25, label_smoothing=0.1,
+                                       lse_square_scale=1e-4, softcap=30.0, reduction="sum",
+                                       seed=13, kind="ce_logits"),
+}
 
 
 def _seed_seqs(seed: int) -> Dict[str, np.random.SeedSequence]:
@@ -195,3 +213,18 @@ def sample_rows(wl: Workload, count: int, salt: int = 0) -> np.ndarray:
         rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([1000 + wl.seed, salt])))
     count = min(count, wl.n)
     return np.sort(rng.choice(wl.n, size=count, replace=False)).astype(np.int64)
+
+
+def generate_logits(wl: Workload, n: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of a cross-entropy-on-logits workload: ``logits`` [n, v] ~ N(0, 1)
+    (bf16 bit patterns or fp32, drawn from the X stream) and ``targets`` as for
+    ``generate``."""
+    n = wl.n if n is None else n
+    sq = _seed_seqs(wl.seed)
+    st = streams(wl.seed)
+    logits = _normal(sq["x"], (n, wl.v), 1.0, wl.dtype)
+    t = draw_targets(st["targets"], n, wl.v, wl.targets, wl.zipf_s)
+    n_ign = int(round(wl.ignore_frac * n))
+    if n_ign:
+        t[st["ignore"].choice(n, size=n_ign, replace=False)] = wl.ignore_index
+    return {"logits": logits, "targets": t}

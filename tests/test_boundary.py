@@ -146,3 +146,58 @@ def test_null_params(lib):
     pp = ctypes.POINTER(_lib.Params)()
     assert lib.flce_forward(pp, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == INVALID
     assert lib.flce_check_status(None, None) == INVALID
+
+
+# ------------------------------------------------- cross-entropy on logits
+
+def ce_fwd(p, r=FAKE, t=FAKE, loss=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return _lib.ce_forward(p, r, t, loss, lse, None, ws, ws_bytes, None)
+
+
+def ce_bwd(p, r=FAKE, t=FAKE, lse=FAKE, g=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return _lib.ce_backward(p, r, t, lse, None, g, ws, ws_bytes, None)
+
+
+def ce_fused(p, r=FAKE, t=FAKE, loss=FAKE, lse=FAKE, g=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return _lib.ce_fused_fwd_bwd(p, r, t, loss, lse, g, ws, ws_bytes, None)
+
+
+def test_ce_workspace_is_per_row_only(lib):
+    p = _lib.make_params(65536, 8, 128256, _lib.DTYPE_BF16)
+    ws = _lib.ce_workspace_size(p)
+    assert 0 < ws < 16 * 65536 + 4096                 # status word, row map, row losses, block sums
+    # the hidden size and the slice width play no part
+    assert _lib.ce_workspace_size(_lib.make_params(65536, 12, 128256, _lib.DTYPE_BF16,
+                                                   vocab_slice=-3)) == ws
+    for bad in (P(v=0), P(n=-1), P(dtype=7), P(label_smoothing=1.5), P(softcap=-1.0),
+                P(lse_square_scale=float("nan")), P(reduction=5)):
+        assert _lib.ce_workspace_size(bad) == 0
+    assert lib.flce_ce_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("call", ["forward", "backward", "fused"])
+def test_ce_host_validation(lib, call):
+    f = {"forward": ce_fwd, "backward": ce_bwd, "fused": ce_fused}[call]
+    bf = dict(dtype=_lib.DTYPE_BF16)
+    assert f(P(v=0)) == INVALID
+    assert f(P(n=-5)) == INVALID
+    assert f(P(dtype=3)) == INVALID
+    assert f(P(label_smoothing=2.0)) == INVALID
+    assert f(P(reduction=7)) == INVALID
+    assert f(P(), r=None) == INVALID                 # missing logits with n > 0
+    assert f(P(), t=None) == INVALID
+    assert f(P(**bf), r=FAKE + 1) == INVALID         # bf16 logits not 2-byte aligned
+    assert f(P(), r=FAKE + 2) == INVALID             # fp32 logits not 4-byte aligned
+    assert f(P(), t=FAKE + 2) == INVALID
+    assert f(P(), ws=FAKE + 64) == INVALID
+    assert f(P(), ws=None) == INVALID
+    need = _lib.ce_workspace_size(P())
+    assert f(P(), ws_bytes=need - 1) == _lib.FLCE_ERR_WORKSPACE_TOO_SMALL
+    assert f(P(), lse=None) == INVALID
+    if call != "forward":
+        assert f(P(), g=None) == INVALID             # nowhere to write dL/dlogits
+        assert f(P(), g=FAKE + 8) == INVALID         # splits rows differently from the logits
+        assert f(P(**bf), g=FAKE + 2) == INVALID
+        assert f(P(reduction=2)) == _lib.FLCE_ERR_UNSUPPORTED
+    if call != "backward":
+        assert f(P(), loss=None) == INVALID
