@@ -346,6 +346,16 @@ def bench_ce(args, wl):
 
     fwd()
     fwd_ms = timed(fwd, max(3, args.steps))
+    grad = out[2]
+
+    def bwd():
+        st = _lib.ce_backward(p, r.data_ptr(), t.data_ptr(), lse.data_ptr(), None, grad.data_ptr(),
+                              ws.data_ptr(), ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise _lib.FLCEError(st, "flce_ce_backward")
+
+    bwd()
+    bwd_ms = timed(bwd, max(3, args.steps))
 
     n_valid = int((inp["targets"] != wl.ignore_index).sum())
     # must-move bytes: the valid rows read once, the gradient written once
@@ -386,8 +396,12 @@ def bench_ce(args, wl):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
             "bytes_per_launch": step_bytes,
+            "timed": "whole flce_ce_fused_fwd_bwd call (k_prep, k_ce_fused, two O(N) reduction "
+                     "launches)",
             "fwd_ms": round(fwd_ms, 4),
             "fwd_gbs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
+            "separate_bwd_ms": round(bwd_ms, 4),
+            "separate_bwd_gbs": round(step_bytes / (bwd_ms * 1e-3) / 1e9, 1),
         },
         "cpu_baseline": cpu,
     }

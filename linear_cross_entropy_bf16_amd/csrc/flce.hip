@@ -502,8 +502,8 @@ void launch_ce_fwd(const flce::CeArgs<T>& a, hipStream_t s) {
 }
 template <typename T, bool kSoftcap, bool kSumZ>
 void launch_ce_fused(const flce::CeArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((flce::k_ce_fused<T, kSoftcap, kSumZ>), dim3(static_cast<unsigned>(a.n)), dim3(256),
-                     0, s, a);
+  hipLaunchKernelGGL((flce::k_ce_fused<T, kSoftcap, kSumZ>), dim3(static_cast<unsigned>(a.n)),
+                     dim3(flce::kCeThreads), 0, s, a);
 }
 
 template <typename T>

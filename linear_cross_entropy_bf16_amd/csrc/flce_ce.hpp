@@ -9,8 +9,8 @@
 //                  row in 16-byte vectors, lse, row loss
 //   k_ce_bwd       one workgroup per row: dL/dr from the saved lse, written in
 //                  the logits' dtype (in place allowed)
-//   k_ce_fused     both in one kernel: the second pass re-reads the row the
-//                  first pass has just streamed
+//   k_ce_fused     both in one kernel, one 768-thread workgroup per row whose
+//                  registers hold the row between the two passes
 //   k_ce_block_sums  fixed-order partial sums of the row losses
 //
 // Streaming and HBM-bound: each element is read once per pass and the
@@ -51,7 +51,9 @@ template <typename T> struct CeVec;
 template <> struct CeVec<uint16_t> {
   static constexpr int n = 8;
   static __device__ __forceinline__ void load(const uint16_t* p, float (&z)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    unpack(*reinterpret_cast<const uint4*>(p), z);
+  }
+  static __device__ __forceinline__ void unpack(const uint4& u, float (&z)[8]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -67,8 +69,11 @@ template <> struct CeVec<uint16_t> {
 template <> struct CeVec<float> {
   static constexpr int n = 4;
   static __device__ __forceinline__ void load(const float* p, float (&z)[4]) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    z[0] = u.x; z[1] = u.y; z[2] = u.z; z[3] = u.w;
+    unpack(*reinterpret_cast<const uint4*>(p), z);
+  }
+  static __device__ __forceinline__ void unpack(const uint4& u, float (&z)[4]) {
+    z[0] = __uint_as_float(u.x); z[1] = __uint_as_float(u.y);
+    z[2] = __uint_as_float(u.z); z[3] = __uint_as_float(u.w);
   }
   static __device__ __forceinline__ void store(float* p, const float (&g)[4]) {
     *reinterpret_cast<float4*>(p) = float4{g[0], g[1], g[2], g[3]};
@@ -127,7 +132,8 @@ __device__ __forceinline__ void stats_add(RowStats& st, const float (&z)[N]) {
 }
 
 // Whole-workgroup merge of the per-thread statistics in a fixed order; every
-// thread gets the row's result.  `sm` holds 12 floats of LDS.
+// thread gets the row's result.  `sm` holds 3 kWaves floats of LDS.
+template <int kWaves = 4>
 __device__ __forceinline__ RowStats block_stats(RowStats st, float* sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -138,15 +144,15 @@ __device__ __forceinline__ RowStats block_stats(RowStats st, float* sm) {
   }
   if (lane == 0) {
     sm[wave] = st.m;
-    sm[4 + wave] = st.d;
-    sm[8 + wave] = st.s;
+    sm[kWaves + wave] = st.d;
+    sm[2 * kWaves + wave] = st.s;
   }
   __syncthreads();
   RowStats r{-INFINITY, 0.f, 0.f};
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    lse_merge(r.m, r.d, sm[w], sm[4 + w]);
-    r.s += sm[8 + w];
+  for (int w = 0; w < kWaves; ++w) {
+    lse_merge(r.m, r.d, sm[w], sm[kWaves + w]);
+    r.s += sm[2 * kWaves + w];
   }
   return r;
 }
@@ -310,24 +316,104 @@ __global__ __launch_bounds__(256) void k_ce_bwd(CeArgs<T> a) {
                         a.ctl->scale);
 }
 
+// Fused forward + backward, one 768-thread workgroup per row.  The first
+// kCeCache vectors of each thread (a whole 128 Ki-entry bf16 row) stay in
+// registers between the statistics pass and the gradient pass, so the row is
+// read from memory once; only a longer row's remainder is read twice.
+// A copy of v the compiler cannot see through: keeps a cached vector packed
+// (4 registers) until the point of use instead of unpacking every cached
+// vector right after its load.
+__device__ __forceinline__ uint4 opaque(uint4 v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+  return v;
+}
+
+constexpr int kCeThreads = 768;   // 3 waves per SIMD: 170 registers each
+constexpr int kCeCache = 21;      // 21 x 768 x 8 = 129024 bf16 entries per row
+
 template <typename T, bool kSoftcap, bool kSumZ>
-__global__ __launch_bounds__(256) void k_ce_fused(CeArgs<T> a) {
-  __shared__ float sm[13];
+__global__ __launch_bounds__(kCeThreads) void k_ce_fused(CeArgs<T> a) {
+  constexpr int kVec = CeVec<T>::n;
+  constexpr int kWaves = kCeThreads / 64;
+  __shared__ float sm[3 * kWaves + 1];
   const int64_t r = blockIdx.x;
   const int32_t t = a.targets[r];
+  const int tid = threadIdx.x;
   const T* row = a.logits + r * a.v;
+  T* grow = a.grad + r * a.v;
   const RowSplit<T> sp = row_split(row, a.v);
-  if (t == a.ignore_index) {
-    if (threadIdx.x == 0) row_ignored(a, r);
-    row_grad<T, kSoftcap>(a, row, a.grad + r * a.v, sp, -1, 0.f, 0.f);
+  // offsets within one row fit in 32 bits (V < 2^31)
+  const int nvec = static_cast<int>((sp.body_end - sp.head) / kVec);
+  const uint4* body = reinterpret_cast<const uint4*>(row + sp.head);
+  uint4* gbody = reinterpret_cast<uint4*>(grow + sp.head);
+  if (t == a.ignore_index) {          // zero loss, zero gradient row, row never read
+    if (tid == 0) row_ignored(a, r);
+    if (tid < sp.n_scalar) store1(grow + scalar_index(sp, tid), 0.f);
+    for (int j = tid; j < nvec; j += kCeThreads) gbody[j] = uint4{0u, 0u, 0u, 0u};
     return;
   }
-  const RowStats st = row_stats<T, kSoftcap, kSumZ>(a, row, sp, sm);
-  if (threadIdx.x == 0) sm[12] = row_finish<T, kSoftcap>(a, row, r, t, st);
+  // pass 1: statistics, the cached vectors all requested up front
+  RowStats st{-INFINITY, 0.f, 0.f};
+  if (tid < sp.n_scalar) {
+    float z[1] = {softcapped(ld_elem(row, scalar_index(sp, tid)), a.softcap, a.inv_softcap, kSoftcap)};
+    stats_add<1, kSumZ>(st, z);
+  }
+  uint4 cache[kCeCache];
+#pragma unroll
+  for (int c = 0; c < kCeCache; ++c) {
+    const int j = tid + c * kCeThreads;
+    cache[c] = j < nvec ? body[j] : uint4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int c = 0; c < kCeCache; ++c) {
+    if (tid + c * kCeThreads < nvec) {
+      float z[kVec];
+      CeVec<T>::unpack(opaque(cache[c]), z);
+      if (kSoftcap) {
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) z[i] = softcapped(z[i], a.softcap, a.inv_softcap, true);
+      }
+      stats_add<kVec, kSumZ>(st, z);
+    }
+  }
+  for (int j = tid + kCeCache * kCeThreads; j < nvec; j += kCeThreads) {
+    float z[kVec];
+    CeVec<T>::unpack(body[j], z);
+    if (kSoftcap) {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) z[i] = softcapped(z[i], a.softcap, a.inv_softcap, true);
+    }
+    stats_add<kVec, kSumZ>(st, z);
+  }
+  st = block_stats<kWaves>(st, sm);
+  if (tid == 0) sm[3 * kWaves] = row_finish<T, kSoftcap>(a, row, r, t, st);
   __syncthreads();
-  // every thread has read its share of the row; with in-place output the
-  // gradient pass overwrites only elements this thread reads first
-  row_grad<T, kSoftcap>(a, row, a.grad + r * a.v, sp, t, sm[12], a.ctl->scale);
+  // pass 2: gradient; each thread overwrites only elements it has read, so
+  // the output may be the logits themselves
+  const float lse = sm[3 * kWaves];
+  const float lse2 = lse * kLog2e, zfac = 1.f + a.two_s * lse, scale = a.ctl->scale;
+  const int t_rel = t - static_cast<int>(sp.head);    // target's offset in the body
+  if (tid < sp.n_scalar) {
+    const int64_t e = scalar_index(sp, tid);
+    store1(grow + e, ce_grad<kSoftcap>(ld_elem(row, e), e == t, lse2, zfac, scale, a.keep_target,
+                                       a.eps_over_v, a.softcap, a.inv_softcap));
+  }
+  auto grad_vec = [&](const uint4& raw, int j) {
+    float z[kVec];
+    CeVec<T>::unpack(raw, z);
+    const int e0 = j * kVec;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i)
+      z[i] = ce_grad<kSoftcap>(z[i], e0 + i == t_rel, lse2, zfac, scale, a.keep_target, a.eps_over_v,
+                               a.softcap, a.inv_softcap);
+    CeVec<T>::store(reinterpret_cast<T*>(gbody + j), z);
+  };
+#pragma unroll
+  for (int c = 0; c < kCeCache; ++c) {
+    const int j = tid + c * kCeThreads;
+    if (j < nvec) grad_vec(opaque(cache[c]), j);
+  }
+  for (int j = tid + kCeCache * kCeThreads; j < nvec; j += kCeThreads) grad_vec(body[j], j);
 }
 
 // block_sums[b] = sum of rows [256 b, 256 b + 256) in double, fixed order.
