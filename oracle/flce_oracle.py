@@ -325,3 +325,48 @@ def megatron_smoothing(eps: float, v: int) -> float:
     1 - eps and every other class gets eps / (V - 1).  Under this module's
     convention that is the target distribution of eps' = eps V / (V - 1)."""
     return eps * v / (v - 1)
+
+
+# ------------------------------------------------- predicted tokens, accuracy
+
+def predicted_tokens(z: np.ndarray, targets: np.ndarray, opts: LossOptions) -> np.ndarray:
+    """Argmax over the vocabulary of each row's final logits z (after bias and
+    softcap), the lowest index among equal maxima; -1 on ignored rows (page
+    "[CuteDSL] FLCE", Summary: the predicted-tokens and token-accuracy
+    outputs of the option set; the pages give no formula, this is the plain
+    reading).  Pinned: brute force, ties at W = 0, torch.argmax, invariance
+    under the (monotonic) softcap."""
+    pred = np.argmax(z, axis=1).astype(np.int32)     # first occurrence of the maximum
+    return np.where(valid_rows(targets, opts), pred, -1).astype(np.int32)
+
+
+def token_accuracy(pred: np.ndarray, targets: np.ndarray, opts: LossOptions,
+                   n_valid: Optional[int] = None) -> float:
+    """Fraction of valid rows whose predicted token is the target (0 when no
+    row is valid)."""
+    valid = valid_rows(targets, opts)
+    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    hits = int(((pred == np.asarray(targets)) & valid).sum())
+    return hits / nv if nv > 0 else 0.0
+
+
+def forward_metrics(x, w, bias, targets, opts: LossOptions,
+                    row_block: int = ROW_BLOCK) -> Tuple[np.ndarray, float]:
+    """(predicted tokens [N], token accuracy) of the fused problem."""
+    x, w, bias = to_f64(x), to_f64(w), to_f64(bias)
+    targets = np.asarray(targets)
+    pred = np.empty(x.shape[0], dtype=np.int32)
+    for r0 in range(0, x.shape[0], row_block):
+        sl = slice(r0, min(x.shape[0], r0 + row_block))
+        pred[sl] = predicted_tokens(logits(x[sl], w, bias, opts.softcap), targets[sl], opts)
+    return pred, token_accuracy(pred, targets, opts)
+
+
+def logits_metrics(r, targets, opts: LossOptions) -> Tuple[np.ndarray, float]:
+    """(predicted tokens [N], token accuracy) on logits given directly."""
+    z = to_f64(r)
+    if opts.softcap > 0.0:
+        z = opts.softcap * np.tanh(z / opts.softcap)
+    targets = np.asarray(targets)
+    pred = predicted_tokens(z, targets, opts)
+    return pred, token_accuracy(pred, targets, opts)

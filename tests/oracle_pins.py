@@ -465,11 +465,62 @@ def pin_megatron_smoothing(O):
         assert np.allclose(a.dx, grad, rtol=0, atol=1e-15)
 
 
+# ------------------------------------------------- predicted tokens, accuracy
+
+def pin_predicted_tokens(O):
+    """Predicted tokens by brute force (a Python loop keeping the first
+    strict maximum), torch.argmax on the same logits, ties at W = 0 (every
+    valid row predicts 0), invariance under the monotonic softcap, and the
+    accuracy as hits over valid rows on a constructed case."""
+    import torch
+
+    x, w, b, t = _problem(n=40, d=10, v=33, bias=True, ignore=6, seed=41)
+    o = _opts(O)
+    pred, acc = O.forward_metrics(x, w, b, t, o)
+    z = x @ w.T + b
+    for i in range(len(t)):
+        if t[i] == IGN:
+            assert pred[i] == -1
+            continue
+        best, arg = -math.inf, -1
+        for v in range(w.shape[0]):
+            zv = sum(float(x[i, k]) * float(w[v, k]) for k in range(x.shape[1])) + float(b[v])
+            if zv > best:
+                best, arg = zv, v
+        assert pred[i] == arg
+    tz = torch.argmax(torch.tensor(z), dim=1).numpy()
+    valid = t != IGN
+    assert np.array_equal(pred[valid], tz[valid])
+    assert acc == float(((tz == t) & valid).sum()) / valid.sum()
+    for c in (0.5, 3.0):
+        pc, _ = O.forward_metrics(x, w, b, t, _opts(O, softcap=c))
+        assert np.array_equal(pc, pred)
+    # W = 0: all logits tie, the lowest index wins
+    p0, a0 = O.forward_metrics(x, np.zeros_like(w), None, t, o)
+    assert np.all(p0[valid] == 0) and np.all(p0[~valid] == -1)
+    assert a0 == float(((t == 0) & valid).sum()) / valid.sum()
+    # constructed: X = identity rows pick class k with logit 1, others 0
+    n = 12
+    xe = np.eye(n)
+    we = np.eye(n)
+    te = np.arange(n, dtype=np.int32)
+    te[[1, 4, 7]] = [0, 0, 0]                          # three misses
+    te[10] = IGN
+    pe, ae = O.forward_metrics(xe, we, None, te, o)
+    assert np.array_equal(pe[te != IGN], np.arange(n)[te != IGN])
+    assert ae == 8 / 11
+    # no valid row: accuracy 0
+    assert O.token_accuracy(pe, np.full(n, IGN, np.int32), o) == 0.0
+    # the logits entry point agrees with the fused one at W = identity
+    pl, al = O.logits_metrics(x @ w.T + b, t, o)
+    assert np.array_equal(pl, pred) and al == acc
+
+
 ALL_PINS = [
     pin_uniform_logits, pin_single_class, pin_two_classes, pin_gradient_row_sums,
     pin_shift_invariance, pin_batch_additivity, pin_vocab_permutation,
     pin_online_merge, pin_no_valid_rows, pin_softcap_limits,
     pin_torch_cross_entropy, pin_finite_differences, pin_brute_force,
     pin_gaussian_lse_level, pin_logits_identity_linear, pin_logits_torch,
-    pin_logits_finite_differences, pin_megatron_smoothing,
+    pin_logits_finite_differences, pin_megatron_smoothing, pin_predicted_tokens,
 ]

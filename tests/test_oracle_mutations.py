@@ -157,10 +157,24 @@ def mut_megatron_plain_eps(m):
     m.megatron_smoothing = lambda eps, v: eps               # forgot the V / (V - 1)
 
 
+def mut_argmax_last_tie(m):
+    def predicted_tokens(z, targets, opts):
+        pred = (z.shape[1] - 1 - np.argmax(z[:, ::-1], axis=1)).astype(np.int32)   # last maximum
+        return np.where(m.valid_rows(targets, opts), pred, -1).astype(np.int32)
+    m.predicted_tokens = predicted_tokens
+
+
+def mut_accuracy_over_all_rows(m):
+    def token_accuracy(pred, targets, opts, n_valid=None):
+        return float((pred == np.asarray(targets)).sum()) / len(targets)
+    m.token_accuracy = token_accuracy
+
+
 MUTATIONS = [mut_drop_smoothing_sum, mut_zloss_grad_sign, mut_no_softcap_derivative,
              mut_target_off_by_one, mut_lse_missing_max, mut_mean_over_all_rows,
              mut_online_no_rescale, mut_smoothing_over_v_minus_1, mut_transposed_dw,
-             mut_logits_ignore_softcap, mut_logits_unscaled_grad, mut_megatron_plain_eps]
+             mut_logits_ignore_softcap, mut_logits_unscaled_grad, mut_megatron_plain_eps,
+             mut_argmax_last_tie, mut_accuracy_over_all_rows]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
