@@ -95,7 +95,7 @@ typedef struct flce_params {
 /* Bytes of workspace the calls need for these parameters.  with_backward = 0
  * sizes flce_forward only; 1 sizes flce_backward and flce_fused_fwd_bwd (and
  * also covers flce_forward).  Returns 0 for invalid parameters.  The size is
- * O(N (V/1024 + D) + N * vocab_slice), far below the N x V logits: the packed
+ * O(N (V/256 + D) + N * vocab_slice), far below the N x V logits: the packed
  * valid rows of X, per-row forward partials, and for the backward one G slice
  * in both orientations, X^T and an fp32 dX accumulator. */
 size_t flce_workspace_size(const flce_params* params, int with_backward);
@@ -115,6 +115,22 @@ flce_status flce_forward(const flce_params* params, const void* x, const void* w
                          const void* bias, const int32_t* targets, float* loss,
                          float* lse, float* row_loss, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* Forward plus the predicted-token and token-accuracy outputs of the option
+ * set (page "[CuteDSL] FLCE", Summary; the pages give no formula, so the plain
+ * reading): the predicted token of a row is the argmax over the vocabulary of
+ * its final logit z (after bias and softcap; the lowest index among equal
+ * maxima), and the token accuracy is the fraction of valid rows whose
+ * predicted token is the target (0 if no row is valid).  The argmax is
+ * tracked in the same GEMM epilogue as the LSE, in fp32.
+ *  pred      int32 [n] or NULL: predicted token, -1 on ignored rows
+ *  accuracy  fp32 [1] or NULL
+ * Other arguments and the workspace size as for flce_forward (both NULL is
+ * flce_forward). */
+flce_status flce_forward_metrics(const flce_params* params, const void* x, const void* w,
+                                 const void* bias, const int32_t* targets, float* loss,
+                                 float* lse, float* row_loss, int32_t* pred, float* accuracy,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Backward from the saved LSE (page "[CuteDSL] FLCE", Summary: the backward
  * recomputes the masked softmax tile by tile over the vocabulary; dW is
@@ -173,6 +189,13 @@ size_t flce_ce_workspace_size(const flce_params* params);
 flce_status flce_ce_forward(const flce_params* params, const void* logits,
                             const int32_t* targets, float* loss, float* lse,
                             float* row_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward on logits with the predicted tokens and token accuracy defined at
+ * flce_forward_metrics (pred int32 [n] or NULL, accuracy fp32 [1] or NULL). */
+flce_status flce_ce_forward_metrics(const flce_params* params, const void* logits,
+                                    const int32_t* targets, float* loss, float* lse,
+                                    float* row_loss, int32_t* pred, float* accuracy, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Backward on logits from the saved lse.
  *  grad_output  fp32 [1] device scalar, or NULL for 1.0

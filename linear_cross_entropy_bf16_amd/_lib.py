@@ -22,8 +22,9 @@ DTYPE_F32 = 1
 
 REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 
-EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_fused_fwd_bwd",
-           "flce_ce_workspace_size", "flce_ce_forward", "flce_ce_backward", "flce_ce_fused_fwd_bwd",
+EXPORTS = ("flce_workspace_size", "flce_forward", "flce_forward_metrics", "flce_backward",
+           "flce_fused_fwd_bwd", "flce_ce_workspace_size", "flce_ce_forward", "flce_ce_forward_metrics",
+           "flce_ce_backward", "flce_ce_fused_fwd_bwd",
            "flce_check_status", "flce_status_string", "flce_version")
 
 
@@ -66,6 +67,10 @@ def load():
     lib.flce_workspace_size.restype = ctypes.c_size_t
     lib.flce_forward.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.flce_forward.restype = ctypes.c_int
+    lib.flce_forward_metrics.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.flce_forward_metrics.restype = ctypes.c_int
+    lib.flce_ce_forward_metrics.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.flce_ce_forward_metrics.restype = ctypes.c_int
     lib.flce_backward.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.flce_backward.restype = ctypes.c_int
     lib.flce_fused_fwd_bwd.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -113,6 +118,18 @@ def workspace_size(params: Params, with_backward: bool) -> int:
 def forward(params, x, w, bias, targets, loss, lse, row_loss, ws, ws_bytes, stream) -> int:
     return load().flce_forward(ctypes.byref(params), x, w, bias, targets, loss, lse, row_loss, ws,
                                ws_bytes, stream)
+
+
+def forward_metrics(params, x, w, bias, targets, loss, lse, row_loss, pred, accuracy, ws, ws_bytes,
+                    stream) -> int:
+    return load().flce_forward_metrics(ctypes.byref(params), x, w, bias, targets, loss, lse, row_loss,
+                                       pred, accuracy, ws, ws_bytes, stream)
+
+
+def ce_forward_metrics(params, logits, targets, loss, lse, row_loss, pred, accuracy, ws, ws_bytes,
+                       stream) -> int:
+    return load().flce_ce_forward_metrics(ctypes.byref(params), logits, targets, loss, lse, row_loss,
+                                          pred, accuracy, ws, ws_bytes, stream)
 
 
 def backward(params, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, ws_bytes, stream) -> int:

@@ -81,9 +81,10 @@ def _workspace(params, with_backward, device) -> Tuple[torch.Tensor, int]:
 
 def forward(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
             lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
-            check_targets=False):
+            check_targets=False, return_metrics=False):
     """Returns (loss, lse, row_loss): loss is a 0-d tensor ([N] for 'none'),
-    lse and row_loss are fp32 [N]."""
+    lse and row_loss are fp32 [N].  With ``return_metrics`` also the predicted
+    tokens (int32 [N], -1 on ignored rows) and the token accuracy (0-d fp32)."""
     x2, w2, t2, b2 = _prepare(x, weight, target, bias)
     n, d = x2.shape
     v = w2.shape[0]
@@ -95,11 +96,19 @@ def forward(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=
     lse = torch.empty(n, dtype=torch.float32, device=dev)
     row_loss = torch.empty(n, dtype=torch.float32, device=dev)
     st = _stream(dev)
-    _check(_lib.forward(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(loss), _ptr(lse),
-                        _ptr(row_loss), _ptr(ws), nbytes, st), "flce_forward")
+    if return_metrics:
+        pred = torch.empty(n, dtype=torch.int32, device=dev)
+        acc = torch.empty(1, dtype=torch.float32, device=dev)
+        _check(_lib.forward_metrics(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(loss), _ptr(lse),
+                                    _ptr(row_loss), _ptr(pred), _ptr(acc), _ptr(ws), nbytes, st),
+               "flce_forward_metrics")
+    else:
+        _check(_lib.forward(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(loss), _ptr(lse),
+                            _ptr(row_loss), _ptr(ws), nbytes, st), "flce_forward")
     if check_targets:
         _check(_lib.check_status(_ptr(ws), st), "target check")
-    return (loss if reduction == "none" else loss[0]), lse, row_loss
+    out = ((loss if reduction == "none" else loss[0]), lse, row_loss)
+    return out + (pred, acc[0]) if return_metrics else out
 
 
 def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_index=-100,
@@ -227,9 +236,11 @@ def _ce_workspace(p, device):
 
 
 def cross_entropy_forward(logits, target, *, ignore_index=-100, label_smoothing=0.0,
-                          lse_square_scale=0.0, softcap=0.0, reduction="mean", check_targets=False):
+                          lse_square_scale=0.0, softcap=0.0, reduction="mean", check_targets=False,
+                          return_metrics=False):
     """Cross-entropy on given logits [..., V]: returns (loss, lse, row_loss)
-    like ``forward``."""
+    like ``forward`` (plus predicted tokens and token accuracy with
+    ``return_metrics``)."""
     r2, t2 = _prepare_logits(logits, target)
     p = _ce_params(r2, ignore_index, label_smoothing, lse_square_scale, softcap, reduction)
     n = r2.shape[0]
@@ -239,11 +250,19 @@ def cross_entropy_forward(logits, target, *, ignore_index=-100, label_smoothing=
     lse = torch.empty(n, dtype=torch.float32, device=dev)
     row_loss = torch.empty(n, dtype=torch.float32, device=dev)
     st = _stream(dev)
-    _check(_lib.ce_forward(p, _ptr(r2), _ptr(t2), _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(ws),
-                           nbytes, st), "flce_ce_forward")
+    if return_metrics:
+        pred = torch.empty(n, dtype=torch.int32, device=dev)
+        acc = torch.empty(1, dtype=torch.float32, device=dev)
+        _check(_lib.ce_forward_metrics(p, _ptr(r2), _ptr(t2), _ptr(loss), _ptr(lse), _ptr(row_loss),
+                                       _ptr(pred), _ptr(acc), _ptr(ws), nbytes, st),
+               "flce_ce_forward_metrics")
+    else:
+        _check(_lib.ce_forward(p, _ptr(r2), _ptr(t2), _ptr(loss), _ptr(lse), _ptr(row_loss),
+                               _ptr(ws), nbytes, st), "flce_ce_forward")
     if check_targets:
         _check(_lib.check_status(_ptr(ws), st), "target check")
-    return (loss if reduction == "none" else loss[0]), lse, row_loss
+    out = ((loss if reduction == "none" else loss[0]), lse, row_loss)
+    return out + (pred, acc[0]) if return_metrics else out
 
 
 def cross_entropy_backward(logits, target, lse, grad_output=None, *, ignore_index=-100,

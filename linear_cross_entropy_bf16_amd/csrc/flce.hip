@@ -50,7 +50,8 @@ struct Layout {
   int64_t n_merge_blocks;
   // byte offsets from the workspace base
   int64_t ctl, rows, tc, xc;   // shared by forward and backward
-  int64_t zt, part_m, part_d, part_s, block_sums, fwd_end;
+  int64_t zt, part_m, part_d, part_s, block_sums;
+  int64_t part_b, part_i, pred, hits, hit_sums, fwd_end;   // predicted tokens / accuracy
   int64_t g, gt, xt, wt, dx_acc, lsep, bwd_end;
 };
 
@@ -95,6 +96,11 @@ Layout make_layout(const flce_params& p) {
   L.part_d = off;      off = round_up(off + 4 * p.n * L.n_chunks, kAlign);
   L.part_s = off;      off = round_up(off + 4 * p.n * L.n_chunks, kAlign);
   L.block_sums = off;  off = round_up(off + 8 * L.n_merge_blocks, kAlign);
+  L.part_b = off;      off = round_up(off + 4 * p.n * L.n_chunks, kAlign);
+  L.part_i = off;      off = round_up(off + 4 * p.n * L.n_chunks, kAlign);
+  L.pred = off;        off = round_up(off + 4 * p.n, kAlign);
+  L.hits = off;        off = round_up(off + 4 * p.n, kAlign);
+  L.hit_sums = off;    off = round_up(off + 8 * L.n_merge_blocks, kAlign);
   L.fwd_end = off;
   // Backward region reuses the forward region (the forward's scratch is dead
   // once its loss is reduced).
@@ -178,7 +184,7 @@ void fill(float* p, int64_t count, float value, hipStream_t s) {
 int64_t grid8(int64_t tiles) { return round_up(tiles, 8); }
 
 // ----------------------------------------------------------------- forward
-template <typename T, bool kBias, bool kSoftcap, bool kSumZ>
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kArgmax>
 void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
   if (L.main_chunks > 0) {
     flce::FwdArgs<T> m = a;
@@ -187,7 +193,7 @@ void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
     m.chunk_base = 0;
     m.n_chunks = L.main_chunks;
     m.tiles_per_chunk = L.tiles_per_chunk;
-    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, false>),
+    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, false, kArgmax>),
                        dim3(static_cast<unsigned>(grid8(L.n_tiles * m.n_chunks))),
                        dim3(tile::kThreads), 0, s, m);
   }
@@ -198,15 +204,33 @@ void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
     t.chunk_base = L.main_chunks;
     t.n_chunks = 1;
     t.tiles_per_chunk = 1;
-    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, true>),
+    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, true, kArgmax>),
                        dim3(static_cast<unsigned>(grid8(L.n_tiles))), dim3(tile::kThreads), 0, s, t);
   }
 }
 
+template <typename T, bool kArgmax>
+void dispatch_fwd(const flce::FwdArgs<T>& a, const Layout& L, int key, hipStream_t s) {
+  switch (key) {
+    case 0: launch_fwd<T, false, false, false, kArgmax>(a, L, s); break;
+    case 1: launch_fwd<T, true, false, false, kArgmax>(a, L, s); break;
+    case 2: launch_fwd<T, false, true, false, kArgmax>(a, L, s); break;
+    case 3: launch_fwd<T, true, true, false, kArgmax>(a, L, s); break;
+    case 4: launch_fwd<T, false, false, true, kArgmax>(a, L, s); break;
+    case 5: launch_fwd<T, true, false, true, kArgmax>(a, L, s); break;
+    case 6: launch_fwd<T, false, true, true, kArgmax>(a, L, s); break;
+    default: launch_fwd<T, true, true, true, kArgmax>(a, L, s); break;
+  }
+}
+
+// pred / accuracy: predicted tokens and token accuracy (either may be null;
+// both null is the plain forward).
 template <typename T>
 flce_status run_forward(const flce_params& p, const Layout& L, const void* x, const void* w,
                         const void* bias, const int32_t* targets, float* loss, float* lse,
-                        float* row_loss, void* ws, hipStream_t s) {
+                        float* row_loss, void* ws, hipStream_t s, int32_t* pred = nullptr,
+                        float* accuracy = nullptr) {
+  const bool metrics = pred != nullptr || accuracy != nullptr;
   Ctl* ctl = reinterpret_cast<Ctl*>(at(ws, L.ctl));
   const bool mean = p.reduction == FLCE_REDUCTION_MEAN;
   int32_t* rows = reinterpret_cast<int32_t*>(at(ws, L.rows));
@@ -216,6 +240,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
                      static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows);
   if (p.n == 0) {
     if (p.reduction != FLCE_REDUCTION_NONE) fill(loss, 1, 0.f, s);
+    if (accuracy) fill(accuracy, 1, 0.f, s);
     return launched();
   }
   hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
@@ -237,18 +262,14 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.part_d = reinterpret_cast<float*>(at(ws, L.part_d));
   a.part_s = reinterpret_cast<float*>(at(ws, L.part_s));
   a.zt = reinterpret_cast<float*>(at(ws, L.zt));
+  a.part_b = reinterpret_cast<float*>(at(ws, L.part_b));
+  a.part_i = reinterpret_cast<int32_t*>(at(ws, L.part_i));
   const bool b = bias != nullptr, c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
   const int key = (b ? 1 : 0) | (c ? 2 : 0) | (z ? 4 : 0);
-  switch (key) {
-    case 0: launch_fwd<T, false, false, false>(a, L, s); break;
-    case 1: launch_fwd<T, true, false, false>(a, L, s); break;
-    case 2: launch_fwd<T, false, true, false>(a, L, s); break;
-    case 3: launch_fwd<T, true, true, false>(a, L, s); break;
-    case 4: launch_fwd<T, false, false, true>(a, L, s); break;
-    case 5: launch_fwd<T, true, false, true>(a, L, s); break;
-    case 6: launch_fwd<T, false, true, true>(a, L, s); break;
-    default: launch_fwd<T, true, true, true>(a, L, s); break;
-  }
+  if (metrics)
+    dispatch_fwd<T, true>(a, L, key, s);
+  else
+    dispatch_fwd<T, false>(a, L, key, s);
   flce::MergeArgs m{};
   m.part_m = a.part_m;
   m.part_d = a.part_d;
@@ -268,10 +289,23 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   m.block_sums = reinterpret_cast<double*>(at(ws, L.block_sums));
   m.rows = rows;
   m.ctl = ctl;
+  if (metrics) {
+    m.part_b = a.part_b;
+    m.part_i = a.part_i;
+    m.pred = pred ? pred : reinterpret_cast<int32_t*>(at(ws, L.pred));
+    m.hits = reinterpret_cast<float*>(at(ws, L.hits));
+  }
   hipLaunchKernelGGL(flce::k_merge, dim3(static_cast<unsigned>(L.n_merge_blocks)), dim3(256), 0, s, m);
   if (p.reduction != FLCE_REDUCTION_NONE)
     hipLaunchKernelGGL(flce::k_loss_final, dim3(1), dim3(256), 0, s, m.block_sums, L.n_merge_blocks,
                        static_cast<const Ctl*>(ctl), mean ? 1 : 0, loss);
+  if (accuracy) {
+    double* hs = reinterpret_cast<double*>(at(ws, L.hit_sums));
+    hipLaunchKernelGGL(flce::k_block_sums, dim3(static_cast<unsigned>(L.n_merge_blocks)), dim3(256), 0, s,
+                       static_cast<const float*>(m.hits), p.n, hs);
+    hipLaunchKernelGGL(flce::k_accuracy_final, dim3(1), dim3(256), 0, s, static_cast<const double*>(hs),
+                       L.n_merge_blocks, static_cast<const Ctl*>(ctl), accuracy);
+  }
   return launched();
 }
 
@@ -415,7 +449,7 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
 // ------------------------------------------------- cross-entropy on logits
 struct CeLayout {
   int64_t elem;
-  int64_t ctl, rows, row_loss, block_sums, end;
+  int64_t ctl, rows, row_loss, block_sums, pred, hits, hit_sums, end;
   int64_t n_blocks;
 };
 
@@ -428,6 +462,9 @@ CeLayout make_ce_layout(const flce_params& p) {
   L.rows = off;        off = round_up(off + 4 * p.n, kAlign);
   L.row_loss = off;    off = round_up(off + 4 * p.n, kAlign);
   L.block_sums = off;  off = round_up(off + 8 * L.n_blocks, kAlign);
+  L.pred = off;        off = round_up(off + 4 * p.n, kAlign);
+  L.hits = off;        off = round_up(off + 4 * p.n, kAlign);
+  L.hit_sums = off;    off = round_up(off + 8 * L.n_blocks, kAlign);
   L.end = off;
   return L;
 }
@@ -488,7 +525,7 @@ void ce_reduce(const flce_params& p, const CeLayout& L, float* loss, void* ws, h
   if (p.reduction == FLCE_REDUCTION_NONE) return;
   double* sums = reinterpret_cast<double*>(at(ws, L.block_sums));
   if (L.n_blocks > 0)
-    hipLaunchKernelGGL(flce::k_ce_block_sums, dim3(static_cast<unsigned>(L.n_blocks)), dim3(256), 0, s,
+    hipLaunchKernelGGL(flce::k_block_sums, dim3(static_cast<unsigned>(L.n_blocks)), dim3(256), 0, s,
                        static_cast<const float*>(reinterpret_cast<float*>(at(ws, L.row_loss))), p.n, sums);
   hipLaunchKernelGGL(flce::k_loss_final, dim3(1), dim3(256), 0, s, static_cast<const double*>(sums),
                      L.n_blocks, reinterpret_cast<const Ctl*>(at(ws, L.ctl)),
@@ -497,8 +534,12 @@ void ce_reduce(const flce_params& p, const CeLayout& L, float* loss, void* ws, h
 
 template <typename T, bool kSoftcap, bool kSumZ>
 void launch_ce_fwd(const flce::CeArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((flce::k_ce_fwd<T, kSoftcap, kSumZ>), dim3(static_cast<unsigned>(a.n)), dim3(256), 0,
-                     s, a);
+  if (a.pred)
+    hipLaunchKernelGGL((flce::k_ce_fwd<T, kSoftcap, kSumZ, true>), dim3(static_cast<unsigned>(a.n)),
+                       dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((flce::k_ce_fwd<T, kSoftcap, kSumZ, false>), dim3(static_cast<unsigned>(a.n)),
+                       dim3(256), 0, s, a);
 }
 template <typename T, bool kSoftcap, bool kSumZ>
 void launch_ce_fused(const flce::CeArgs<T>& a, hipStream_t s) {
@@ -509,8 +550,9 @@ void launch_ce_fused(const flce::CeArgs<T>& a, hipStream_t s) {
 template <typename T>
 flce_status run_ce(const flce_params& p, const CeLayout& L, const void* logits, const int32_t* targets,
                    float* loss, float* lse, float* row_loss, const float* lse_in,
-                   const float* grad_output, void* grad, void* ws, hipStream_t s, int mode) {
-  // mode 0: forward, 1: backward, 2: fused
+                   const float* grad_output, void* grad, void* ws, hipStream_t s, int mode,
+                   int32_t* pred = nullptr, float* accuracy = nullptr) {
+  // mode 0: forward, 1: backward, 2: fused; pred / accuracy: forward metrics
   ce_prep(p, L, targets, grad_output, ws, s);
   flce::CeArgs<T> a = ce_args<T>(p, L, logits, targets, ws);
   a.lse = lse;
@@ -518,6 +560,10 @@ flce_status run_ce(const flce_params& p, const CeLayout& L, const void* logits, 
   a.row_loss = row_loss;
   a.loss_rows = (mode == 0 && p.reduction == FLCE_REDUCTION_NONE) ? loss : nullptr;
   a.grad = static_cast<T*>(grad);
+  if (pred || accuracy) {
+    a.pred = pred ? pred : reinterpret_cast<int32_t*>(at(ws, L.pred));
+    a.hits = reinterpret_cast<float*>(at(ws, L.hits));
+  }
   const bool c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
   if (p.n > 0) {
     if (mode == 1) {
@@ -547,6 +593,14 @@ flce_status run_ce(const flce_params& p, const CeLayout& L, const void* logits, 
     return launched();
   }
   ce_reduce(p, L, loss, ws, s);
+  if (accuracy) {
+    double* hs = reinterpret_cast<double*>(at(ws, L.hit_sums));
+    if (L.n_blocks > 0)
+      hipLaunchKernelGGL(flce::k_block_sums, dim3(static_cast<unsigned>(L.n_blocks)), dim3(256), 0, s,
+                         static_cast<const float*>(a.hits), p.n, hs);
+    hipLaunchKernelGGL(flce::k_accuracy_final, dim3(1), dim3(256), 0, s, static_cast<const double*>(hs),
+                       L.n_blocks, a.ctl, accuracy);
+  }
   return launched();
 }
 
@@ -579,6 +633,27 @@ flce_status flce_forward(const flce_params* params, const void* x, const void* w
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s);
   return run_forward<float>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s);
+}
+
+flce_status flce_forward_metrics(const flce_params* params, const void* x, const void* w,
+                                 const void* bias, const int32_t* targets, float* loss, float* lse,
+                                 float* row_loss, int32_t* pred, float* accuracy, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  flce_status st = check_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if ((st = check_inputs(p, x, w, bias, targets)) != FLCE_OK) return st;
+  if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p.n > 0 && (!lse || !aligned(lse, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (row_loss && !aligned(row_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if ((pred && !aligned(pred, 4)) || (accuracy && !aligned(accuracy, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  const Layout L = make_layout(p);
+  if ((st = check_ws(ws, ws_bytes, L.fwd_end)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16)
+    return run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s, pred, accuracy);
+  return run_forward<float>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s, pred, accuracy);
 }
 
 static flce_status check_backward_args(const flce_params& p, const Layout& L, const float* lse,
@@ -664,6 +739,29 @@ flce_status flce_ce_forward(const flce_params* params, const void* logits, const
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_ce<uint16_t>(p, L, logits, targets, loss, lse, row_loss, nullptr, nullptr, nullptr, ws, s, 0);
   return run_ce<float>(p, L, logits, targets, loss, lse, row_loss, nullptr, nullptr, nullptr, ws, s, 0);
+}
+
+flce_status flce_ce_forward_metrics(const flce_params* params, const void* logits,
+                                    const int32_t* targets, float* loss, float* lse, float* row_loss,
+                                    int32_t* pred, float* accuracy, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  flce_status st = check_ce_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if ((st = check_ce_ptrs(p, logits, targets, nullptr)) != FLCE_OK) return st;
+  if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p.n > 0 && (!lse || !aligned(lse, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (row_loss && !aligned(row_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if ((pred && !aligned(pred, 4)) || (accuracy && !aligned(accuracy, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  const CeLayout L = make_ce_layout(p);
+  if ((st = check_ws(ws, ws_bytes, L.end)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16)
+    return run_ce<uint16_t>(p, L, logits, targets, loss, lse, row_loss, nullptr, nullptr, nullptr, ws, s, 0,
+                            pred, accuracy);
+  return run_ce<float>(p, L, logits, targets, loss, lse, row_loss, nullptr, nullptr, nullptr, ws, s, 0,
+                       pred, accuracy);
 }
 
 flce_status flce_ce_backward(const flce_params* params, const void* logits, const int32_t* targets,

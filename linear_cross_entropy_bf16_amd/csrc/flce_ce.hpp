@@ -11,7 +11,6 @@
 //                  the logits' dtype (in place allowed)
 //   k_ce_fused     both in one kernel, one 768-thread workgroup per row whose
 //                  registers hold the row between the two passes
-//   k_ce_block_sums  fixed-order partial sums of the row losses
 //
 // Streaming and HBM-bound: each element is read once per pass and the
 // gradient written once; nothing is staged.  A row whose base address is not
@@ -44,6 +43,8 @@ struct CeArgs {
   float* row_loss;          // [n] or null: per-row losses for the caller
   float* loss_rows;         // [n] or null: reduction 'none'
   T* grad;                  // [n, v] dL/dr (may be `logits`)
+  int32_t* pred;            // [n] predicted token, -1 on ignored rows (forward with metrics)
+  float* hits;              // [n] 1 where the prediction is the target
 };
 
 // 16 bytes of a row as floats, and back (bf16 with round to nearest even).
@@ -157,17 +158,50 @@ __device__ __forceinline__ RowStats block_stats(RowStats st, float* sm) {
   return r;
 }
 
+// Largest logit of a thread's elements and its lowest index.
+struct RowArgmax {
+  float b;
+  int32_t i;
+};
+
+template <int N>
+__device__ __forceinline__ void argmax_add(RowArgmax& am, const float (&z)[N], int64_t e0) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) argmax_merge(am.b, am.i, z[k], static_cast<int32_t>(e0 + k));
+}
+
+// Whole-workgroup argmax in a fixed order (4 waves); `sm` holds 8 floats.
+__device__ __forceinline__ RowArgmax block_argmax(RowArgmax am, float* sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1)
+    argmax_merge(am.b, am.i, __shfl_xor(am.b, off), __shfl_xor(am.i, off));
+  __syncthreads();                       // sm may still be read by block_stats
+  if (lane == 0) {
+    sm[wave] = am.b;
+    sm[4 + wave] = __int_as_float(am.i);
+  }
+  __syncthreads();
+  RowArgmax r{-INFINITY, 0x7fffffff};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) argmax_merge(r.b, r.i, sm[w], __float_as_int(sm[4 + w]));
+  return r;
+}
+
 // Statistics of row `row` (all 256 threads); returns the merged result.
-template <typename T, bool kSoftcap, bool kSumZ>
+// kArgmax: also the row's argmax into *am (thread-local; merged by the caller).
+template <typename T, bool kSoftcap, bool kSumZ, bool kArgmax = false>
 __device__ __forceinline__ RowStats row_stats(const CeArgs<T>& a, const T* row, const RowSplit<T>& sp,
-                                              float* sm) {
+                                              float* sm, RowArgmax* am = nullptr) {
   constexpr int kVec = CeVec<T>::n;
   constexpr int kUnroll = 4;
   const int tid = threadIdx.x;
   RowStats st{-INFINITY, 0.f, 0.f};
   if (tid < sp.n_scalar) {
-    float z[1] = {softcapped(ld_elem(row, scalar_index(sp, tid)), a.softcap, a.inv_softcap, kSoftcap)};
+    const int64_t e = scalar_index(sp, tid);
+    float z[1] = {softcapped(ld_elem(row, e), a.softcap, a.inv_softcap, kSoftcap)};
     stats_add<1, kSumZ>(st, z);
+    if (kArgmax) argmax_add(*am, z, e);
   }
   const int64_t nvec = (sp.body_end - sp.head) / kVec;
   const T* body = row + sp.head;
@@ -184,6 +218,7 @@ __device__ __forceinline__ RowStats row_stats(const CeArgs<T>& a, const T* row, 
         for (int i = 0; i < kVec; ++i) z[u][i] = softcapped(z[u][i], a.softcap, a.inv_softcap, true);
       }
       stats_add<kVec, kSumZ>(st, z[u]);
+      if (kArgmax) argmax_add(*am, z[u], sp.head + (j + u * 256) * kVec);
     }
   }
   for (; j < nvec; j += 256) {
@@ -194,6 +229,7 @@ __device__ __forceinline__ RowStats row_stats(const CeArgs<T>& a, const T* row, 
       for (int i = 0; i < kVec; ++i) z[i] = softcapped(z[i], a.softcap, a.inv_softcap, true);
     }
     stats_add<kVec, kSumZ>(st, z);
+    if (kArgmax) argmax_add(*am, z, sp.head + j * kVec);
   }
   return block_stats(st, sm);
 }
@@ -290,19 +326,34 @@ __device__ __forceinline__ void row_ignored(const CeArgs<T>& a, int64_t r) {
   if (a.loss_rows) a.loss_rows[r] = 0.f;
 }
 
-template <typename T, bool kSoftcap, bool kSumZ>
+// kArgmax: also the predicted token and whether it is the target.
+template <typename T, bool kSoftcap, bool kSumZ, bool kArgmax>
 __global__ __launch_bounds__(256) void k_ce_fwd(CeArgs<T> a) {
   __shared__ float sm[12];
   const int64_t r = blockIdx.x;
   const int32_t t = a.targets[r];
   if (t == a.ignore_index) {       // zero loss, row never read
-    if (threadIdx.x == 0) row_ignored(a, r);
+    if (threadIdx.x == 0) {
+      row_ignored(a, r);
+      if (kArgmax) {
+        a.pred[r] = -1;
+        a.hits[r] = 0.f;
+      }
+    }
     return;
   }
   const T* row = a.logits + r * a.v;
   const RowSplit<T> sp = row_split(row, a.v);
-  const RowStats st = row_stats<T, kSoftcap, kSumZ>(a, row, sp, sm);
-  if (threadIdx.x == 0) row_finish<T, kSoftcap>(a, row, r, t, st);
+  RowArgmax am{-INFINITY, 0x7fffffff};
+  const RowStats st = row_stats<T, kSoftcap, kSumZ, kArgmax>(a, row, sp, sm, &am);
+  if (kArgmax) am = block_argmax(am, sm);
+  if (threadIdx.x == 0) {
+    row_finish<T, kSoftcap>(a, row, r, t, st);
+    if (kArgmax) {
+      a.pred[r] = am.i;
+      a.hits[r] = am.i == t ? 1.f : 0.f;
+    }
+  }
 }
 
 template <typename T, bool kSoftcap>
@@ -414,20 +465,6 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_fused(CeArgs<T> a) {
     if (j < nvec) grad_vec(opaque(cache[c]), j);
   }
   for (int j = tid + kCeCache * kCeThreads; j < nvec; j += kCeThreads) grad_vec(body[j], j);
-}
-
-// block_sums[b] = sum of rows [256 b, 256 b + 256) in double, fixed order.
-__global__ __launch_bounds__(256) void k_ce_block_sums(const float* __restrict__ rows, int64_t n,
-                                                       double* __restrict__ block_sums) {
-  __shared__ double red[256];
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  red[threadIdx.x] = i < n ? static_cast<double>(rows[i]) : 0.0;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) block_sums[blockIdx.x] = red[0];
 }
 
 }  // namespace flce

@@ -6,6 +6,7 @@
 //                 target logit captured by the one tile that holds it
 //   k_merge       partials -> lse, per-row loss, per-block loss sums
 //   k_loss_final  fixed-order sum of the block sums -> scalar loss
+//   k_block_sums, k_accuracy_final  the same for per-row hits -> token accuracy
 //   k_transpose   X^T once per backward, W^T once per vocabulary slice
 //   k_pack_lse    lse of the valid rows, in packed-row order
 //   k_bwd_g       recomputed logits of one vocabulary slice -> G slice, in
@@ -180,6 +181,8 @@ struct FwdArgs {
   float* part_m;          // [n_chunks, n] running max, log2 units
   float* part_d;          // [n_chunks, n] sum of 2^(z log2e - m)
   float* part_s;          // [n_chunks, n] sum of z
+  float* part_b;          // [n_chunks, n] largest z (predicted tokens only)
+  int32_t* part_i;        // [n_chunks, n] its lowest vocabulary index
   float* zt;              // [n] target logit, by packed row
   const Ctl* ctl;         // n_valid: rows of x (packed) that take part
 };
@@ -187,12 +190,21 @@ struct FwdArgs {
 // max without NaN canonicalisation (logits here are finite or -inf)
 __device__ __forceinline__ float fmax_fast(float a, float b) { return a > b ? a : b; }
 
-template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked>
+// (b, i) <- the larger of (b, i) and (b2, i2), the lower index on a tie
+__device__ __forceinline__ void argmax_merge(float& b, int32_t& i, float b2, int32_t i2) {
+  if (b2 > b || (b2 == b && i2 < i)) {
+    b = b2;
+    i = i2;
+  }
+}
+
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked, bool kArgmax>
 __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32x16 (&acc)[4][4],
                                                   int64_t v0, int vw, int vlim,
                                                   const int32_t (&tgt)[4], int64_t n0, int wn,
                                                   int lane, float (&m_run)[4], float (&d_run)[4],
-                                                  float (&s_run)[4]) {
+                                                  float (&s_run)[4], float (&b_run)[4],
+                                                  int32_t (&i_run)[4]) {
   // 32-bit throughout: targets and vocabulary offsets are below 2^31
   const int v0i = static_cast<int>(v0);
 #pragma unroll
@@ -226,6 +238,18 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
       float mt = z[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmax_fast(mt, z[r]);
+      if (kArgmax) {
+        // r ascends with the vocabulary index: the first r holding the block
+        // maximum is its lowest index; blocks and tiles arrive in ascending
+        // vocabulary order, so a strict comparison keeps the lowest overall
+        int first = 15;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) first = z[r] == mt ? r : first;
+        if (mt > b_run[nb]) {
+          b_run[nb] = mt;
+          i_run[nb] = v0i + vw + mb * 32 + 8 * (first >> 2) + (first & 3);
+        }
+      }
       if (kSumZ) {
         float sz = 0.f;
 #pragma unroll
@@ -250,7 +274,9 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
 // kSumZ: label smoothing needs sum_v z of every row.
 // kMasked: this launch covers the one partial vocabulary tile (V mod 256 rows);
 // the main launch covers whole tiles only and carries no masking code.
-template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked>
+// kArgmax: also the largest logit of each row and its lowest index (predicted
+// tokens, token accuracy).
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked, bool kArgmax>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fwd(FwdArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
@@ -274,9 +300,13 @@ void k_fwd(FwdArgs<T> a) {
     const int64_t tok = n0 + wn * 128 + nb * 32 + (lane & 31);
     tgt[nb] = tok < nv ? a.targets[tok] : -1;
   }
-  float m_run[4], d_run[4], s_run[4];
+  float m_run[4], d_run[4], s_run[4], b_run[4];
+  int32_t i_run[4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) { m_run[nb] = -INFINITY; d_run[nb] = 0.f; s_run[nb] = 0.f; }
+  for (int nb = 0; nb < 4; ++nb) {
+    m_run[nb] = -INFINITY; d_run[nb] = 0.f; s_run[nb] = 0.f;
+    b_run[nb] = -INFINITY; i_run[nb] = 0x7fffffff;
+  }
 
   const Operand<T> A{a.w, a.d, a.v, a.d};   // rows: vocabulary
   const Operand<T> B{a.x, a.d, nv, a.d};    // rows: valid tokens
@@ -298,8 +328,9 @@ void k_fwd(FwdArgs<T> a) {
     // One token column and one 32-row block at a time: 16 logits of this lane,
     // bias and softcap applied in registers, merged into the running
     // (max, sum-exp) of the column; the accumulators are never written back.
-    fwd_tile_epilogue<T, kBias, kSoftcap, kSumZ, kMasked>(a, acc, v0, vw, vlim, tgt, n0, wn, lane,
-                                                          m_run, d_run, s_run);
+    fwd_tile_epilogue<T, kBias, kSoftcap, kSumZ, kMasked, kArgmax>(a, acc, v0, vw, vlim, tgt, n0, wn,
+                                                                   lane, m_run, d_run, s_run, b_run,
+                                                                   i_run);
   }
 
   // Combine the two lane halves (same token, disjoint vocabulary rows) ...
@@ -310,6 +341,7 @@ void k_fwd(FwdArgs<T> a) {
     const float s2 = __shfl_xor(s_run[nb], 32);
     lse_merge(m_run[nb], d_run[nb], m2, d2);
     s_run[nb] += s2;
+    if (kArgmax) argmax_merge(b_run[nb], i_run[nb], __shfl_xor(b_run[nb], 32), __shfl_xor(i_run[nb], 32));
   }
   // ... then the two wave rows through LDS, in a fixed order.
   if (wm == 1 && lane < 32) {
@@ -318,6 +350,10 @@ void k_fwd(FwdArgs<T> a) {
       xch[0][wn][nb][lane] = m_run[nb];
       xch[1][wn][nb][lane] = d_run[nb];
       xch[2][wn][nb][lane] = s_run[nb];
+      if (kArgmax) {
+        xch[3][wn][nb][lane] = b_run[nb];
+        xch[4][wn][nb][lane] = __int_as_float(i_run[nb]);
+      }
     }
   }
   __syncthreads();
@@ -326,12 +362,18 @@ void k_fwd(FwdArgs<T> a) {
     for (int nb = 0; nb < 4; ++nb) {
       lse_merge(m_run[nb], d_run[nb], xch[0][wn][nb][lane], xch[1][wn][nb][lane]);
       const float s = s_run[nb] + xch[2][wn][nb][lane];
+      if (kArgmax)
+        argmax_merge(b_run[nb], i_run[nb], xch[3][wn][nb][lane], __float_as_int(xch[4][wn][nb][lane]));
       const int64_t tok = n0 + wn * 128 + nb * 32 + lane;
       if (tok < nv) {
         const int64_t slot = (a.chunk_base + ch) * a.n + tok;
         a.part_m[slot] = m_run[nb];
         a.part_d[slot] = d_run[nb];
         a.part_s[slot] = s;
+        if (kArgmax) {
+          a.part_b[slot] = b_run[nb];
+          a.part_i[slot] = i_run[nb];
+        }
       }
     }
   }
@@ -341,6 +383,10 @@ struct MergeArgs {
   const float* part_m;
   const float* part_d;
   const float* part_s;
+  const float* part_b;  // null unless predicted tokens are wanted
+  const int32_t* part_i;
+  int32_t* pred;        // [n] or null: predicted token, -1 on ignored rows
+  float* hits;          // [n] or null: 1 where the prediction is the target
   const float* zt;
   const int32_t* targets;
   int64_t n, v, n_chunks;
@@ -376,11 +422,30 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
     if (a.row_loss) a.row_loss[r] = rl;
     if (a.loss_rows) a.loss_rows[r] = rl;
     row = rl;
+    if (a.pred) {
+      // chunks in ascending vocabulary order: a strict comparison keeps the
+      // lowest index among equal maxima
+      float b = -INFINITY;
+      int32_t idx = -1;
+      for (int64_t c = 0; c < a.n_chunks; ++c) {
+        const float bc = a.part_b[c * a.n + j];
+        if (bc > b) {
+          b = bc;
+          idx = a.part_i[c * a.n + j];
+        }
+      }
+      a.pred[r] = idx;
+      a.hits[r] = idx == a.targets[r] ? 1.f : 0.f;
+    }
   }
   if (j < a.n && a.targets[j] == a.ignore_index) {   // row j itself, if ignored
     a.lse[j] = 0.f;
     if (a.row_loss) a.row_loss[j] = 0.f;
     if (a.loss_rows) a.loss_rows[j] = 0.f;
+    if (a.pred) {
+      a.pred[j] = -1;
+      a.hits[j] = 0.f;
+    }
   }
   red[threadIdx.x] = row;
   __syncthreads();
@@ -389,6 +454,39 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
     __syncthreads();
   }
   if (threadIdx.x == 0) a.block_sums[blockIdx.x] = red[0];
+}
+
+// block_sums[b] = sum of vals [256 b, 256 b + 256) in double, fixed order.
+__global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ vals, int64_t n,
+                                                    double* __restrict__ block_sums) {
+  __shared__ double red[256];
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  red[threadIdx.x] = i < n ? static_cast<double>(vals[i]) : 0.0;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = red[0];
+}
+
+// Token accuracy: the block sums of the per-row hits over n_valid (0 if none).
+__global__ __launch_bounds__(256) void k_accuracy_final(const double* __restrict__ block_sums,
+                                                        int64_t nblocks, const Ctl* __restrict__ ctl,
+                                                        float* __restrict__ accuracy) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < nblocks; i += 256) s += block_sums[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int32_t nv = ctl->n_valid;
+    accuracy[0] = nv > 0 ? static_cast<float>(red[0] / nv) : 0.f;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ block_sums,

@@ -115,3 +115,32 @@ def compare_full(inp, dtype, o: O.LossOptions, vocab_slice=0, got=None):
     if ref.db is not None and got["db"] is not None:
         assert_close(got["db"], ref.db, "db")
     return got, ref
+
+
+def check_predictions(pred: np.ndarray, acc: float, z: np.ndarray, targets: np.ndarray,
+                      o: O.LossOptions, n_valid=None, tie_tol: float = 1e-3):
+    """Predicted tokens against the fp64 logits ``z`` of the same rows.  The
+    argmax is an integer decided in fp32 on the GPU: where it differs from the
+    fp64 argmax, the two logits must be a near-tie (within ``tie_tol`` of the
+    row's logit scale); ignored rows must hold -1.  The accuracy must be the
+    GPU's own hit rate (``n_valid`` overrides the denominator for sampled
+    rows: then only the predictions are checked)."""
+    valid = np.asarray(targets) != o.ignore_index
+    assert np.all(pred[~valid] == -1), "ignored rows must predict -1"
+    ref = np.argmax(z, axis=1)
+    rows = np.nonzero(valid & (pred != ref))[0]
+    scale = max(1.0, float(np.abs(z).max()))
+    for i in rows:
+        p = int(pred[i])
+        assert 0 <= p < z.shape[1], f"row {i}: predicted {p} outside the vocabulary"
+        gap = z[i, ref[i]] - z[i, p]
+        assert gap <= tie_tol * scale, f"row {i}: predicted {p}, fp64 argmax {ref[i]}, gap {gap:.3e}"
+    if n_valid is None:
+        nv = int(valid.sum())
+        hits = int(((pred == targets) & valid).sum())
+        want = hits / nv if nv else 0.0
+        assert abs(acc - want) <= 1e-6, (acc, want)
+        # and the oracle's accuracy, up to the near-tie rows
+        ref_acc = O.token_accuracy(np.where(valid, ref, -1), targets, o)
+        assert abs(acc - ref_acc) <= len(rows) / max(nv, 1) + 1e-6, (acc, ref_acc)
+    return len(rows)

@@ -200,3 +200,25 @@ def test_llama3_seq_sampled_rows(mode):
     # each row's entries sum to 0 up to the bf16 rounding of each entry
     gd = g.double()
     assert torch.all(gd.sum(dim=1).abs() <= 2.0 ** -8 * gd.abs().sum(dim=1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("v", [1, 7, 1000, 4097])
+def test_forward_metrics(dtype, v):
+    inp = logits_problem(129, v, dtype, seed=v + 1, spread=2.0)
+    o = O.LossOptions(softcap=5.0, label_smoothing=0.1)
+    banner(f"metrics {dtype} v={v}")
+    r = U.dev_tensor(inp["logits"], dtype)
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, rl, pred, acc = api.cross_entropy_forward(r, t, return_metrics=True, **U.lib_opts(o))
+    loss0, lse0, rl0 = api.cross_entropy_forward(r, t, **U.lib_opts(o))
+    torch.cuda.synchronize()
+    assert torch.equal(lse, lse0) and torch.equal(rl, rl0) and float(loss) == float(loss0)
+    z = O.to_f64(inp["logits"])
+    z = o.softcap * np.tanh(z / o.softcap)
+    U.check_predictions(pred.cpu().numpy(), float(acc), z, inp["targets"], o)
+    # exact ties resolve to the lowest index
+    r2 = torch.zeros_like(r)
+    _, _, _, p2, _ = api.cross_entropy_forward(r2, t, return_metrics=True)
+    valid = inp["targets"] != IGN
+    assert np.all(p2.cpu().numpy()[valid] == 0)

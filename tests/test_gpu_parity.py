@@ -303,3 +303,53 @@ def test_noncontiguous_and_batched_inputs():
     U.assert_loss(float(api.linear_cross_entropy(x, wt, t).item()), ref.loss, "column-major W")
     loss3 = api.linear_cross_entropy(x.reshape(4, 60, 64), w, t.reshape(4, 60).long())
     U.assert_loss(float(loss3.item()), ref.loss, "batched x")
+
+
+# ------------------------------------------------- predicted tokens, accuracy
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,d,v,feats", [
+    (300, 136, 1000, dict()), (513, 64, 4097, dict(softcap=3.0, label_smoothing=0.1)),
+    (257, 264, 257, dict(lse_square_scale=1e-3)), (64, 1024, 3000, dict(softcap=30.0)),
+])
+def test_forward_metrics(dtype, n, d, v, feats):
+    """Predicted tokens and token accuracy from the forward epilogue: equal
+    to the fp64 argmax except at near-ties, -1 on ignored rows, accuracy the
+    hit rate; the loss and lse equal the plain forward's bit for bit."""
+    inp = small_problem(n, d, v, dtype, bias=True, seed=n + v, w_std=0.5)
+    o = O.LossOptions(**feats)
+    banner(f"metrics {dtype} n={n} d={d} v={v} {feats}")
+    x = U.dev_tensor(inp["x"], dtype)
+    w = U.dev_tensor(inp["w"], dtype)
+    b = U.dev_tensor(inp["bias"], dtype)
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, rl, pred, acc = api.forward(x, w, t, b, return_metrics=True, **U.lib_opts(o))
+    loss0, lse0, rl0 = api.forward(x, w, t, b, **U.lib_opts(o))
+    torch.cuda.synchronize()
+    assert torch.equal(lse, lse0) and torch.equal(rl, rl0) and float(loss) == float(loss0)
+    z = O.logits(O.to_f64(inp["x"]), O.to_f64(inp["w"]), O.to_f64(inp["bias"]), o.softcap)
+    U.check_predictions(pred.cpu().numpy(), float(acc), z, inp["targets"], o)
+
+
+def test_forward_metrics_exact_ties():
+    """Equal logits resolve to the lowest index, also across vocabulary tiles
+    and chunks: W = 0 predicts 0 everywhere; a row of W duplicated at a higher
+    index (another tile) and made the largest predicts the lower copy."""
+    n, d, v = 200, 64, 2000
+    inp = small_problem(n, d, v, "bf16", seed=7)
+    x = U.dev_tensor(inp["x"], "bf16")
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    w0 = torch.zeros((v, d), dtype=torch.bfloat16, device="cuda")
+    _, _, _, pred, acc = api.forward(x, w0, t, None, return_metrics=True)
+    valid = inp["targets"] != IGN
+    p = pred.cpu().numpy()
+    assert np.all(p[valid] == 0) and np.all(p[~valid] == -1)
+    assert abs(float(acc) - ((inp["targets"] == 0) & valid).sum() / valid.sum()) <= 1e-6
+    wd = U.dev_tensor(inp["w"], "bf16").clone()
+    wd[300] = U.dev_tensor(inp["x"], "bf16")[0] * 4      # row 0's best class by far
+    wd[1700] = wd[300]                                  # a tied copy in a later tile
+    _, _, _, pred, _ = api.forward(x, wd, t, None, return_metrics=True)
+    p = pred.cpu().numpy()
+    assert not np.any(p == 1700)                        # always tied with 300, never chosen
+    if valid[0]:
+        assert p[0] == 300
