@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_batch8")
     ap.add_argument("--vocab-slice", type=int, default=0)
+    ap.add_argument("--token-chunk", type=int, default=0,
+                    help="backward over this many packed rows at a time (0 = whole batch)")
+    ap.add_argument("--dw-bf16", action="store_true", help="dW in bf16 instead of fp32")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle baseline runs on (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -132,7 +135,7 @@ def main():
     t = torch.from_numpy(inp["targets"]).to(dev)
     opts = dict(ignore_index=wl.ignore_index, label_smoothing=wl.label_smoothing,
                 lse_square_scale=wl.lse_square_scale, softcap=wl.softcap, reduction=wl.reduction,
-                vocab_slice=args.vocab_slice)
+                vocab_slice=args.vocab_slice, token_chunk=args.token_chunk, dw_bf16=args.dw_bf16)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
     base_alloc = torch.cuda.memory_allocated(dev)
@@ -143,7 +146,8 @@ def main():
     out = (torch.empty(1, dtype=torch.float32, device=dev),
            torch.empty(wl.n, dtype=torch.float32, device=dev),
            torch.empty((wl.n, wl.d), dtype=x.dtype, device=dev),
-           torch.empty((wl.v, wl.d), dtype=torch.float32, device=dev),
+           torch.empty((wl.v, wl.d), dtype=torch.bfloat16 if args.dw_bf16 else torch.float32,
+                       device=dev),
            torch.empty(wl.v, dtype=torch.float32, device=dev) if b is not None else None)
 
     def step():
@@ -233,6 +237,8 @@ def main():
                    "ignore_frac": wl.ignore_frac, "reduction": wl.reduction, "bias": wl.bias,
                    "label_smoothing": wl.label_smoothing, "lse_square_scale": wl.lse_square_scale,
                    "softcap": wl.softcap, "vocab_slice": args.vocab_slice or "default",
+                   "token_chunk": args.token_chunk or "whole batch",
+                   "dw_dtype": "bf16" if args.dw_bf16 else "fp32",
                    "parallelism": "single GPU"},
         "mfma_frac_step": round(step_tflops / peak, 4),
         "step_tflops": round(step_tflops, 1),

@@ -90,14 +90,24 @@ typedef struct flce_params {
   int32_t reduction;         /* flce_reduction */
   int32_t vocab_slice;       /* backward vocabulary slice width; 0 = library default.
                                 Rounded up to a multiple of 256. */
+  int32_t token_chunk;       /* backward token chunk: 0 = the whole batch in one pass;
+                                else the packed valid rows are processed this many at a
+                                time (rounded up to 256), so the backward workspace (G
+                                slices, X^T, the dX running sum) is sized by the chunk,
+                                not by N, and dW / db accumulate over the chunks */
+  int32_t dw_bf16;           /* 0: dW is fp32; 1: dW is bf16 (half the memory; rounded
+                                once per token chunk, as it accumulates in its own dtype) */
 } flce_params;
 
 /* Bytes of workspace the calls need for these parameters.  with_backward = 0
  * sizes flce_forward only; 1 sizes flce_backward and flce_fused_fwd_bwd (and
  * also covers flce_forward).  Returns 0 for invalid parameters.  The size is
- * O(N (V/256 + D) + N * vocab_slice), far below the N x V logits: the packed
- * valid rows of X, per-row forward partials, and for the backward one G slice
- * in both orientations, X^T and an fp32 dX accumulator. */
+ * O(N (V/256 + D) + C * (vocab_slice + D)), far below the N x V logits: the
+ * packed valid rows of X, per-row forward partials, and for the backward one
+ * G slice in both orientations, X^T and an fp32 dX accumulator, for C = N
+ * tokens or the token chunk (page "Cutting LLM Memory by 84%", "Path to
+ * Production": processing the tokens in blocks along N keeps the memory
+ * constant in the sequence length). */
 size_t flce_workspace_size(const flce_params* params, int with_backward);
 
 /* Forward: loss and per-row LSE.
@@ -138,14 +148,14 @@ flce_status flce_forward_metrics(const flce_params* params, const void* x, const
  *  lse          fp32 [n] from flce_forward with the same inputs and options
  *  grad_output  fp32 [1] device scalar g (d total / d loss), or NULL for 1.0
  *  dx           [n, d] dtype, overwritten
- *  dw           fp32 [v, d], overwritten
+ *  dw           [v, d] fp32 (bf16 with params->dw_bf16), overwritten
  *  dbias        fp32 [v], overwritten; may be NULL only when bias is NULL
  *  ws           at least flce_workspace_size(params, 1) bytes
  * reduction NONE returns FLCE_ERR_UNSUPPORTED (a per-token upstream gradient
  * cannot be folded into the vocabulary-sliced weight-gradient contraction). */
 flce_status flce_backward(const flce_params* params, const void* x, const void* w,
                           const void* bias, const int32_t* targets, const float* lse,
-                          const float* grad_output, void* dx, float* dw, float* dbias,
+                          const float* grad_output, void* dx, void* dw, float* dbias,
                           void* ws, size_t ws_bytes, void* stream);
 
 /* Forward and backward in one call with grad_output = 1.0 (the fwd+bwd
@@ -154,7 +164,7 @@ flce_status flce_backward(const flce_params* params, const void* x, const void* 
  * then consumed).  reduction NONE returns FLCE_ERR_UNSUPPORTED. */
 flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const void* w,
                                const void* bias, const int32_t* targets, float* loss,
-                               float* lse, void* dx, float* dw, float* dbias, void* ws,
+                               float* lse, void* dx, void* dw, float* dbias, void* ws,
                                size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

@@ -40,6 +40,8 @@ class Params(ctypes.Structure):
         ("softcap", ctypes.c_float),
         ("reduction", ctypes.c_int32),
         ("vocab_slice", ctypes.c_int32),
+        ("token_chunk", ctypes.c_int32),
+        ("dw_bf16", ctypes.c_int32),
     ]
 
 
@@ -101,14 +103,15 @@ def status_string(status: int) -> str:
 
 
 def make_params(n, d, v, dtype, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0,
-                softcap=0.0, reduction="mean", vocab_slice=0) -> Params:
+                softcap=0.0, reduction="mean", vocab_slice=0, token_chunk=0, dw_bf16=0) -> Params:
     """``reduction`` is 'mean', 'sum', 'none' or the raw enum value."""
     if isinstance(reduction, str):
         if reduction not in REDUCTIONS:
             raise ValueError(f"reduction must be one of {tuple(REDUCTIONS)}, got {reduction!r}")
         reduction = REDUCTIONS[reduction]
     return Params(int(n), int(d), int(v), int(dtype), int(ignore_index), float(label_smoothing),
-                  float(lse_square_scale), float(softcap), int(reduction), int(vocab_slice))
+                  float(lse_square_scale), float(softcap), int(reduction), int(vocab_slice),
+                  int(token_chunk), int(dw_bf16))
 
 
 def workspace_size(params: Params, with_backward: bool) -> int:

@@ -63,12 +63,16 @@ def _prepare(x, weight, target, bias):
 
 
 def make_params(n, d, v, dtype, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0,
-                softcap=0.0, reduction="mean", vocab_slice=0) -> _lib.Params:
+                softcap=0.0, reduction="mean", vocab_slice=0, token_chunk=0,
+                dw_bf16=False) -> _lib.Params:
     return _lib.make_params(n, d, v, _DTYPES[dtype], ignore_index, label_smoothing,
-                            lse_square_scale, softcap, reduction, vocab_slice)
+                            lse_square_scale, softcap, reduction, vocab_slice, token_chunk,
+                            1 if dw_bf16 else 0)
 
 
 def workspace_bytes(n, d, v, dtype=torch.bfloat16, with_backward=True, **opts) -> int:
+    """Workspace of the calls for these sizes and options (``make_params``
+    keywords)."""
     return _lib.workspace_size(make_params(n, d, v, dtype, **opts), with_backward)
 
 
@@ -113,14 +117,16 @@ def forward(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=
 
 def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_index=-100,
              label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0, reduction="mean",
-             vocab_slice=0):
-    """Returns (dx, dw, db): dx in x's dtype, dw and db fp32 (db None without
-    bias).  grad_output is a device scalar (None = 1.0)."""
+             vocab_slice=0, token_chunk=0, dw_bf16=False):
+    """Returns (dx, dw, db): dx in x's dtype, dw fp32 (bf16 with ``dw_bf16``)
+    and db fp32 (db None without bias).  grad_output is a device scalar
+    (None = 1.0).  ``token_chunk`` > 0 runs the backward over that many packed
+    rows at a time."""
     x2, w2, t2, b2 = _prepare(x, weight, target, bias)
     n, d = x2.shape
     v = w2.shape[0]
     p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
-                    reduction, vocab_slice)
+                    reduction, vocab_slice, token_chunk, dw_bf16)
     dev = x2.device
     ws, nbytes = _workspace(p, True, dev)
     g = None
@@ -128,7 +134,7 @@ def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_inde
         g = grad_output.detach().reshape(1).to(device=dev, dtype=torch.float32).contiguous()
     lse = lse.detach().to(torch.float32).contiguous()
     dx = torch.empty((n, d), dtype=x2.dtype, device=dev)
-    dw = torch.empty((v, d), dtype=torch.float32, device=dev)
+    dw = torch.empty((v, d), dtype=torch.bfloat16 if dw_bf16 else torch.float32, device=dev)
     db = torch.empty(v, dtype=torch.float32, device=dev) if b2 is not None else None
     _check(_lib.backward(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(lse), _ptr(g), _ptr(dx),
                          _ptr(dw), _ptr(db), _ptr(ws), nbytes, _stream(dev)), "flce_backward")
@@ -137,15 +143,16 @@ def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_inde
 
 def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
                   lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
-                  workspace: Optional[torch.Tensor] = None, out=None):
+                  token_chunk=0, dw_bf16=False, workspace: Optional[torch.Tensor] = None, out=None):
     """One call computing (loss, lse, dx, dw, db) with grad_output = 1.
     ``workspace`` and ``out`` (a tuple of preallocated loss, lse, dx, dw, db)
-    let a caller reuse buffers across steps."""
+    let a caller reuse buffers across steps; ``token_chunk`` and ``dw_bf16``
+    as for ``backward``."""
     x2, w2, t2, b2 = _prepare(x, weight, target, bias)
     n, d = x2.shape
     v = w2.shape[0]
     p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
-                    reduction, vocab_slice)
+                    reduction, vocab_slice, token_chunk, dw_bf16)
     dev = x2.device
     nbytes = _lib.workspace_size(p, True)
     if workspace is None:
@@ -158,7 +165,7 @@ def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoo
         loss = torch.empty(1, dtype=torch.float32, device=dev)
         lse = torch.empty(n, dtype=torch.float32, device=dev)
         dx = torch.empty((n, d), dtype=x2.dtype, device=dev)
-        dw = torch.empty((v, d), dtype=torch.float32, device=dev)
+        dw = torch.empty((v, d), dtype=torch.bfloat16 if dw_bf16 else torch.float32, device=dev)
         db = torch.empty(v, dtype=torch.float32, device=dev) if b2 is not None else None
     else:
         loss, lse, dx, dw, db = out

@@ -46,7 +46,8 @@ struct Layout {
   int64_t v_tiles, n_tiles, tiles_per_chunk, n_chunks;
   int64_t v_full, main_chunks;   // whole vocabulary tiles; chunks of the unmasked launch
   int64_t slice, ldg;     // backward slice width (multiple of 256) and G row pitch
-  int64_t ldt;            // token pitch of X^T and G^T (N rounded up to 256, plus kPitchPad)
+  int64_t chunk, n_tok_chunks;   // backward token chunk (multiple of 256) and their count
+  int64_t ldt;            // token pitch of X^T and G^T (chunk, plus kPitchPad)
   int64_t n_merge_blocks;
   // byte offsets from the workspace base
   int64_t ctl, rows, tc, xc;   // shared by forward and backward
@@ -80,7 +81,13 @@ Layout make_layout(const flce_params& p) {
   }
   L.slice = round_up(slice < p.v ? slice : p.v, tile::kM);
   L.ldg = L.slice + kPitchPad;
-  L.ldt = round_up(p.n, tile::kN) + kPitchPad;
+  // the backward works on at most `chunk` packed rows at a time; one chunk
+  // (the whole batch) unless params.token_chunk asks for less
+  const int64_t all = round_up(p.n > 0 ? p.n : 1, tile::kN);
+  L.chunk = p.token_chunk > 0 ? round_up(p.token_chunk, tile::kN) : all;
+  if (L.chunk > all) L.chunk = all;
+  L.n_tok_chunks = p.n > 0 ? cdiv(p.n, L.chunk) : 1;
+  L.ldt = L.chunk + kPitchPad;
   L.n_merge_blocks = cdiv(p.n, 256);
 
   int64_t off = 0;
@@ -105,13 +112,13 @@ Layout make_layout(const flce_params& p) {
   // Backward region reuses the forward region (the forward's scratch is dead
   // once its loss is reduced).
   off = base;
-  L.g = off;           off = round_up(off + L.elem * p.n * L.ldg, kAlign);
+  L.g = off;           off = round_up(off + L.elem * L.chunk * L.ldg, kAlign);
   L.gt = off;          off = round_up(off + L.elem * L.ldg * L.ldt, kAlign);
   L.xt = off;          off = round_up(off + L.elem * p.d * L.ldt, kAlign);
   L.wt = off;          off = round_up(off + L.elem * p.d * L.ldg, kAlign);
   const bool multi_slice = L.slice < p.v;
-  L.dx_acc = off;   // one fp32 256 x 256 block per (token tile, d tile), in accumulator order
-  if (multi_slice) off = round_up(off + 4 * round_up(p.n, tile::kN) * round_up(p.d, tile::kM), kAlign);
+  L.dx_acc = off;   // one fp32 256 x 256 block per (token tile, d tile) of a chunk, in accumulator order
+  if (multi_slice) off = round_up(off + 4 * L.chunk * round_up(p.d, tile::kM), kAlign);
   L.lsep = off;        off = round_up(off + 4 * p.n, kAlign);
   L.bwd_end = off;
   return L;
@@ -134,6 +141,8 @@ flce_status check_params(const flce_params* p) {
     return FLCE_ERR_INVALID_ARGUMENT;
   if (!(p->softcap >= 0.f) || !std::isfinite(p->softcap)) return FLCE_ERR_INVALID_ARGUMENT;
   if (p->vocab_slice < 0 || p->vocab_slice > (1 << 20)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->token_chunk < 0 || p->token_chunk > (1 << 22)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->dw_bf16 != 0 && p->dw_bf16 != 1) return FLCE_ERR_INVALID_ARGUMENT;
   // per-tile buffer offsets are 32-bit: 256 rows of the widest K-major operand
   if (p->d > (1 << 20) || p->n > (1 << 22)) return FLCE_ERR_INVALID_ARGUMENT;
   // byte sizes of the largest tensors must fit comfortably in int64
@@ -318,17 +327,41 @@ void launch_g(const flce::GArgs<T>& a, int64_t grid, hipStream_t s) {
 
 template <typename T>
 void transpose(const T* in, int64_t rows, int64_t cols, int64_t ld_in, T* out, int64_t out_rows,
-               int64_t ld_out_used, int64_t ld_out, hipStream_t s, const Ctl* row_bound = nullptr) {
+               int64_t ld_out_used, int64_t ld_out, hipStream_t s, const Ctl* row_bound = nullptr,
+               int64_t row0 = 0) {
   const int64_t gx = cdiv(ld_out_used, 64), gy = cdiv(out_rows, 64);
   if (gx <= 0 || gy <= 0) return;
   hipLaunchKernelGGL((flce::k_transpose<T>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
-                     dim3(256), 0, s, in, rows, cols, ld_in, out, out_rows, ld_out, row_bound);
+                     dim3(256), 0, s, in, rows, cols, ld_in, out, out_rows, ld_out, row_bound, row0);
+}
+
+template <typename T, typename DW>
+void launch_dw(const T* xt, const T* gt, const flce_params& p, const Layout& L, int64_t v0, int64_t len,
+               int64_t gcols, int64_t d_tiles, int64_t s_tiles, int64_t c0, bool accumulate,
+               const Ctl* ctl, DW* dw, hipStream_t s) {
+  flce::DwArgs<T, DW> wa{};
+  wa.xt = xt;
+  wa.gt = gt;
+  wa.d = p.d;
+  wa.v0 = v0;
+  wa.slice_len = len;
+  wa.ldt = L.ldt;
+  wa.gcols = gcols;
+  wa.ctl = ctl;
+  wa.dw = dw;
+  wa.d_tiles = d_tiles;
+  wa.s_tiles = s_tiles;
+  wa.row0 = c0;
+  wa.cap = L.chunk;
+  wa.accumulate = accumulate ? 1 : 0;
+  hipLaunchKernelGGL((flce::k_dw<T, DW>), dim3(static_cast<unsigned>(grid8(d_tiles * s_tiles))),
+                     dim3(tile::kThreads), 0, s, wa);
 }
 
 template <typename T>
 flce_status run_backward(const flce_params& p, const Layout& L, const void* x, const void* w,
                          const void* bias, const int32_t* targets, const float* lse,
-                         const float* grad_output, void* dx, float* dw, float* dbias, void* ws,
+                         const float* grad_output, void* dx, void* dw, float* dbias, void* ws,
                          hipStream_t s, bool packed) {
   Ctl* ctl = reinterpret_cast<Ctl*>(at(ws, L.ctl));
   const bool mean = p.reduction == FLCE_REDUCTION_MEAN;
@@ -352,92 +385,92 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
     hipLaunchKernelGGL(flce::k_pack_lse, dim3(static_cast<unsigned>(cdiv(p.n, 256))), dim3(256), 0, s,
                        lse, static_cast<const int32_t*>(rows), static_cast<const Ctl*>(ctl), lsep);
   const T* W = static_cast<const T*>(w);
-  // X^T of the packed valid rows [d][ldt], tokens >= n_valid zero
-  transpose<T>(xc, p.n, p.d, p.d, xt, p.d, round_up(p.n, tile::kN), L.ldt, s, ctl);
   const int64_t n_slices = cdiv(p.v, L.slice);
   const int64_t d_tiles = cdiv(p.d, tile::kM);
+  const int64_t c_tiles = L.chunk / tile::kN;   // token tiles of a chunk (upper bound)
   const bool has_bias = bias != nullptr;
-  for (int64_t si = 0; si < n_slices; ++si) {
-    const int64_t v0 = si * L.slice;
-    const int64_t len = (p.v - v0) < L.slice ? (p.v - v0) : L.slice;
-    const int64_t s_tiles = cdiv(len, tile::kM);
-    const int64_t gcols = s_tiles * tile::kM;
-    // W^T of the slice [d][ldg], vocabulary >= len zero
-    transpose<T>(W + v0 * p.d, len, p.d, p.d, wt, p.d, gcols, L.ldg, s);
-    if (p.n > 0) {
-      flce::GArgs<T> ga{};
-      ga.x = xc;
-      ga.w = W;
-      ga.bias = static_cast<const T*>(bias);
-      ga.targets = tc;
-      ga.ctl = ctl;
-      ga.lsep = lsep;
-      ga.n = p.n;
-      ga.d = p.d;
-      ga.v = p.v;
-      ga.ignore_index = p.ignore_index;
-      ga.softcap = p.softcap;
-      ga.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
-      ga.keep_target = 1.0f - p.label_smoothing;
-      ga.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
-      ga.two_s = 2.0f * p.lse_square_scale;
-      ga.v0 = v0;
-      ga.slice_len = len;
-      ga.ldg = L.ldg;
-      ga.ldt = L.ldt;
-      ga.g = g;
-      ga.gt = gt;
-      ga.s_tiles = s_tiles;
-      const int64_t g_grid = grid8(L.n_tiles * s_tiles);   // upper bound: all rows valid
-      ga.group = kRasterGroup;
-      const int key = (has_bias ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
-      switch (key) {
-        case 0: launch_g<T, false, false>(ga, g_grid, s); break;
-        case 1: launch_g<T, true, false>(ga, g_grid, s); break;
-        case 2: launch_g<T, false, true>(ga, g_grid, s); break;
-        default: launch_g<T, true, true>(ga, g_grid, s); break;
+  // Token chunks outer, vocabulary slices inner: dX of a chunk is finished
+  // within its pass; dW and db of every slice accumulate over the chunks.
+  for (int64_t ci = 0; ci < L.n_tok_chunks; ++ci) {
+    const int64_t c0 = ci * L.chunk;              // first packed row of the chunk
+    // X^T of the chunk's packed valid rows [d][ldt], tokens past them zero
+    transpose<T>(xc + c0 * p.d, L.chunk, p.d, p.d, xt, p.d, L.chunk, L.ldt, s, ctl, c0);
+    for (int64_t si = 0; si < n_slices; ++si) {
+      const int64_t v0 = si * L.slice;
+      const int64_t len = (p.v - v0) < L.slice ? (p.v - v0) : L.slice;
+      const int64_t s_tiles = cdiv(len, tile::kM);
+      const int64_t gcols = s_tiles * tile::kM;
+      // W^T of the slice [d][ldg], vocabulary >= len zero
+      transpose<T>(W + v0 * p.d, len, p.d, p.d, wt, p.d, gcols, L.ldg, s);
+      if (p.n > 0) {
+        flce::GArgs<T> ga{};
+        ga.x = xc + c0 * p.d;
+        ga.w = W;
+        ga.bias = static_cast<const T*>(bias);
+        ga.targets = tc + c0;
+        ga.ctl = ctl;
+        ga.lsep = lsep + c0;
+        ga.n = L.chunk;
+        ga.row0 = c0;
+        ga.d = p.d;
+        ga.v = p.v;
+        ga.ignore_index = p.ignore_index;
+        ga.softcap = p.softcap;
+        ga.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
+        ga.keep_target = 1.0f - p.label_smoothing;
+        ga.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
+        ga.two_s = 2.0f * p.lse_square_scale;
+        ga.v0 = v0;
+        ga.slice_len = len;
+        ga.ldg = L.ldg;
+        ga.ldt = L.ldt;
+        ga.g = g;
+        ga.gt = gt;
+        ga.s_tiles = s_tiles;
+        const int64_t g_grid = grid8(c_tiles * s_tiles);   // upper bound: all rows valid
+        ga.group = kRasterGroup;
+        const int key = (has_bias ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
+        switch (key) {
+          case 0: launch_g<T, false, false>(ga, g_grid, s); break;
+          case 1: launch_g<T, true, false>(ga, g_grid, s); break;
+          case 2: launch_g<T, false, true>(ga, g_grid, s); break;
+          default: launch_g<T, true, true>(ga, g_grid, s); break;
+        }
       }
-    }
-    flce::DwArgs<T> wa{};
-    wa.xt = xt;
-    wa.gt = gt;
-    wa.d = p.d;
-    wa.v0 = v0;
-    wa.slice_len = len;
-    wa.ldt = L.ldt;
-    wa.gcols = gcols;
-    wa.ctl = ctl;
-    wa.dw = dw;
-    wa.d_tiles = d_tiles;
-    wa.s_tiles = s_tiles;
-    hipLaunchKernelGGL((flce::k_dw<T>), dim3(static_cast<unsigned>(grid8(d_tiles * s_tiles))),
-                       dim3(tile::kThreads), 0, s, wa);
-    if (p.n > 0) {
-      flce::DxArgs<T> xa{};
-      xa.wt = wt;
-      xa.g = g;
-      xa.n = p.n;
-      xa.d = p.d;
-      xa.kdim = gcols;
-      xa.ldg = L.ldg;
-      xa.ctl = ctl;
-      xa.acc_buf = dx_acc;
-      xa.rows = rows;
-      xa.dx = static_cast<T*>(dx);
-      xa.first = si == 0;
-      xa.d_tiles = d_tiles;
-      const int64_t x_grid = grid8(d_tiles * L.n_tiles);   // upper bound: all rows valid
-      if (si + 1 == n_slices)
-        hipLaunchKernelGGL((flce::k_dx<T, true>), dim3(static_cast<unsigned>(x_grid)),
-                           dim3(tile::kThreads), 0, s, xa);
+      if (p.dw_bf16)
+        launch_dw<T, uint16_t>(xt, gt, p, L, v0, len, gcols, d_tiles, s_tiles, c0, ci > 0, ctl,
+                               static_cast<uint16_t*>(dw), s);
       else
-        hipLaunchKernelGGL((flce::k_dx<T, false>), dim3(static_cast<unsigned>(x_grid)),
-                           dim3(tile::kThreads), 0, s, xa);
+        launch_dw<T, float>(xt, gt, p, L, v0, len, gcols, d_tiles, s_tiles, c0, ci > 0, ctl,
+                            static_cast<float*>(dw), s);
+      if (p.n > 0) {
+        flce::DxArgs<T> xa{};
+        xa.wt = wt;
+        xa.g = g;
+        xa.n = L.chunk;
+        xa.row0 = c0;
+        xa.d = p.d;
+        xa.kdim = gcols;
+        xa.ldg = L.ldg;
+        xa.ctl = ctl;
+        xa.acc_buf = dx_acc;
+        xa.rows = rows + c0;
+        xa.dx = static_cast<T*>(dx);
+        xa.first = si == 0;
+        xa.d_tiles = d_tiles;
+        const int64_t x_grid = grid8(d_tiles * c_tiles);   // upper bound: all rows valid
+        if (si + 1 == n_slices)
+          hipLaunchKernelGGL((flce::k_dx<T, true>), dim3(static_cast<unsigned>(x_grid)),
+                             dim3(tile::kThreads), 0, s, xa);
+        else
+          hipLaunchKernelGGL((flce::k_dx<T, false>), dim3(static_cast<unsigned>(x_grid)),
+                             dim3(tile::kThreads), 0, s, xa);
+      }
+      if (has_bias)
+        hipLaunchKernelGGL((flce::k_db<T>), dim3(static_cast<unsigned>(cdiv(len, 4))), dim3(256), 0, s,
+                           static_cast<const T*>(gt), L.ldt, L.chunk, v0, len,
+                           static_cast<const Ctl*>(ctl), dbias, c0, ci > 0 ? 1 : 0);
     }
-    if (has_bias)
-      hipLaunchKernelGGL((flce::k_db<T>), dim3(static_cast<unsigned>(cdiv(len, 4))), dim3(256), 0, s,
-                         static_cast<const T*>(gt), L.ldt, p.n, v0, len, static_cast<const Ctl*>(ctl),
-                         dbias);
   }
   // rows of dX with an ignored target (never written by k_dx) are zero
   if (p.n > 0)
@@ -657,7 +690,7 @@ flce_status flce_forward_metrics(const flce_params* params, const void* x, const
 }
 
 static flce_status check_backward_args(const flce_params& p, const Layout& L, const float* lse,
-                                       void* dx, float* dw, float* dbias, const void* bias,
+                                       void* dx, void* dw, float* dbias, const void* bias,
                                        const void* ws, size_t ws_bytes) {
   if (p.reduction == FLCE_REDUCTION_NONE) return FLCE_ERR_UNSUPPORTED;
   if (p.n > 0 && (!lse || !aligned(lse, 4) || !dx || !aligned(dx, 16))) return FLCE_ERR_INVALID_ARGUMENT;
@@ -669,7 +702,7 @@ static flce_status check_backward_args(const flce_params& p, const Layout& L, co
 
 flce_status flce_backward(const flce_params* params, const void* x, const void* w, const void* bias,
                           const int32_t* targets, const float* lse, const float* grad_output, void* dx,
-                          float* dw, float* dbias, void* ws, size_t ws_bytes, void* stream) {
+                          void* dw, float* dbias, void* ws, size_t ws_bytes, void* stream) {
   flce_status st = check_params(params);
   if (st != FLCE_OK) return st;
   const flce_params& p = *params;
@@ -687,7 +720,7 @@ flce_status flce_backward(const flce_params* params, const void* x, const void* 
 
 flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const void* w,
                                const void* bias, const int32_t* targets, float* loss, float* lse,
-                               void* dx, float* dw, float* dbias, void* ws, size_t ws_bytes,
+                               void* dx, void* dw, float* dbias, void* ws, size_t ws_bytes,
                                void* stream) {
   flce_status st = check_params(params);
   if (st != FLCE_OK) return st;

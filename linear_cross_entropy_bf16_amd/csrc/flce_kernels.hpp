@@ -37,6 +37,13 @@ struct Ctl {           // first bytes of the workspace
   float pad;
 };
 
+// Valid packed rows of a backward token chunk: the chunk starts at packed row
+// row0 and holds at most cap rows (the whole batch is one chunk by default).
+__device__ __forceinline__ int64_t chunk_valid(const Ctl* ctl, int64_t row0, int64_t cap) {
+  const int64_t left = static_cast<int64_t>(ctl->n_valid) - row0;
+  return left < 0 ? 0 : (left < cap ? left : cap);
+}
+
 __device__ __forceinline__ float ld_elem(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
@@ -519,9 +526,10 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, int64_t rows,
                                                    int64_t cols, int64_t ld_in,
                                                    T* __restrict__ out, int64_t out_rows,
-                                                   int64_t ld_out, const Ctl* __restrict__ ctl) {
+                                                   int64_t ld_out, const Ctl* __restrict__ ctl,
+                                                   int64_t row0) {
   __shared__ T t[64][65];
-  if (ctl && ctl->n_valid < rows) rows = ctl->n_valid;   // X: only the packed valid rows
+  if (ctl) rows = chunk_valid(ctl, row0, rows);   // X: only the chunk's packed valid rows
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -557,6 +565,7 @@ struct GArgs {
   T* g;                 // [n, ldg]       G slice, columns >= slice_len written as 0
   T* gt;                // [gcols, ldt]   the same slice transposed, tokens >= n_valid as 0
   int64_t s_tiles, group;   // vocabulary tiles of the slice; raster group
+  int64_t row0;         // token chunk: its first packed row (x, targets, lsep start there)
   const Ctl* ctl;
 };
 
@@ -712,7 +721,7 @@ template <typename T, bool kBias, bool kSoftcap>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bwd_g(GArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
-  const int64_t nv = a.ctl->n_valid;
+  const int64_t nv = chunk_valid(a.ctl, a.row0, a.n);
   const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;   // valid rows only
   int64_t L;
   if (!xcd_logical_n(blockIdx.x, n_tiles * a.s_tiles, L)) return;
@@ -786,29 +795,38 @@ void k_bwd_g(GArgs<T> a) {
   }
 }
 
-template <typename T>
+template <typename T, typename DW>
 struct DwArgs {
-  const T* xt;          // [d, ldt]      X^T of the packed rows, tokens >= n_valid are 0
+  const T* xt;          // [d, ldt]      X^T of the chunk's packed rows, tokens past them 0
   const T* gt;          // [gcols, ldt]  G^T slice
   int64_t d, v0, slice_len, ldt, gcols;
   const Ctl* ctl;
-  float* dw;            // [v, d]
+  DW* dw;               // [v, d] fp32, or bf16 bits
   int64_t d_tiles, s_tiles;
+  int64_t row0, cap;    // token chunk: first packed row, capacity
+  int32_t accumulate;   // add to dW (a later token chunk) instead of overwriting it
 };
+
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
 
 // dW[v0 + v, :] = scale sum_n G[n, v] X[n, :]: one dedicated contraction over
 // all tokens, each output tile written exactly once (page "Cutting LLM Memory
 // by 84%", "Path to Production": a dW kernel whose programs own a block of W
 // and iterate over the batch).  Computed as C[d, v] so each lane stores four
 // consecutive d.
-template <typename T>
-__device__ __forceinline__ void dw_tile(const DwArgs<T>& a, int64_t L, char* lds) {
+template <typename T, typename DW>
+__device__ __forceinline__ void dw_tile(const DwArgs<T, DW>& a, int64_t L, char* lds) {
   int64_t dt, st;
   grouped(L, a.d_tiles, a.s_tiles, kGroup, dt, st);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const int64_t kdim = (static_cast<int64_t>(a.ctl->n_valid) + 7) / 8 * 8;   // packed valid rows
+  const int64_t kdim = (chunk_valid(a.ctl, a.row0, a.cap) + 7) / 8 * 8;   // the chunk's valid rows
   const Operand<T> A{a.xt, a.ldt, a.d, kdim};       // (d, n) at xt[d*ldt + n]
   const Operand<T> B{a.gt, a.ldt, a.gcols, kdim};   // (v, n) at gt[v*ldt + n]
   f32x16 acc[4][4];
@@ -819,15 +837,21 @@ __device__ __forceinline__ void dw_tile(const DwArgs<T>& a, int64_t L, char* lds
   for (int nb = 0; nb < 4; ++nb) {
     const int64_t vl = st * tile::kN + wn * 128 + nb * 32 + (lane & 31);
     if (vl >= a.slice_len) continue;
-    float* row = a.dw + (a.v0 + vl) * a.d;
+    DW* row = a.dw + (a.v0 + vl) * a.d;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t dd = dt * tile::kM + wm * 128 + mb * 32 + 8 * q + 4 * (lane >> 5);
-        if (dd < a.d)
-          store4(row + dd, scale * acc[mb][nb][4 * q], scale * acc[mb][nb][4 * q + 1],
-                 scale * acc[mb][nb][4 * q + 2], scale * acc[mb][nb][4 * q + 3]);
+        if (dd < a.d) {
+          float4 v{scale * acc[mb][nb][4 * q], scale * acc[mb][nb][4 * q + 1],
+                   scale * acc[mb][nb][4 * q + 2], scale * acc[mb][nb][4 * q + 3]};
+          if (a.accumulate) {
+            const float4 p = load4(row + dd);
+            v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+          }
+          store4(row + dd, v.x, v.y, v.z, v.w);
+        }
       }
   }
 }
@@ -842,7 +866,8 @@ struct DxArgs {
   T* dx;                // [n, d]
   int32_t first;
   int64_t d_tiles;
-  const int32_t* rows;  // packed row -> row
+  const int32_t* rows;  // packed row -> row (from the chunk's first packed row)
+  int64_t row0;         // token chunk: first packed row; n is its capacity
 };
 
 // dX (+)= G_slice W_slice, computed as C[d, n] tile by tile.  The running
@@ -948,9 +973,9 @@ __device__ __forceinline__ void dx_tile(const DxArgs<T>& a, int64_t L, int64_t n
 // at the headline shape run as two lock-step rounds whose concurrent tiles
 // share their K = N operand panels in L2 (interleaving them with dX tiles in
 // one launch desynchronised them and made the slice 1.8x slower).
-template <typename T>
+template <typename T, typename DW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_dw(DwArgs<T> a) {
+void k_dw(DwArgs<T, DW> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
   int64_t L;
   if (!xcd_logical_n(blockIdx.x, a.d_tiles * a.s_tiles, L)) return;
@@ -961,7 +986,7 @@ template <typename T, bool kLast>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_dx(DxArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
-  const int64_t nv = a.ctl->n_valid;
+  const int64_t nv = chunk_valid(a.ctl, a.row0, a.n);
   const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;   // valid rows only
   int64_t L;
   if (!xcd_logical_n(blockIdx.x, a.d_tiles * n_tiles, L)) return;
@@ -970,20 +995,23 @@ void k_dx(DxArgs<T> a) {
 
 // db[v0 + v] = scale sum_n G^T[v, n]: one wave per vocabulary row, lanes
 // striding over the tokens, then a fixed-order wave reduction.
+// accumulate: add to db (a later token chunk); n, row0: the chunk's capacity
+// and first packed row.
 template <typename T>
 __global__ __launch_bounds__(256) void k_db(const T* __restrict__ gt, int64_t ldt, int64_t n,
                                             int64_t v0, int64_t slice_len,
-                                            const Ctl* __restrict__ ctl, float* __restrict__ db) {
+                                            const Ctl* __restrict__ ctl, float* __restrict__ db,
+                                            int64_t row0, int32_t accumulate) {
   const int64_t v = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (v >= slice_len) return;
   const int lane = threadIdx.x & 63;
   const T* row = gt + v * ldt;
-  const int64_t nv = ctl->n_valid < n ? ctl->n_valid : n;
+  const int64_t nv = chunk_valid(ctl, row0, n);
   float s = 0.f;
   for (int64_t i = lane; i < nv; i += 64) s += ld_elem(row, i);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) db[v0 + v] = ctl->scale * s;
+  if (lane == 0) db[v0 + v] = ctl->scale * s + (accumulate ? db[v0 + v] : 0.f);
 }
 
 __global__ __launch_bounds__(256) void k_fill(float* __restrict__ p, int64_t count, float value) {

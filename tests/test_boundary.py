@@ -202,3 +202,23 @@ def test_ce_host_validation(lib, call):
         assert f(P(reduction=2)) == _lib.FLCE_ERR_UNSUPPORTED
     if call != "backward":
         assert f(P(), loss=None) == INVALID
+
+
+def test_token_chunk_and_dw_bf16_params(lib):
+    assert _lib.workspace_size(P(token_chunk=-1), True) == 0
+    assert _lib.workspace_size(P(dw_bf16=2), True) == 0
+    assert fwd(P(token_chunk=-256)) == INVALID
+    assert bwd(P(dw_bf16=-1)) == INVALID
+    # the backward workspace is sized by the chunk, not by the batch
+    full = _lib.workspace_size(_lib.make_params(65536, 4096, 128256, _lib.DTYPE_BF16), True)
+    chunked = _lib.workspace_size(_lib.make_params(65536, 4096, 128256, _lib.DTYPE_BF16,
+                                                   token_chunk=16384), True)
+    assert chunked < full / 2
+    a = _lib.workspace_size(_lib.make_params(32768, 4096, 128256, _lib.DTYPE_BF16,
+                                             token_chunk=8192), True)
+    b = _lib.workspace_size(_lib.make_params(65536, 4096, 128256, _lib.DTYPE_BF16,
+                                             token_chunk=8192), True)
+    # doubling N adds only the per-row and packed-row parts (forward partials, packed X)
+    assert b - a < 32768 * (4096 * 2 + 4 * 600) * 1.1
+    # a chunk larger than the batch is the whole batch
+    assert (_lib.workspace_size(P(token_chunk=1 << 20), True) == _lib.workspace_size(P(), True))

@@ -353,3 +353,55 @@ def test_forward_metrics_exact_ties():
     assert not np.any(p == 1700)                        # always tied with 300, never chosen
     if valid[0]:
         assert p[0] == 300
+
+
+# ------------------------------------------------- token chunks, bf16 dW
+
+def _fused_opts(inp, dtype, o, to_host=True, **kw):
+    x = U.dev_tensor(inp["x"], dtype)
+    w = U.dev_tensor(inp["w"], dtype)
+    b = U.dev_tensor(inp["bias"], dtype) if inp.get("bias") is not None else None
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, dx, dw, db = api.fused_fwd_bwd(x, w, t, b, **U.lib_opts(o), **kw)
+    torch.cuda.synchronize()
+    out = dict(loss=float(loss.item()), lse=U.host(lse), dx_raw=dx, dw_raw=dw)
+    if to_host:
+        out.update(dx=U.host(dx), dw=U.host(dw), db=None if db is None else U.host(db))
+    return out
+
+
+@pytest.mark.parametrize("dw_bf16", [False, True])
+@pytest.mark.parametrize("n,chunk,ignore", [(1000, 256, 0.1), (1000, 512, 0.0), (700, 256, 0.6),
+                                            (300, 1024, 0.1)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_token_chunks(dtype, n, chunk, ignore, dw_bf16):
+    """The backward over chunks of packed rows (the last one ragged; with 60%
+    ignored rows the later chunks start past n_valid and hold nothing), dW and
+    db accumulated over the chunks, dW optionally bf16: every output against
+    the oracle; dX bit for bit equal to the single-pass schedule."""
+    inp = small_problem(n, 136, 1000, dtype, bias=True, ignore_frac=ignore, seed=n + chunk)
+    o = O.LossOptions(label_smoothing=0.05, lse_square_scale=1e-3)
+    banner(f"token chunks {dtype} n={n} chunk={chunk} ignore={ignore} dw_bf16={dw_bf16}")
+    got = _fused_opts(inp, dtype, o, token_chunk=chunk, dw_bf16=dw_bf16, vocab_slice=256)
+    assert got["dw_raw"].dtype == (torch.bfloat16 if dw_bf16 else torch.float32)
+    U.compare_full(inp, dtype, o, got=got)
+    one = _fused_opts(inp, dtype, o, vocab_slice=256)
+    assert torch.equal(got["dx_raw"], one["dx_raw"])
+    assert got["loss"] == one["loss"] and np.array_equal(got["lse"], one["lse"])
+
+
+@pytest.mark.timeout(600)
+def test_token_chunks_llama3_seq():
+    """One Llama-3-8B sequence (8192 x 4096 x 128256) in chunks of 2048 with
+    bf16 dW against the single-pass fp32 run: same loss and dX bit for bit,
+    dW within bf16 rounding."""
+    wl = W.WORKLOADS["llama3_8b_seq"]
+    banner(f"token chunks {wl}")
+    inp = W.generate(wl)
+    o = U.options(wl)
+    a = _fused_opts(inp, wl.dtype, o, to_host=False, token_chunk=2048, dw_bf16=True)
+    b = _fused_opts(inp, wl.dtype, o, to_host=False)
+    assert a["loss"] == b["loss"] and torch.equal(a["dx_raw"], b["dx_raw"])
+    dwa, dwb = a["dw_raw"].double(), b["dw_raw"].double()
+    rel = (torch.linalg.norm(dwa - dwb) / torch.linalg.norm(dwb)).item()
+    assert rel <= 4e-3, rel
