@@ -29,32 +29,38 @@ HBM_PEAK_GBS = 8000.0
 # The pages' own figure for this shape (B200, CuTe-DSL FLCE, bf16, BT = 65 536,
 # V = 128 256, H = 4096): 194 ms per fwd+bwd, i.e. 337.8 k tokens/s.
 PAGES_TOKENS_PER_S = 65536 / 0.194
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fwd_llama3_8b_batch8_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "linear_cross_entropy_bf16_amd", "csrc", f)
-                  for f in ("flce_gemm.hpp", "flce_kernels.hpp", "flce.hip")]
+_CSRC = os.path.join(ROOT, "linear_cross_entropy_bf16_amd", "csrc")
+# committed counter summaries, and the sources each measured kernel is built from
+TRAFFIC = {
+    "k_fwd": (os.path.join(ROOT, "profiles", "k_fwd_llama3_8b_batch8_traffic.json"),
+              ("flce_gemm.hpp", "flce_kernels.hpp", "flce.hip")),
+    "k_ce_fused": (os.path.join(ROOT, "profiles", "k_ce_fused_ce_logits_llama3_8b_seq_traffic.json"),
+                   ("flce_kernels.hpp", "flce_ce.hpp", "flce.hip")),
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "k_fwd") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in TRAFFIC[kernel][1]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """Per-launch HBM bytes of k_fwd from the committed counter summary, or
-    None when it is missing, for another workload, or stale."""
+def measured_traffic(workload: str, kernel: str = "k_fwd"):
+    """Per-launch HBM bytes of ``kernel`` from the committed counter summary,
+    or None when it is missing, for another workload, or stale (taken on other
+    kernel sources)."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC[kernel][0]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload or t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("workload") != workload or t.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -400,7 +406,7 @@ def bench_ce(args, wl):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name, "k_ce_fused"),
             "bytes_per_launch": step_bytes,
             "timed": "whole flce_ce_fused_fwd_bwd call (k_prep, k_ce_fused, two O(N) reduction "
                      "launches)",
