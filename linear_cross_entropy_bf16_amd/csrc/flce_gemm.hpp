@@ -358,6 +358,11 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
     load_frags(a1, b1, 0, 3);
     mfmas(a0, b0);
     interleave<false>();
+    // Keep this step's MFMAs above the wait: they cover the latency of the
+    // fragment reads issued with their first half (the scheduler otherwise
+    // sinks most of them below the barrier and the wait stalls on reads it
+    // has just issued).
+    __builtin_amdgcn_sched_barrier(0);
     // every load but A(s+2) done, so A(s+1) and B(s+1) landed (own loads);
     // own reads of slab s done; after the barrier both hold for every wave
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
