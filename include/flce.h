@@ -226,6 +226,23 @@ flce_status flce_ce_fused_fwd_bwd(const flce_params* params, const void* logits,
                                   const int32_t* targets, float* loss, float* lse,
                                   void* dlogits, void* ws, size_t ws_bytes, void* stream);
 
+/* Forward and backward with three contractions instead of four (the
+ * chunked-store schedule the page "[CuteDSL] FLCE" compares against: 6 N D V
+ * FLOPs instead of 8 N D V, more memory): the packed valid rows go in token
+ * chunks of params->token_chunk rows (0 = 8192); the forward GEMM of a chunk
+ * keeps its raw logits (fp32, C x V x 4 bytes of workspace) next to the
+ * online-softmax partials, the G kernel reads them back instead of
+ * recomputing them, dX of the chunk contracts over the whole vocabulary at
+ * once, and dW / db accumulate over the chunks.  Same arguments, outputs and
+ * options as flce_fused_fwd_bwd (params->vocab_slice is unused); the
+ * workspace is flce_stored_workspace_size(params). */
+size_t flce_stored_workspace_size(const flce_params* params);
+
+flce_status flce_fused_fwd_bwd_stored(const flce_params* params, const void* x, const void* w,
+                                      const void* bias, const int32_t* targets, float* loss,
+                                      float* lse, void* dx, void* dw, float* dbias, void* ws,
+                                      size_t ws_bytes, void* stream);
+
 /* Synchronises `stream`, then reports the device-side target check of the
  * last call that used this workspace: FLCE_OK or FLCE_ERR_TARGET_OUT_OF_RANGE
  * (FLCE_ERR_DEVICE if the synchronisation or copy fails).  When it reports an

@@ -24,7 +24,8 @@ REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_forward_metrics", "flce_backward",
            "flce_fused_fwd_bwd", "flce_ce_workspace_size", "flce_ce_forward", "flce_ce_forward_metrics",
-           "flce_ce_backward", "flce_ce_fused_fwd_bwd",
+           "flce_ce_backward", "flce_ce_fused_fwd_bwd", "flce_stored_workspace_size",
+           "flce_fused_fwd_bwd_stored",
            "flce_check_status", "flce_status_string", "flce_version")
 
 
@@ -77,6 +78,11 @@ def load():
     lib.flce_backward.restype = ctypes.c_int
     lib.flce_fused_fwd_bwd.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.flce_fused_fwd_bwd.restype = ctypes.c_int
+    lib.flce_stored_workspace_size.argtypes = [pp]
+    lib.flce_stored_workspace_size.restype = ctypes.c_size_t
+    lib.flce_fused_fwd_bwd_stored.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                              _P]
+    lib.flce_fused_fwd_bwd_stored.restype = ctypes.c_int
     lib.flce_ce_workspace_size.argtypes = [pp]
     lib.flce_ce_workspace_size.restype = ctypes.c_size_t
     lib.flce_ce_forward.argtypes = [pp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -143,6 +149,16 @@ def backward(params, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, w
 def fused_fwd_bwd(params, x, w, bias, targets, loss, lse, dx, dw, dbias, ws, ws_bytes, stream) -> int:
     return load().flce_fused_fwd_bwd(ctypes.byref(params), x, w, bias, targets, loss, lse, dx, dw,
                                      dbias, ws, ws_bytes, stream)
+
+
+def stored_workspace_size(params: Params) -> int:
+    return int(load().flce_stored_workspace_size(ctypes.byref(params)))
+
+
+def fused_fwd_bwd_stored(params, x, w, bias, targets, loss, lse, dx, dw, dbias, ws, ws_bytes,
+                         stream) -> int:
+    return load().flce_fused_fwd_bwd_stored(ctypes.byref(params), x, w, bias, targets, loss, lse, dx,
+                                            dw, dbias, ws, ws_bytes, stream)
 
 
 def ce_workspace_size(params: Params) -> int:

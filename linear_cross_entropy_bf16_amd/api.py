@@ -70,10 +70,12 @@ def make_params(n, d, v, dtype, ignore_index=-100, label_smoothing=0.0, lse_squa
                             1 if dw_bf16 else 0)
 
 
-def workspace_bytes(n, d, v, dtype=torch.bfloat16, with_backward=True, **opts) -> int:
+def workspace_bytes(n, d, v, dtype=torch.bfloat16, with_backward=True, stored_logits=False,
+                    **opts) -> int:
     """Workspace of the calls for these sizes and options (``make_params``
-    keywords)."""
-    return _lib.workspace_size(make_params(n, d, v, dtype, **opts), with_backward)
+    keywords); ``stored_logits``: of the three-contraction schedule."""
+    p = make_params(n, d, v, dtype, **opts)
+    return _lib.stored_workspace_size(p) if stored_logits else _lib.workspace_size(p, with_backward)
 
 
 def _workspace(params, with_backward, device) -> Tuple[torch.Tensor, int]:
@@ -143,20 +145,24 @@ def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_inde
 
 def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
                   lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
-                  token_chunk=0, dw_bf16=False, workspace: Optional[torch.Tensor] = None, out=None):
+                  token_chunk=0, dw_bf16=False, workspace: Optional[torch.Tensor] = None, out=None,
+                  stored_logits=False):
     """One call computing (loss, lse, dx, dw, db) with grad_output = 1.
     ``workspace`` and ``out`` (a tuple of preallocated loss, lse, dx, dw, db)
     let a caller reuse buffers across steps; ``token_chunk`` and ``dw_bf16``
-    as for ``backward``."""
+    as for ``backward``.  ``stored_logits`` selects the three-contraction
+    schedule (each token chunk's logits kept instead of recomputed)."""
     x2, w2, t2, b2 = _prepare(x, weight, target, bias)
     n, d = x2.shape
     v = w2.shape[0]
     p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
                     reduction, vocab_slice, token_chunk, dw_bf16)
     dev = x2.device
-    nbytes = _lib.workspace_size(p, True)
+    nbytes = _lib.stored_workspace_size(p) if stored_logits else _lib.workspace_size(p, True)
     if workspace is None:
-        workspace, nbytes = _workspace(p, True, dev)
+        if nbytes == 0:
+            raise _lib.FLCEError(_lib.FLCE_ERR_INVALID_ARGUMENT, "workspace size")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     elif workspace.numel() < nbytes:
         raise _lib.FLCEError(_lib.FLCE_ERR_WORKSPACE_TOO_SMALL, "fused_fwd_bwd")
     else:
@@ -169,9 +175,10 @@ def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoo
         db = torch.empty(v, dtype=torch.float32, device=dev) if b2 is not None else None
     else:
         loss, lse, dx, dw, db = out
-    _check(_lib.fused_fwd_bwd(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(loss), _ptr(lse),
-                              _ptr(dx), _ptr(dw), _ptr(db), _ptr(workspace), nbytes, _stream(dev)),
-           "flce_fused_fwd_bwd")
+    call = _lib.fused_fwd_bwd_stored if stored_logits else _lib.fused_fwd_bwd
+    _check(call(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(loss), _ptr(lse), _ptr(dx), _ptr(dw),
+                _ptr(db), _ptr(workspace), nbytes, _stream(dev)),
+           "flce_fused_fwd_bwd_stored" if stored_logits else "flce_fused_fwd_bwd")
     return loss[0], lse, dx, dw, db
 
 

@@ -273,6 +273,8 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.zt = reinterpret_cast<float*>(at(ws, L.zt));
   a.part_b = reinterpret_cast<float*>(at(ws, L.part_b));
   a.part_i = reinterpret_cast<int32_t*>(at(ws, L.part_i));
+  a.row0 = 0;
+  a.cap = p.n;
   const bool b = bias != nullptr, c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
   const int key = (b ? 1 : 0) | (c ? 2 : 0) | (z ? 4 : 0);
   if (metrics)
@@ -476,6 +478,203 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
   if (p.n > 0)
     hipLaunchKernelGGL((flce::k_zero_ignored_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0,
                        s, static_cast<T*>(dx), p.d, targets, p.ignore_index);
+  return launched();
+}
+
+// ------------------------------------------------- stored-logits variant
+// Forward and backward with three contractions instead of four: each token
+// chunk's raw logits are kept (fp32, register order) by the forward GEMM and
+// read back by the G kernel instead of being recomputed; dX then contracts
+// over the whole vocabulary at once.  6 N D V FLOPs, at the price of the
+// chunk's logits in the workspace (C x V x 4 bytes).
+constexpr int64_t kStoredChunk = 8192;   // default token chunk of the stored variant
+
+struct StoredLayout {
+  Layout base;             // ctl, rows, tc, xc, forward partials (shared with the other calls)
+  int64_t chunk, n_tok_chunks, v_tiles, vpad, ldg, ldt;
+  int64_t zs, g, gt, xt, wt, lsep, end;
+};
+
+StoredLayout make_stored_layout(const flce_params& p) {
+  StoredLayout S{};
+  S.base = make_layout(p);
+  const Layout& L = S.base;
+  const int64_t all = round_up(p.n > 0 ? p.n : 1, tile::kN);
+  S.chunk = round_up(p.token_chunk > 0 ? p.token_chunk : kStoredChunk, tile::kN);
+  if (S.chunk > all) S.chunk = all;
+  S.n_tok_chunks = p.n > 0 ? cdiv(p.n, S.chunk) : 1;
+  S.v_tiles = L.v_tiles;
+  S.vpad = L.v_tiles * tile::kM;
+  S.ldg = S.vpad + kPitchPad;
+  S.ldt = S.chunk + kPitchPad;
+  int64_t off = L.fwd_end;
+  S.zs = off;    off = round_up(off + 4 * S.chunk * S.vpad, kAlign);
+  S.g = off;     off = round_up(off + L.elem * S.chunk * S.ldg, kAlign);
+  S.gt = off;    off = round_up(off + L.elem * S.vpad * S.ldt, kAlign);
+  S.xt = off;    off = round_up(off + L.elem * p.d * S.ldt, kAlign);
+  S.wt = off;    off = round_up(off + L.elem * p.d * S.ldg, kAlign);
+  S.lsep = off;  off = round_up(off + 4 * p.n, kAlign);
+  S.end = off;
+  return S;
+}
+
+template <typename T>
+flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const void* x, const void* w,
+                             const void* bias, const int32_t* targets, float* loss, float* lse, void* dx,
+                             void* dw, float* dbias, void* ws, hipStream_t s) {
+  const Layout& L = S.base;
+  Ctl* ctl = reinterpret_cast<Ctl*>(at(ws, L.ctl));
+  const bool mean = p.reduction == FLCE_REDUCTION_MEAN;
+  int32_t* rows = reinterpret_cast<int32_t*>(at(ws, L.rows));
+  int32_t* tc = reinterpret_cast<int32_t*>(at(ws, L.tc));
+  T* xc = reinterpret_cast<T*>(at(ws, L.xc));
+  float* zs = reinterpret_cast<float*>(at(ws, S.zs));
+  T* g = reinterpret_cast<T*>(at(ws, S.g));
+  T* gt = reinterpret_cast<T*>(at(ws, S.gt));
+  T* xt = reinterpret_cast<T*>(at(ws, S.xt));
+  T* wt = reinterpret_cast<T*>(at(ws, S.wt));
+  float* lsep = reinterpret_cast<float*>(at(ws, S.lsep));
+  const T* W = static_cast<const T*>(w);
+  hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
+                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows);
+  if (p.n > 0)
+    hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
+                       static_cast<const T*>(x), p.d, targets, static_cast<const int32_t*>(rows),
+                       static_cast<const Ctl*>(ctl), xc, tc);
+  // W^T of the whole vocabulary [d][ldg], once
+  transpose<T>(W, p.v, p.d, p.d, wt, p.d, S.vpad, S.ldg, s);
+  const int64_t d_tiles = cdiv(p.d, tile::kM);
+  const int64_t c_tiles = S.chunk / tile::kN;
+  const bool has_bias = bias != nullptr, c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
+  const int fkey = (has_bias ? 1 : 0) | (c ? 2 : 0) | (z ? 4 : 0);
+  double* block_sums = reinterpret_cast<double*>(at(ws, L.block_sums));
+  for (int64_t ci = 0; ci < S.n_tok_chunks; ++ci) {
+    const int64_t c0 = ci * S.chunk;
+    if (p.n > 0) {
+      // forward of the chunk, keeping its raw logits
+      flce::FwdArgs<T> a{};
+      a.x = xc + c0 * p.d;
+      a.w = W;
+      a.bias = static_cast<const T*>(bias);
+      a.targets = tc + c0;
+      a.ctl = ctl;
+      a.n = p.n;
+      a.d = p.d;
+      a.v = p.v;
+      a.softcap = p.softcap;
+      a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
+      a.group = kRasterGroup;
+      a.part_m = reinterpret_cast<float*>(at(ws, L.part_m)) + c0;
+      a.part_d = reinterpret_cast<float*>(at(ws, L.part_d)) + c0;
+      a.part_s = reinterpret_cast<float*>(at(ws, L.part_s)) + c0;
+      a.zt = reinterpret_cast<float*>(at(ws, L.zt)) + c0;
+      a.row0 = c0;
+      a.cap = S.chunk;
+      a.zs = zs;
+      a.zs_vt = S.v_tiles;
+      Layout Lc = L;                     // the chunk's token tiles only
+      Lc.n_tiles = c_tiles;
+      dispatch_fwd<T, false>(a, Lc, fkey, s);
+      // lse, packed lse and row losses of the chunk's rows
+      flce::MergeArgs m{};
+      m.part_m = reinterpret_cast<float*>(at(ws, L.part_m));
+      m.part_d = reinterpret_cast<float*>(at(ws, L.part_d));
+      m.part_s = reinterpret_cast<float*>(at(ws, L.part_s));
+      m.zt = reinterpret_cast<float*>(at(ws, L.zt));
+      m.targets = targets;
+      m.n = p.n;
+      m.v = p.v;
+      m.n_chunks = L.n_chunks;
+      m.ignore_index = p.ignore_index;
+      m.keep_target = 1.0f - p.label_smoothing;
+      m.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
+      m.zloss = p.lse_square_scale;
+      m.lse = lse;
+      m.block_sums = block_sums;
+      m.rows = rows;
+      m.ctl = ctl;
+      m.row0 = c0;
+      m.lsep = lsep;
+      hipLaunchKernelGGL(flce::k_merge, dim3(static_cast<unsigned>(c_tiles)), dim3(256), 0, s, m);
+      // G of the chunk over the whole vocabulary, from the kept logits
+      flce::GArgs<T> ga{};
+      ga.x = xc + c0 * p.d;
+      ga.w = W;
+      ga.bias = static_cast<const T*>(bias);
+      ga.targets = tc + c0;
+      ga.ctl = ctl;
+      ga.lsep = lsep + c0;
+      ga.n = S.chunk;
+      ga.row0 = c0;
+      ga.d = p.d;
+      ga.v = p.v;
+      ga.ignore_index = p.ignore_index;
+      ga.softcap = p.softcap;
+      ga.inv_softcap = a.inv_softcap;
+      ga.keep_target = m.keep_target;
+      ga.eps_over_v = m.eps_over_v;
+      ga.two_s = 2.0f * p.lse_square_scale;
+      ga.v0 = 0;
+      ga.slice_len = p.v;
+      ga.ldg = S.ldg;
+      ga.ldt = S.ldt;
+      ga.g = g;
+      ga.gt = gt;
+      ga.s_tiles = S.v_tiles;
+      ga.group = kRasterGroup;
+      ga.zs = zs;
+      ga.zs_vt = S.v_tiles;
+      const int64_t g_grid = grid8(c_tiles * S.v_tiles);
+      switch ((has_bias ? 1 : 0) | (c ? 2 : 0)) {
+        case 0: launch_g<T, false, false>(ga, g_grid, s); break;
+        case 1: launch_g<T, true, false>(ga, g_grid, s); break;
+        case 2: launch_g<T, false, true>(ga, g_grid, s); break;
+        default: launch_g<T, true, true>(ga, g_grid, s); break;
+      }
+    }
+    // X^T of the chunk; dW over the whole vocabulary, accumulated over chunks
+    transpose<T>(xc + c0 * p.d, S.chunk, p.d, p.d, xt, p.d, S.chunk, S.ldt, s, ctl, c0);
+    Layout Lw = L;
+    Lw.ldt = S.ldt;
+    Lw.chunk = S.chunk;
+    if (p.dw_bf16)
+      launch_dw<T, uint16_t>(xt, gt, p, Lw, 0, p.v, S.vpad, d_tiles, S.v_tiles, c0, ci > 0, ctl,
+                             static_cast<uint16_t*>(dw), s);
+    else
+      launch_dw<T, float>(xt, gt, p, Lw, 0, p.v, S.vpad, d_tiles, S.v_tiles, c0, ci > 0, ctl,
+                          static_cast<float*>(dw), s);
+    if (p.n > 0) {
+      // dX of the chunk in one contraction over the whole vocabulary
+      flce::DxArgs<T> xa{};
+      xa.wt = wt;
+      xa.g = g;
+      xa.n = S.chunk;
+      xa.row0 = c0;
+      xa.d = p.d;
+      xa.kdim = S.vpad;
+      xa.ldg = S.ldg;
+      xa.ctl = ctl;
+      xa.acc_buf = nullptr;              // first and last slice: no running sum
+      xa.rows = rows + c0;
+      xa.dx = static_cast<T*>(dx);
+      xa.first = 1;
+      xa.d_tiles = d_tiles;
+      hipLaunchKernelGGL((flce::k_dx<T, true>), dim3(static_cast<unsigned>(grid8(d_tiles * c_tiles))),
+                         dim3(tile::kThreads), 0, s, xa);
+    }
+    if (has_bias)
+      hipLaunchKernelGGL((flce::k_db<T>), dim3(static_cast<unsigned>(cdiv(p.v, 4))), dim3(256), 0, s,
+                         static_cast<const T*>(gt), S.ldt, S.chunk, int64_t{0}, p.v,
+                         static_cast<const Ctl*>(ctl), dbias, c0, ci > 0 ? 1 : 0);
+  }
+  if (p.n == 0) {
+    fill(loss, 1, 0.f, s);
+    return launched();
+  }
+  hipLaunchKernelGGL(flce::k_loss_final, dim3(1), dim3(256), 0, s, static_cast<const double*>(block_sums),
+                     L.n_merge_blocks, static_cast<const Ctl*>(ctl), mean ? 1 : 0, loss);
+  hipLaunchKernelGGL((flce::k_zero_ignored_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
+                     static_cast<T*>(dx), p.d, targets, p.ignore_index);
   return launched();
 }
 
@@ -739,6 +938,33 @@ flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const v
   st = run_forward<float>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
   if (st != FLCE_OK) return st;
   return run_backward<float>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s, true);
+}
+
+size_t flce_stored_workspace_size(const flce_params* params) {
+  if (check_params(params) != FLCE_OK) return 0;
+  return static_cast<size_t>(make_stored_layout(*params).end);
+}
+
+flce_status flce_fused_fwd_bwd_stored(const flce_params* params, const void* x, const void* w,
+                                      const void* bias, const int32_t* targets, float* loss, float* lse,
+                                      void* dx, void* dw, float* dbias, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  flce_status st = check_params(params);
+  if (st != FLCE_OK) return st;
+  const flce_params& p = *params;
+  if ((st = check_inputs(p, x, w, bias, targets)) != FLCE_OK) return st;
+  if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p.reduction == FLCE_REDUCTION_NONE) return FLCE_ERR_UNSUPPORTED;
+  if (p.n > 0 && (!lse || !aligned(lse, 4) || !dx || !aligned(dx, 16))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!dw || !aligned(dw, 16)) return FLCE_ERR_INVALID_ARGUMENT;
+  if (bias && (!dbias || !aligned(dbias, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  const StoredLayout S = make_stored_layout(p);
+  if ((st = check_ws(ws, ws_bytes, S.end)) != FLCE_OK) return st;
+  if ((st = check_device()) != FLCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.dtype == FLCE_DTYPE_BF16)
+    return run_fused_stored<uint16_t>(p, S, x, w, bias, targets, loss, lse, dx, dw, dbias, ws, s);
+  return run_fused_stored<float>(p, S, x, w, bias, targets, loss, lse, dx, dw, dbias, ws, s);
 }
 
 flce_status flce_check_status(const void* ws, void* stream) {

@@ -192,7 +192,20 @@ struct FwdArgs {
   int32_t* part_i;        // [n_chunks, n] its lowest vocabulary index
   float* zt;              // [n] target logit, by packed row
   const Ctl* ctl;         // n_valid: rows of x (packed) that take part
+  int64_t row0, cap;      // token chunk: first packed row (pointers above start there), capacity
+  float* zs;              // null, or the raw logit tiles of the chunk, stored in register order
+  int64_t zs_vt;          // vocabulary tiles per token tile in zs
 };
+
+// Raw logits of one 256 x 256 tile stored for a later pass, in the
+// accumulators' register order: tile (nt, vt) owns 64 Ki floats at
+// (nt * vt_count + vt) * 65536, wave w's register group i = (mb, nb, q) the
+// 1 KiB at (w * 64 + i) * 256, lane l's four values at 4 l.  Every store and
+// load of it is one contiguous 1 KiB wave access.
+__device__ __forceinline__ float4* stored_tile(float* zs, int64_t nt, int64_t vt, int64_t vt_count,
+                                               int wave, int lane) {
+  return reinterpret_cast<float4*>(zs + (nt * vt_count + vt) * 65536) + wave * 4096 + lane;
+}
 
 // max without NaN canonicalisation (logits here are finite or -inf)
 __device__ __forceinline__ float fmax_fast(float a, float b) { return a > b ? a : b; }
@@ -290,7 +303,7 @@ void k_fwd(FwdArgs<T> a) {
   // wave-row exchange of the final partials; gemm_tile has released `lds` by then
   float (*xch)[2][4][32] = reinterpret_cast<float (*)[2][4][32]>(lds);
   // token tiles of the valid rows only, spread evenly over the XCDs
-  const int64_t nv = a.ctl->n_valid;
+  const int64_t nv = chunk_valid(a.ctl, a.row0, a.cap);
   const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;
   int64_t L;
   if (!xcd_logical_n(blockIdx.x, n_tiles * a.n_chunks, L)) return;   // whole workgroup leaves
@@ -328,6 +341,17 @@ void k_fwd(FwdArgs<T> a) {
     f32x16 acc[4][4];
     gemm_tile<T, true>(A, B, v0, n0, a.d, lds, acc);
     if (vt + 1 < vt_end) gemm_prefetch(A, B, v0 + tile::kM, n0, lds);
+    if (a.zs) {   // logits kept for the stored-logits backward
+      float4* z = stored_tile(a.zs, nt, vt, a.zs_vt, wave, lane);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            z[((mb * 4 + nb) * 4 + q) * 64] = float4{acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
+                                                     acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
+    }
     // tile-local vocabulary row of (mb, r) = vw + mb*32 + 8(r/4) + r%4
     const int vw = wm * 128 + 4 * (lane >> 5);
     const int vlim = a.v - v0 < tile::kM ? static_cast<int>(a.v - v0) : tile::kM;
@@ -404,16 +428,19 @@ struct MergeArgs {
   float* lse;           // [n]
   float* row_loss;      // [n] or null
   float* loss_rows;     // [n] or null (reduction none)
-  double* block_sums;   // [gridDim.x]
+  double* block_sums;   // [n / 256]
   const int32_t* rows;  // packed row -> row
   const Ctl* ctl;
+  int64_t row0;         // this launch covers rows [row0, row0 + 256 gridDim.x)
+  float* lsep;          // null, or [n] lse by packed row
 };
 
 // lse = (m + log2 d) ln 2; row loss = lse - (1-eps) z_t - (eps/V) sum z + s lse^2
 // on valid rows, 0 elsewhere.
 __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   __shared__ double red[256];
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (a.row0 + static_cast<int64_t>(blockIdx.x) * 256 >= a.n) return;   // whole block past the batch
+  const int64_t j = a.row0 + static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t nv = a.ctl->n_valid;
   double row = 0.0;
   if (j < nv) {                      // packed row j: partials, target logit, sum z by packed index
@@ -426,6 +453,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
     const float rl = lse - a.keep_target * a.zt[j] - a.eps_over_v * s + a.zloss * lse * lse;
     const int64_t r = a.rows[j];
     a.lse[r] = lse;
+    if (a.lsep) a.lsep[j] = lse;
     if (a.row_loss) a.row_loss[r] = rl;
     if (a.loss_rows) a.loss_rows[r] = rl;
     row = rl;
@@ -460,7 +488,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
     if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.block_sums[blockIdx.x] = red[0];
+  if (threadIdx.x == 0) a.block_sums[a.row0 / 256 + blockIdx.x] = red[0];
 }
 
 // block_sums[b] = sum of vals [256 b, 256 b + 256) in double, fixed order.
@@ -567,6 +595,8 @@ struct GArgs {
   int64_t s_tiles, group;   // vocabulary tiles of the slice; raster group
   int64_t row0;         // token chunk: its first packed row (x, targets, lsep start there)
   const Ctl* ctl;
+  const float* zs;      // null, or the chunk's raw logit tiles (see stored_tile): read, not recomputed
+  int64_t zs_vt;        // vocabulary tiles per token tile in zs (the slice is then all of V)
 };
 
 __device__ __forceinline__ void store1(uint16_t* p, float a) {
@@ -743,10 +773,26 @@ void k_bwd_g(GArgs<T> a) {
     lse_t[nb] = a.lsep[j];
   }
 
-  const Operand<T> A{a.w + a.v0 * a.d, a.d, a.v - a.v0, a.d};
-  const Operand<T> B{a.x, a.d, nv, a.d};       // packed valid rows
   f32x16 acc[4][4];
-  gemm_tile(A, B, vl0, n0, a.d, lds, acc);
+  if (a.zs) {
+    const float4* z = stored_tile(const_cast<float*>(a.zs), nt, st, a.zs_vt, wave, lane);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = z[((mb * 4 + nb) * 4 + q) * 64];
+          acc[mb][nb][4 * q] = v.x;
+          acc[mb][nb][4 * q + 1] = v.y;
+          acc[mb][nb][4 * q + 2] = v.z;
+          acc[mb][nb][4 * q + 3] = v.w;
+        }
+  } else {
+    const Operand<T> A{a.w + a.v0 * a.d, a.d, a.v - a.v0, a.d};
+    const Operand<T> B{a.x, a.d, nv, a.d};       // packed valid rows
+    gemm_tile(A, B, vl0, n0, a.d, lds, acc);
+  }
 
   const int vw = wm * 128 + 4 * (lane >> 5);              // tile-local v of (mb = 0, r = 0)
   const int vlim = a.slice_len - vl0 < tile::kM ? static_cast<int>(a.slice_len - vl0) : tile::kM;

@@ -405,3 +405,54 @@ def test_token_chunks_llama3_seq():
     dwa, dwb = a["dw_raw"].double(), b["dw_raw"].double()
     rel = (torch.linalg.norm(dwa - dwb) / torch.linalg.norm(dwb)).item()
     assert rel <= 4e-3, rel
+
+
+# ------------------------------------------------- stored-logits schedule
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,d,v,chunk,feats", [
+    (1000, 136, 1000, 256, dict(label_smoothing=0.05, lse_square_scale=1e-3)),
+    (700, 64, 4097, 512, dict(softcap=3.0)),
+    (300, 264, 257, 0, dict(label_smoothing=0.1, reduction="sum")),
+    (1, 8, 1, 0, dict()),
+])
+def test_stored_logits(dtype, n, d, v, chunk, feats):
+    """Three contractions (logits kept per token chunk): every output against
+    the oracle; loss and lse bit for bit those of the recompute schedule (the
+    forward is the same)."""
+    inp = small_problem(n, d, v, dtype, bias=True, seed=n + v + 1)
+    o = O.LossOptions(**feats)
+    banner(f"stored logits {dtype} n={n} d={d} v={v} chunk={chunk} {feats}")
+    got = _fused_opts(inp, dtype, o, stored_logits=True, token_chunk=chunk)
+    U.compare_full(inp, dtype, o, got=got)
+    ref = _fused_opts(inp, dtype, o)
+    assert got["loss"] == ref["loss"] and np.array_equal(got["lse"], ref["lse"])
+
+
+def test_stored_logits_empty_and_ignored():
+    for n in (0, 40):
+        inp = small_problem(n, 64, 300, "bf16", bias=True, seed=5)
+        inp["targets"][:] = IGN
+        got = _fused_opts(inp, "bf16", O.LossOptions(), stored_logits=True)
+        assert got["loss"] == 0.0
+        assert np.all(got["dx"] == 0) and np.all(got["dw"] == 0) and np.all(got["db"] == 0)
+
+
+@pytest.mark.timeout(600)
+def test_stored_logits_llama3_seq():
+    """One Llama-3-8B sequence: the stored-logits schedule (chunks of 4096, so
+    dW accumulates) against the recompute schedule; G is the same bf16 tensor
+    in both, so dX and dW differ only by fp32 summation order."""
+    wl = W.WORKLOADS["llama3_8b_seq"]
+    banner(f"stored logits {wl}")
+    inp = W.generate(wl)
+    o = U.options(wl)
+    a = _fused_opts(inp, wl.dtype, o, to_host=False, stored_logits=True, token_chunk=4096)
+    b = _fused_opts(inp, wl.dtype, o, to_host=False)
+    assert a["loss"] == b["loss"] and np.array_equal(a["lse"], b["lse"])
+    # dX leaves in bf16, where an fp32 difference in the last bits can flip an
+    # element by one bf16 ulp (2^-8): a looser bound than for the fp32 dW
+    for k, bound in (("dx_raw", 1e-3), ("dw_raw", 1e-4)):
+        x1, x2 = a[k].double(), b[k].double()
+        rel = (torch.linalg.norm(x1 - x2) / torch.linalg.norm(x2)).item()
+        assert rel <= bound, (k, rel)
