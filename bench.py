@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--token-chunk", type=int, default=0,
                     help="backward over this many packed rows at a time (0 = whole batch)")
     ap.add_argument("--dw-bf16", action="store_true", help="dW in bf16 instead of fp32")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the extra measurement of the stored-logits schedule")
     ap.add_argument("--stored-logits", action="store_true",
                     help="three-contraction schedule: logits kept per token chunk, not recomputed "
                          "(6 N D V FLOPs; the MFMA fractions are then quoted against 6 N D V)")
@@ -227,6 +229,10 @@ def main():
     tokens_per_s = wl.n / (ms * 1e-3)
     traffic = measured_traffic(wl.name)
 
+    variants = None
+    if not args.no_variants and not args.stored_logits and wl.dtype == "bf16":
+        variants = {"stored_logits": bench_stored_variant(args, wl, x, w, t, b, opts, dev, n_valid)}
+
     cpu = None
     if args.cpu_rows > 0:
         log(f"cpu oracle baseline on {args.cpu_rows} rows")
@@ -277,7 +283,59 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if variants:
+        result["variants"] = variants
     print(json.dumps(result), flush=True)
+
+
+def bench_stored_variant(args, wl, x, w, t, b, opts, dev, n_valid):
+    """The same workload through the three-contraction schedule (each token
+    chunk's logits kept, not recomputed): reported beside the headline, never
+    as it, with its own FLOP count (6 N D V) and peak memory."""
+    import torch
+    from linear_cross_entropy_bf16_amd import api
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    inputs = sum(a.numel() * a.element_size() for a in (x, w, t, b) if a is not None)
+    nbytes = api.workspace_bytes(wl.n, wl.d, wl.v, x.dtype, True, stored_logits=True, **opts)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = (torch.empty(1, dtype=torch.float32, device=dev),
+           torch.empty(wl.n, dtype=torch.float32, device=dev),
+           torch.empty((wl.n, wl.d), dtype=x.dtype, device=dev),
+           torch.empty((wl.v, wl.d), dtype=torch.bfloat16 if opts.get("dw_bf16") else torch.float32,
+                       device=dev),
+           torch.empty(wl.v, dtype=torch.float32, device=dev) if b is not None else None)
+
+    def step():
+        api.fused_fwd_bwd(x, w, t, b, workspace=ws, out=out, stored_logits=True, **opts)
+
+    step()
+    steps = max(3, args.steps // 2)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    peak = PEAK_BF16_TFLOPS
+    tflops = 6.0 * wl.n * wl.d * wl.v / (ms * 1e-3) / 1e12
+    tflops_valid = 6.0 * n_valid * wl.d * wl.v / (ms * 1e-3) / 1e12
+    log(f"stored-logits schedule: {ms:.3f} ms/step")
+    res = {"schedule": "stored logits (6 N D V: forward GEMM keeps each 8192-token chunk's logits, "
+                       "no recompute)", "steps": steps, "ms_per_step": round(ms, 3),
+           "tokens_per_s": round(wl.n / (ms * 1e-3), 1),
+           "vs_baseline": round(wl.n / (ms * 1e-3) / PAGES_TOKENS_PER_S, 4)
+           if wl.name == "llama3_8b_batch8" else None,
+           "mfma_frac_6ndv": round(tflops / peak, 4), "mfma_frac_6ndv_valid_rows": round(tflops_valid / peak, 4),
+           # this schedule's own peak: its buffers on top of the inputs
+           "peak_hbm_bytes": int(torch.cuda.max_memory_allocated(dev) - base) + inputs,
+           "workspace_bytes": int(nbytes), "loss": float(out[0].item())}
+    del ws, out
+    return res
 
 
 def cpu_baseline_ce(wl, inp, max_rows: int):
