@@ -193,7 +193,7 @@ void fill(float* p, int64_t count, float value, hipStream_t s) {
 int64_t grid8(int64_t tiles) { return round_up(tiles, 8); }
 
 // ----------------------------------------------------------------- forward
-template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kArgmax>
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kArgmax, bool kStore>
 void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
   if (L.main_chunks > 0) {
     flce::FwdArgs<T> m = a;
@@ -202,7 +202,7 @@ void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
     m.chunk_base = 0;
     m.n_chunks = L.main_chunks;
     m.tiles_per_chunk = L.tiles_per_chunk;
-    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, false, kArgmax>),
+    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, false, kArgmax, kStore>),
                        dim3(static_cast<unsigned>(grid8(L.n_tiles * m.n_chunks))),
                        dim3(tile::kThreads), 0, s, m);
   }
@@ -213,22 +213,23 @@ void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
     t.chunk_base = L.main_chunks;
     t.n_chunks = 1;
     t.tiles_per_chunk = 1;
-    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, true, kArgmax>),
+    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, true, kArgmax, kStore>),
                        dim3(static_cast<unsigned>(grid8(L.n_tiles))), dim3(tile::kThreads), 0, s, t);
   }
 }
 
-template <typename T, bool kArgmax>
+// kStore (the stored-logits schedule) requires a.zs; it never combines with kArgmax.
+template <typename T, bool kArgmax, bool kStore = false>
 void dispatch_fwd(const flce::FwdArgs<T>& a, const Layout& L, int key, hipStream_t s) {
   switch (key) {
-    case 0: launch_fwd<T, false, false, false, kArgmax>(a, L, s); break;
-    case 1: launch_fwd<T, true, false, false, kArgmax>(a, L, s); break;
-    case 2: launch_fwd<T, false, true, false, kArgmax>(a, L, s); break;
-    case 3: launch_fwd<T, true, true, false, kArgmax>(a, L, s); break;
-    case 4: launch_fwd<T, false, false, true, kArgmax>(a, L, s); break;
-    case 5: launch_fwd<T, true, false, true, kArgmax>(a, L, s); break;
-    case 6: launch_fwd<T, false, true, true, kArgmax>(a, L, s); break;
-    default: launch_fwd<T, true, true, true, kArgmax>(a, L, s); break;
+    case 0: launch_fwd<T, false, false, false, kArgmax, kStore>(a, L, s); break;
+    case 1: launch_fwd<T, true, false, false, kArgmax, kStore>(a, L, s); break;
+    case 2: launch_fwd<T, false, true, false, kArgmax, kStore>(a, L, s); break;
+    case 3: launch_fwd<T, true, true, false, kArgmax, kStore>(a, L, s); break;
+    case 4: launch_fwd<T, false, false, true, kArgmax, kStore>(a, L, s); break;
+    case 5: launch_fwd<T, true, false, true, kArgmax, kStore>(a, L, s); break;
+    case 6: launch_fwd<T, false, true, true, kArgmax, kStore>(a, L, s); break;
+    default: launch_fwd<T, true, true, true, kArgmax, kStore>(a, L, s); break;
   }
 }
 
@@ -574,7 +575,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       a.zs_vt = S.v_tiles;
       Layout Lc = L;                     // the chunk's token tiles only
       Lc.n_tiles = c_tiles;
-      dispatch_fwd<T, false>(a, Lc, fkey, s);
+      dispatch_fwd<T, false, true>(a, Lc, fkey, s);
       // lse, packed lse and row losses of the chunk's rows
       flce::MergeArgs m{};
       m.part_m = reinterpret_cast<float*>(at(ws, L.part_m));

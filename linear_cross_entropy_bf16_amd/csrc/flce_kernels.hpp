@@ -295,8 +295,10 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
 // kMasked: this launch covers the one partial vocabulary tile (V mod 256 rows);
 // the main launch covers whole tiles only and carries no masking code.
 // kArgmax: also the largest logit of each row and its lowest index (predicted
-// tokens, token accuracy).
-template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked, bool kArgmax>
+// tokens, token accuracy).  kStore: also keep the raw logit tiles in a.zs (a
+// separate instantiation: the store code costs the plain forward registers).
+template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kMasked, bool kArgmax,
+          bool kStore = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fwd(FwdArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
@@ -341,17 +343,6 @@ void k_fwd(FwdArgs<T> a) {
     f32x16 acc[4][4];
     gemm_tile<T, true>(A, B, v0, n0, a.d, lds, acc);
     if (vt + 1 < vt_end) gemm_prefetch(A, B, v0 + tile::kM, n0, lds);
-    if (a.zs) {   // logits kept for the stored-logits backward
-      float4* z = stored_tile(a.zs, nt, vt, a.zs_vt, wave, lane);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            z[((mb * 4 + nb) * 4 + q) * 64] = float4{acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
-                                                     acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
-    }
     // tile-local vocabulary row of (mb, r) = vw + mb*32 + 8(r/4) + r%4
     const int vw = wm * 128 + 4 * (lane >> 5);
     const int vlim = a.v - v0 < tile::kM ? static_cast<int>(a.v - v0) : tile::kM;
@@ -362,6 +353,19 @@ void k_fwd(FwdArgs<T> a) {
     fwd_tile_epilogue<T, kBias, kSoftcap, kSumZ, kMasked, kArgmax>(a, acc, v0, vw, vlim, tgt, n0, wn,
                                                                    lane, m_run, d_run, s_run, b_run,
                                                                    i_run);
+    // after the epilogue: the accumulators are still intact, and the store
+    // adds no registers to the epilogue
+    if constexpr (kStore) {   // logits kept for the stored-logits backward
+      float4* z = stored_tile(a.zs, nt, vt, a.zs_vt, wave, lane);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            z[((mb * 4 + nb) * 4 + q) * 64] = float4{acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
+                                                     acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
+    }
   }
 
   // Combine the two lane halves (same token, disjoint vocabulary rows) ...
