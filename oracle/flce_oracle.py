@@ -41,6 +41,11 @@ displayed equation of the first page is missing from the extracted text):
   n_valid = 0 the loss and every gradient are 0.
 * ignored rows report lse = 0 and row_loss = 0.
 * grad_output g scales every gradient; scale = g / n_valid (mean) or g (sum).
+* class weights w [V] (option ``class_weight``; page "[CuteDSL] FLCE",
+  Summary, names ce_weight): torch's weighted cross-entropy, i.e. row loss
+  (1-eps) w_t (lse - z_t) + (eps/V) sum_c w_c (lse - z_c), the mean taken over
+  sum_valid w_t instead of n_valid; the z-loss term is weighted by w_t too (so
+  w = 1 is the unweighted loss).
 
 Parity status of each function is stated in its docstring; every function is
 pinned by tests in ``tests/test_oracle_pins.py`` except where a docstring says
@@ -63,6 +68,7 @@ class LossOptions:
     lse_square_scale: float = 0.0
     softcap: float = 0.0
     reduction: str = "mean"
+    class_weight: object = None      # [V] per-class weights, or None
 
 
 # --------------------------------------------------------------------- inputs
@@ -122,6 +128,16 @@ def valid_rows(targets: np.ndarray, opts: LossOptions) -> np.ndarray:
     return np.asarray(targets) != opts.ignore_index
 
 
+def mean_denominator(targets: np.ndarray, opts: LossOptions) -> float:
+    """What 'mean' divides by: n_valid, or with class weights the sum of the
+    valid rows' target weights."""
+    valid = valid_rows(targets, opts)
+    if opts.class_weight is None:
+        return int(valid.sum())
+    w = np.asarray(opts.class_weight, dtype=np.float64)
+    return float(w[np.asarray(targets)[valid]].sum())
+
+
 def check_targets(targets: np.ndarray, v: int, opts: LossOptions) -> None:
     t = np.asarray(targets)
     bad = (t != opts.ignore_index) & ((t < 0) | (t >= v))
@@ -140,6 +156,15 @@ def row_losses(z: np.ndarray, lse: np.ndarray, targets: np.ndarray,
     t = np.where(valid, targets, 0)
     zt = z[np.arange(n), t]
     eps = opts.label_smoothing
+    if opts.class_weight is not None:
+        w = np.asarray(opts.class_weight, dtype=np.float64)
+        wt = w[t]
+        out = (1.0 - eps) * wt * (lse - zt)
+        if eps != 0.0:
+            out = out + (eps / v) * (w.sum() * lse - z @ w)
+        if opts.lse_square_scale != 0.0:
+            out = out + opts.lse_square_scale * wt * lse * lse
+        return np.where(valid, out, 0.0)
     out = lse - (1.0 - eps) * zt
     if eps != 0.0:
         out = out - (eps / v) * z.sum(axis=1)
@@ -160,6 +185,21 @@ def grad_logits(z: np.ndarray, lse: np.ndarray, targets: np.ndarray,
     t = np.where(valid, targets, 0)
     p = np.exp(z - lse[:, None])
     s = opts.lse_square_scale
+    if opts.class_weight is not None:
+        # d/dz_c of the weighted row: p_c [(1-eps) w_t + (eps/V) sum w + 2 s w_t lse]
+        #   - (1-eps) w_t [c = t] - (eps/V) w_c
+        w = np.asarray(opts.class_weight, dtype=np.float64)
+        wt = w[t]
+        eps = opts.label_smoothing
+        fac = (1.0 - eps) * wt + (eps / v) * w.sum() + 2.0 * s * wt * lse
+        g = p * fac[:, None]
+        g[np.arange(n), t] -= (1.0 - eps) * wt
+        if eps != 0.0:
+            g -= (eps / v) * w[None, :]
+        if opts.softcap > 0.0:
+            g *= 1.0 - (z / opts.softcap) ** 2
+        g[~valid] = 0.0
+        return g
     g = p * (1.0 + 2.0 * s * lse)[:, None] if s != 0.0 else p
     g[np.arange(n), t] -= (1.0 - opts.label_smoothing)
     if opts.label_smoothing != 0.0:
@@ -207,13 +247,14 @@ class Result:
 def forward(x, w, bias, targets, opts: LossOptions,
             n_valid: Optional[int] = None, row_block: int = ROW_BLOCK) -> Result:
     """Loss, per-row LSE and per-row loss.  ``n_valid`` overrides the mean
-    denominator (sampled rows of a larger batch use the full batch's count)."""
+    denominator (sampled rows of a larger batch use the full batch's count,
+    or with class weights its sum of target weights)."""
     x, w, bias = to_f64(x), to_f64(w), to_f64(bias)
     targets = np.asarray(targets)
     check_targets(targets, w.shape[0], opts)
     n = x.shape[0]
     valid = valid_rows(targets, opts)
-    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    nv = mean_denominator(targets, opts) if n_valid is None else n_valid
     lse = np.zeros(n)
     rl = np.zeros(n)
     for r0 in range(0, n, row_block):
@@ -237,7 +278,7 @@ def forward_backward(x, w, bias, targets, opts: LossOptions,
     n, d = x.shape
     v = w.shape[0]
     valid = valid_rows(targets, opts)
-    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    nv = mean_denominator(targets, opts) if n_valid is None else n_valid
     scale = grad_scale(opts, nv, grad_output)
     lse = np.zeros(n)
     rl = np.zeros(n)
@@ -267,7 +308,7 @@ def dw_blocks(x, w, bias, targets, opts: LossOptions, grad_output: float = 1.0,
     x, w, bias = to_f64(x), to_f64(w), to_f64(bias)
     targets = np.asarray(targets)
     valid = valid_rows(targets, opts)
-    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    nv = mean_denominator(targets, opts) if n_valid is None else n_valid
     scale = grad_scale(opts, nv, grad_output)
     v = w.shape[0]
     z = logits(x, w, bias, opts.softcap)
@@ -300,7 +341,7 @@ def cross_entropy_on_logits(r, targets, opts: LossOptions, grad_output: float = 
     n, v = r.shape
     check_targets(targets, v, opts)
     valid = valid_rows(targets, opts)
-    nv = int(valid.sum()) if n_valid is None else int(n_valid)
+    nv = mean_denominator(targets, opts) if n_valid is None else n_valid
     scale = grad_scale(opts, nv, grad_output) if want_grad else 0.0
     lse = np.zeros(n)
     rl = np.zeros(n)

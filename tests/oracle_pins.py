@@ -516,6 +516,71 @@ def pin_predicted_tokens(O):
     assert np.array_equal(pl, pred) and al == acc
 
 
+# ------------------------------------------------- class weights
+
+def pin_class_weight_torch(O):
+    """Per-class weights without softcap and z-loss are torch's weighted
+    cross-entropy of the materialised logits: loss (mean over the sum of the
+    valid rows' target weights, sum, none; with label smoothing) and autograd
+    gradients through the linear layer, float64 on the CPU."""
+    import torch
+    import torch.nn.functional as F
+
+    x, w, b, t = _problem(n=36, d=10, v=23, bias=True, ignore=4, seed=13)
+    cw = np.random.default_rng(3).uniform(0.1, 3.0, w.shape[0])
+    for eps in (0.0, 0.15):
+        for red in ("mean", "sum", "none"):
+            o = _opts(O, label_smoothing=eps, reduction=red, class_weight=cw)
+            xt = torch.tensor(x, requires_grad=True)
+            wt = torch.tensor(w, requires_grad=True)
+            bt = torch.tensor(b, requires_grad=True)
+            lt = F.cross_entropy(xt @ wt.T + bt, torch.tensor(t, dtype=torch.long),
+                                 weight=torch.tensor(cw), ignore_index=IGN, label_smoothing=eps,
+                                 reduction=red)
+            if red == "none":
+                r = O.forward(x, w, b, t, o)
+                assert np.allclose(r.loss, lt.detach().numpy(), rtol=0, atol=1e-13)
+                continue
+            lt.backward()
+            r = O.forward_backward(x, w, b, t, o)
+            assert abs(r.loss - lt.item()) <= 1e-13 * max(1.0, abs(lt.item())), (eps, red)
+            assert np.allclose(r.dx, xt.grad.numpy(), rtol=0, atol=1e-14)
+            assert np.allclose(r.dw, wt.grad.numpy(), rtol=0, atol=1e-14)
+            assert np.allclose(r.db, bt.grad.numpy(), rtol=0, atol=1e-14)
+
+
+def pin_class_weight_unit_and_fd(O, directions=8, seed=29):
+    """Unit weights give the unweighted problem exactly, for every feature
+    combination; with random weights, softcap and z-loss (outside torch's
+    reach) central differences along X and W agree with the gradient."""
+    x, w, b, t = _problem(n=40, d=12, v=50, bias=True, ignore=5, seed=seed)
+    ones = np.ones(w.shape[0])
+    for feats in FEATURE_SETS:
+        a = O.forward_backward(x, w, b, t, _opts(O, **feats))
+        c = O.forward_backward(x, w, b, t, _opts(O, class_weight=ones, **feats))
+        assert abs(a.loss - c.loss) <= 1e-13 * max(1.0, abs(a.loss)), feats
+        assert np.allclose(a.dx, c.dx, rtol=0, atol=1e-15) and np.allclose(a.dw, c.dw, rtol=0, atol=1e-15)
+    rng = np.random.default_rng(seed)
+    cw = rng.uniform(0.2, 2.5, w.shape[0])
+    h = 1e-5
+    for feats in (dict(softcap=2.0, lse_square_scale=3e-2, label_smoothing=0.2),
+                  dict(lse_square_scale=1e-2, reduction="sum"), dict(label_smoothing=0.1)):
+        o = _opts(O, class_weight=cw, **feats)
+        r = O.forward_backward(x, w, b, t, o)
+        for k in range(directions):
+            if k % 2 == 0:
+                dv = rng.standard_normal(x.shape)
+                dv /= np.linalg.norm(dv)
+                fd = (O.forward(x + h * dv, w, b, t, o).loss - O.forward(x - h * dv, w, b, t, o).loss) / (2 * h)
+                an, gn = float((r.dx * dv).sum()), np.linalg.norm(r.dx)
+            else:
+                dv = rng.standard_normal(w.shape)
+                dv /= np.linalg.norm(dv)
+                fd = (O.forward(x, w + h * dv, b, t, o).loss - O.forward(x, w - h * dv, b, t, o).loss) / (2 * h)
+                an, gn = float((r.dw * dv).sum()), np.linalg.norm(r.dw)
+            assert abs(fd - an) <= 1e-7 * gn + 1e-12, (feats, k, fd, an)
+
+
 ALL_PINS = [
     pin_uniform_logits, pin_single_class, pin_two_classes, pin_gradient_row_sums,
     pin_shift_invariance, pin_batch_additivity, pin_vocab_permutation,
@@ -523,4 +588,5 @@ ALL_PINS = [
     pin_torch_cross_entropy, pin_finite_differences, pin_brute_force,
     pin_gaussian_lse_level, pin_logits_identity_linear, pin_logits_torch,
     pin_logits_finite_differences, pin_megatron_smoothing, pin_predicted_tokens,
+    pin_class_weight_torch, pin_class_weight_unit_and_fd,
 ]

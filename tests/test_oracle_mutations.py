@@ -170,11 +170,36 @@ def mut_accuracy_over_all_rows(m):
     m.token_accuracy = token_accuracy
 
 
+def mut_weighted_mean_over_rows(m):
+    orig = m.mean_denominator
+
+    def mean_denominator(targets, opts):
+        if opts.class_weight is None:
+            return orig(targets, opts)
+        return int(m.valid_rows(targets, opts).sum())           # forgot the weights in the mean
+    m.mean_denominator = mean_denominator
+
+
+def mut_weighted_smoothing_unweighted(m):
+    orig = m.grad_logits
+
+    def grad_logits(z, lse, targets, opts):
+        g = orig(z, lse, targets, opts)
+        if opts.class_weight is not None and opts.label_smoothing:
+            w = np.asarray(opts.class_weight, dtype=np.float64)
+            valid = m.valid_rows(targets, opts)
+            fac = 1.0 - (z / opts.softcap) ** 2 if opts.softcap > 0 else 1.0
+            g = g + (opts.label_smoothing / z.shape[1]) * (w[None, :] - 1.0) * fac * valid[:, None]
+        return g                                                  # eps/V instead of eps w_c / V
+    m.grad_logits = grad_logits
+
+
 MUTATIONS = [mut_drop_smoothing_sum, mut_zloss_grad_sign, mut_no_softcap_derivative,
              mut_target_off_by_one, mut_lse_missing_max, mut_mean_over_all_rows,
              mut_online_no_rescale, mut_smoothing_over_v_minus_1, mut_transposed_dw,
              mut_logits_ignore_softcap, mut_logits_unscaled_grad, mut_megatron_plain_eps,
-             mut_argmax_last_tie, mut_accuracy_over_all_rows]
+             mut_argmax_last_tie, mut_accuracy_over_all_rows, mut_weighted_mean_over_rows,
+             mut_weighted_smoothing_unweighted]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
