@@ -97,6 +97,13 @@ typedef struct flce_params {
                                 not by N, and dW / db accumulate over the chunks */
   int32_t dw_bf16;           /* 0: dW is fp32; 1: dW is bf16 (half the memory; rounded
                                 once per token chunk, as it accumulates in its own dtype) */
+  const float* class_weight; /* NULL, or fp32 [v] per-class weights on the device (the
+                                ce_weight option of the page "[CuteDSL] FLCE", Summary),
+                                with torch's weighted cross-entropy meaning: row loss
+                                (1-eps) w_t (lse - z_t) + (eps/V) sum_v w_v (lse - z_v)
+                                + s w_t lse^2, 'mean' divided by the valid rows' sum of
+                                w_t.  Fused-path calls only; the flce_ce_* calls return
+                                FLCE_ERR_UNSUPPORTED with weights. */
 } flce_params;
 
 /* Bytes of workspace the calls need for these parameters.  with_backward = 0

@@ -43,6 +43,7 @@ class Params(ctypes.Structure):
         ("vocab_slice", ctypes.c_int32),
         ("token_chunk", ctypes.c_int32),
         ("dw_bf16", ctypes.c_int32),
+        ("class_weight", ctypes.c_void_p),
     ]
 
 
@@ -109,15 +110,17 @@ def status_string(status: int) -> str:
 
 
 def make_params(n, d, v, dtype, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0,
-                softcap=0.0, reduction="mean", vocab_slice=0, token_chunk=0, dw_bf16=0) -> Params:
-    """``reduction`` is 'mean', 'sum', 'none' or the raw enum value."""
+                softcap=0.0, reduction="mean", vocab_slice=0, token_chunk=0, dw_bf16=0,
+                class_weight=None) -> Params:
+    """``reduction`` is 'mean', 'sum', 'none' or the raw enum value;
+    ``class_weight`` a device address of fp32 [v] weights, or None."""
     if isinstance(reduction, str):
         if reduction not in REDUCTIONS:
             raise ValueError(f"reduction must be one of {tuple(REDUCTIONS)}, got {reduction!r}")
         reduction = REDUCTIONS[reduction]
     return Params(int(n), int(d), int(v), int(dtype), int(ignore_index), float(label_smoothing),
                   float(lse_square_scale), float(softcap), int(reduction), int(vocab_slice),
-                  int(token_chunk), int(dw_bf16))
+                  int(token_chunk), int(dw_bf16), class_weight)
 
 
 def workspace_size(params: Params, with_backward: bool) -> int:

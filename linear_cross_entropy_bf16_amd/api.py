@@ -64,10 +64,20 @@ def _prepare(x, weight, target, bias):
 
 def make_params(n, d, v, dtype, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0,
                 softcap=0.0, reduction="mean", vocab_slice=0, token_chunk=0,
-                dw_bf16=False) -> _lib.Params:
+                dw_bf16=False, class_weight=None) -> _lib.Params:
+    """``class_weight``: None, or a contiguous fp32 [v] tensor on the device
+    (the caller keeps it alive while the call runs)."""
     return _lib.make_params(n, d, v, _DTYPES[dtype], ignore_index, label_smoothing,
                             lse_square_scale, softcap, reduction, vocab_slice, token_chunk,
-                            1 if dw_bf16 else 0)
+                            1 if dw_bf16 else 0, _ptr(class_weight))
+
+
+def _weights(class_weight, v, device):
+    if class_weight is None:
+        return None
+    if class_weight.numel() != v:
+        raise ValueError(f"class_weight must have V = {v} entries, got {class_weight.numel()}")
+    return class_weight.detach().to(device=device, dtype=torch.float32).reshape(v).contiguous()
 
 
 def workspace_bytes(n, d, v, dtype=torch.bfloat16, with_backward=True, stored_logits=False,
@@ -87,15 +97,16 @@ def _workspace(params, with_backward, device) -> Tuple[torch.Tensor, int]:
 
 def forward(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
             lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
-            check_targets=False, return_metrics=False):
+            check_targets=False, return_metrics=False, class_weight=None):
     """Returns (loss, lse, row_loss): loss is a 0-d tensor ([N] for 'none'),
     lse and row_loss are fp32 [N].  With ``return_metrics`` also the predicted
     tokens (int32 [N], -1 on ignored rows) and the token accuracy (0-d fp32)."""
     x2, w2, t2, b2 = _prepare(x, weight, target, bias)
     n, d = x2.shape
     v = w2.shape[0]
+    cw = _weights(class_weight, v, x2.device)
     p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
-                    reduction, vocab_slice)
+                    reduction, vocab_slice, class_weight=cw)
     dev = x2.device
     ws, nbytes = _workspace(p, False, dev)
     loss = torch.empty(n if reduction == "none" else 1, dtype=torch.float32, device=dev)
@@ -119,7 +130,7 @@ def forward(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=
 
 def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_index=-100,
              label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0, reduction="mean",
-             vocab_slice=0, token_chunk=0, dw_bf16=False):
+             vocab_slice=0, token_chunk=0, dw_bf16=False, class_weight=None):
     """Returns (dx, dw, db): dx in x's dtype, dw fp32 (bf16 with ``dw_bf16``)
     and db fp32 (db None without bias).  grad_output is a device scalar
     (None = 1.0).  ``token_chunk`` > 0 runs the backward over that many packed
@@ -127,8 +138,9 @@ def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_inde
     x2, w2, t2, b2 = _prepare(x, weight, target, bias)
     n, d = x2.shape
     v = w2.shape[0]
+    cw = _weights(class_weight, v, x2.device)
     p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
-                    reduction, vocab_slice, token_chunk, dw_bf16)
+                    reduction, vocab_slice, token_chunk, dw_bf16, cw)
     dev = x2.device
     ws, nbytes = _workspace(p, True, dev)
     g = None
@@ -146,7 +158,7 @@ def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_inde
 def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
                   lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
                   token_chunk=0, dw_bf16=False, workspace: Optional[torch.Tensor] = None, out=None,
-                  stored_logits=False):
+                  stored_logits=False, class_weight=None):
     """One call computing (loss, lse, dx, dw, db) with grad_output = 1.
     ``workspace`` and ``out`` (a tuple of preallocated loss, lse, dx, dw, db)
     let a caller reuse buffers across steps; ``token_chunk`` and ``dw_bf16``
@@ -155,8 +167,9 @@ def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoo
     x2, w2, t2, b2 = _prepare(x, weight, target, bias)
     n, d = x2.shape
     v = w2.shape[0]
+    cw = _weights(class_weight, v, x2.device)
     p = make_params(n, d, v, x2.dtype, ignore_index, label_smoothing, lse_square_scale, softcap,
-                    reduction, vocab_slice, token_chunk, dw_bf16)
+                    reduction, vocab_slice, token_chunk, dw_bf16, cw)
     dev = x2.device
     nbytes = _lib.stored_workspace_size(p) if stored_logits else _lib.workspace_size(p, True)
     if workspace is None:
@@ -188,13 +201,14 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, weight, target, bias, ignore_index, label_smoothing, lse_square_scale,
-                softcap, reduction):
+                softcap, reduction, class_weight=None):
         loss, lse, _ = forward(x, weight, target, bias, ignore_index=ignore_index,
                                label_smoothing=label_smoothing, lse_square_scale=lse_square_scale,
-                               softcap=softcap, reduction=reduction)
+                               softcap=softcap, reduction=reduction, class_weight=class_weight)
         ctx.save_for_backward(x, weight, target, bias, lse)
         ctx.opts = dict(ignore_index=ignore_index, label_smoothing=label_smoothing,
-                        lse_square_scale=lse_square_scale, softcap=softcap, reduction=reduction)
+                        lse_square_scale=lse_square_scale, softcap=softcap, reduction=reduction,
+                        class_weight=class_weight)
         ctx.mark_non_differentiable(lse)
         return loss
 
@@ -206,15 +220,17 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
                                "use 'mean' or 'sum'")
         dx, dw, db = backward(x, weight, target, lse, grad_output=grad_loss, bias=bias, **ctx.opts)
         return (dx.to(x.dtype), dw.to(weight.dtype), None,
-                db.to(bias.dtype) if db is not None else None, None, None, None, None, None)
+                db.to(bias.dtype) if db is not None else None, None, None, None, None, None, None)
 
 
 def linear_cross_entropy(x, weight, target, bias=None, ignore_index=-100, label_smoothing=0.0,
-                         lse_square_scale=0.0, softcap=0.0, reduction="mean"):
+                         lse_square_scale=0.0, softcap=0.0, reduction="mean", class_weight=None):
     """Fused LM-head projection + cross-entropy; differentiable in x, weight
-    and bias (reduction 'mean' or 'sum'; 'none' is forward-only)."""
+    and bias (reduction 'mean' or 'sum'; 'none' is forward-only).
+    ``class_weight``: optional [V] per-class weights (torch's weighted
+    cross-entropy; not differentiated)."""
     return LinearCrossEntropyFunction.apply(x, weight, target, bias, ignore_index, label_smoothing,
-                                            lse_square_scale, softcap, reduction)
+                                            lse_square_scale, softcap, reduction, class_weight)
 
 
 # ------------------------------------------------- cross-entropy on logits

@@ -143,6 +143,7 @@ flce_status check_params(const flce_params* p) {
   if (p->vocab_slice < 0 || p->vocab_slice > (1 << 20)) return FLCE_ERR_INVALID_ARGUMENT;
   if (p->token_chunk < 0 || p->token_chunk > (1 << 22)) return FLCE_ERR_INVALID_ARGUMENT;
   if (p->dw_bf16 != 0 && p->dw_bf16 != 1) return FLCE_ERR_INVALID_ARGUMENT;
+  if (p->class_weight && !aligned(p->class_weight, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   // per-tile buffer offsets are 32-bit: 256 rows of the widest K-major operand
   if (p->d > (1 << 20) || p->n > (1 << 22)) return FLCE_ERR_INVALID_ARGUMENT;
   // byte sizes of the largest tensors must fit comfortably in int64
@@ -247,7 +248,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   int32_t* tc = reinterpret_cast<int32_t*>(at(ws, L.tc));
   T* xc = reinterpret_cast<T*>(at(ws, L.xc));
   hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows);
+                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows, p.class_weight);
   if (p.n == 0) {
     if (p.reduction != FLCE_REDUCTION_NONE) fill(loss, 1, 0.f, s);
     if (accuracy) fill(accuracy, 1, 0.f, s);
@@ -276,6 +277,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.part_i = reinterpret_cast<int32_t*>(at(ws, L.part_i));
   a.row0 = 0;
   a.cap = p.n;
+  a.weight = p.class_weight;
   const bool b = bias != nullptr, c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
   const int key = (b ? 1 : 0) | (c ? 2 : 0) | (z ? 4 : 0);
   if (metrics)
@@ -301,6 +303,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   m.block_sums = reinterpret_cast<double*>(at(ws, L.block_sums));
   m.rows = rows;
   m.ctl = ctl;
+  m.weight = p.class_weight;
   if (metrics) {
     m.part_b = a.part_b;
     m.part_i = a.part_i;
@@ -322,10 +325,24 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
 }
 
 // ----------------------------------------------------------------- backward
-template <typename T, bool kBias, bool kSoftcap>
+template <typename T, bool kBias, bool kSoftcap, bool kWeight>
 void launch_g(const flce::GArgs<T>& a, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((flce::k_bwd_g<T, kBias, kSoftcap>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((flce::k_bwd_g<T, kBias, kSoftcap, kWeight>), dim3(static_cast<unsigned>(grid)),
                      dim3(tile::kThreads), 0, s, a);
+}
+
+template <typename T>
+void dispatch_g(const flce::GArgs<T>& a, int64_t grid, bool bias, bool softcap, hipStream_t s) {
+  switch ((bias ? 1 : 0) | (softcap ? 2 : 0) | (a.weight ? 4 : 0)) {
+    case 0: launch_g<T, false, false, false>(a, grid, s); break;
+    case 1: launch_g<T, true, false, false>(a, grid, s); break;
+    case 2: launch_g<T, false, true, false>(a, grid, s); break;
+    case 3: launch_g<T, true, true, false>(a, grid, s); break;
+    case 4: launch_g<T, false, false, true>(a, grid, s); break;
+    case 5: launch_g<T, true, false, true>(a, grid, s); break;
+    case 6: launch_g<T, false, true, true>(a, grid, s); break;
+    default: launch_g<T, true, true, true>(a, grid, s); break;
+  }
 }
 
 template <typename T>
@@ -372,7 +389,7 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
   int32_t* tc = reinterpret_cast<int32_t*>(at(ws, L.tc));
   T* xc = reinterpret_cast<T*>(at(ws, L.xc));
   hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     grad_output, mean ? 1 : 0, ctl, rows);
+                     grad_output, mean ? 1 : 0, ctl, rows, p.class_weight);
   // the fused call reuses the forward's packed rows
   if (!packed && p.n > 0)
     hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
@@ -432,13 +449,8 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
         ga.s_tiles = s_tiles;
         const int64_t g_grid = grid8(c_tiles * s_tiles);   // upper bound: all rows valid
         ga.group = kRasterGroup;
-        const int key = (has_bias ? 1 : 0) | (p.softcap > 0.f ? 2 : 0);
-        switch (key) {
-          case 0: launch_g<T, false, false>(ga, g_grid, s); break;
-          case 1: launch_g<T, true, false>(ga, g_grid, s); break;
-          case 2: launch_g<T, false, true>(ga, g_grid, s); break;
-          default: launch_g<T, true, true>(ga, g_grid, s); break;
-        }
+        ga.weight = p.class_weight;
+        dispatch_g<T>(ga, g_grid, has_bias, p.softcap > 0.f, s);
       }
       if (p.dw_bf16)
         launch_dw<T, uint16_t>(xt, gt, p, L, v0, len, gcols, d_tiles, s_tiles, c0, ci > 0, ctl,
@@ -537,7 +549,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
   float* lsep = reinterpret_cast<float*>(at(ws, S.lsep));
   const T* W = static_cast<const T*>(w);
   hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows);
+                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows, p.class_weight);
   if (p.n > 0)
     hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
                        static_cast<const T*>(x), p.d, targets, static_cast<const int32_t*>(rows),
@@ -573,6 +585,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       a.cap = S.chunk;
       a.zs = zs;
       a.zs_vt = S.v_tiles;
+      a.weight = p.class_weight;
       Layout Lc = L;                     // the chunk's token tiles only
       Lc.n_tiles = c_tiles;
       dispatch_fwd<T, false, true>(a, Lc, fkey, s);
@@ -596,6 +609,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       m.ctl = ctl;
       m.row0 = c0;
       m.lsep = lsep;
+      m.weight = p.class_weight;
       hipLaunchKernelGGL(flce::k_merge, dim3(static_cast<unsigned>(c_tiles)), dim3(256), 0, s, m);
       // G of the chunk over the whole vocabulary, from the kept logits
       flce::GArgs<T> ga{};
@@ -626,12 +640,8 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       ga.zs = zs;
       ga.zs_vt = S.v_tiles;
       const int64_t g_grid = grid8(c_tiles * S.v_tiles);
-      switch ((has_bias ? 1 : 0) | (c ? 2 : 0)) {
-        case 0: launch_g<T, false, false>(ga, g_grid, s); break;
-        case 1: launch_g<T, true, false>(ga, g_grid, s); break;
-        case 2: launch_g<T, false, true>(ga, g_grid, s); break;
-        default: launch_g<T, true, true>(ga, g_grid, s); break;
-      }
+      ga.weight = p.class_weight;
+      dispatch_g<T>(ga, g_grid, has_bias, c, s);
     }
     // X^T of the chunk; dW over the whole vocabulary, accumulated over chunks
     transpose<T>(xc + c0 * p.d, S.chunk, p.d, p.d, xt, p.d, S.chunk, S.ldt, s, ctl, c0);
@@ -710,6 +720,7 @@ flce_status check_ce_params(const flce_params* p) {
   q.vocab_slice = 0;
   const flce_status st = check_params(&q);
   if (st != FLCE_OK) return st;
+  if (p->class_weight) return FLCE_ERR_UNSUPPORTED;   // class weights: fused path only
   if (static_cast<double>(p->n) * static_cast<double>(p->v) > 1e17) return FLCE_ERR_INVALID_ARGUMENT;
   return FLCE_OK;
 }
@@ -751,7 +762,8 @@ void ce_prep(const flce_params& p, const CeLayout& L, const int32_t* targets,
              const float* grad_output, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
                      grad_output, p.reduction == FLCE_REDUCTION_MEAN ? 1 : 0,
-                     reinterpret_cast<Ctl*>(at(ws, L.ctl)), reinterpret_cast<int32_t*>(at(ws, L.rows)));
+                     reinterpret_cast<Ctl*>(at(ws, L.ctl)), reinterpret_cast<int32_t*>(at(ws, L.rows)),
+                     static_cast<const float*>(nullptr));
 }
 
 void ce_reduce(const flce_params& p, const CeLayout& L, float* loss, void* ws, hipStream_t s) {

@@ -33,8 +33,9 @@ constexpr int64_t kGroup = 8;   // grouped-raster width (tiles sharing a panel)
 struct Ctl {           // first bytes of the workspace
   int32_t n_valid;
   int32_t status;      // 0 = targets fine, 1 = some target out of range
-  float scale;         // d loss / d (row loss): g / n_valid (mean) or g (sum)
-  float pad;
+  float scale;         // d loss / d (row loss): g / wsum (mean) or g (sum)
+  float wall;          // sum of the class weights over the vocabulary (V without weights)
+  float wsum;          // what 'mean' divides by: n_valid, or the valid rows' target weights
 };
 
 // Valid packed rows of a backward token chunk: the chunk starts at packed row
@@ -86,27 +87,42 @@ __global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targe
                                                int64_t v, int32_t ignore_index,
                                                const float* __restrict__ grad_output,
                                                int32_t reduction_mean, Ctl* __restrict__ ctl,
-                                               int32_t* __restrict__ rows) {
+                                               int32_t* __restrict__ rows,
+                                               const float* __restrict__ weight) {
   // Wave w owns the contiguous rows [w * per, (w + 1) * per) and walks them 64
   // at a time (coalesced); a ballot gives each valid row its place, so the
-  // valid rows land in `rows` in row order.
+  // valid rows land in `rows` in row order.  With class weights, the valid
+  // rows' target weights and all the weights are summed too (fixed order).
   __shared__ int32_t s_cnt[16];
   __shared__ int32_t s_bad[16];
+  __shared__ double s_w[2][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t per = ((n + 15) / 16 + 63) / 64 * 64;
   const int64_t lo = wave * per, hi = lo + per < n ? lo + per : n;
   int32_t cnt = 0, bad = 0;
+  double wt = 0.0, wa = 0.0;
   for (int64_t i0 = lo; i0 < hi; i0 += 64) {
     const int64_t i = i0 + lane;
     const int32_t t = i < hi ? targets[i] : ignore_index;
     const bool ok = t != ignore_index;
+    const bool in = ok && t >= 0 && static_cast<int64_t>(t) < v;
     cnt += __popcll(__ballot(ok));
-    bad |= (ok && (t < 0 || static_cast<int64_t>(t) >= v)) ? 1 : 0;
+    bad |= (ok && !in) ? 1 : 0;
+    if (weight && in) wt += weight[t];
   }
+  if (weight)
+    for (int64_t c = static_cast<int64_t>(wave) * 64 + lane; c < v; c += 1024) wa += weight[c];
   bad = __ballot(bad) != 0 ? 1 : 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    wt += __shfl_xor(wt, off);
+    wa += __shfl_xor(wa, off);
+  }
   if (lane == 0) {
     s_cnt[wave] = cnt;
     s_bad[wave] = bad;
+    s_w[0][wave] = wt;
+    s_w[1][wave] = wa;
   }
   __syncthreads();
   int32_t k = 0, nv = 0, any_bad = 0;
@@ -124,11 +140,18 @@ __global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targe
     k += __popcll(m);
   }
   if (threadIdx.x == 0) {
+    double wts = 0.0, was = 0.0;
+    for (int w = 0; w < 16; ++w) {
+      wts += s_w[0][w];
+      was += s_w[1][w];
+    }
     const float g = grad_output ? grad_output[0] : 1.0f;
+    const float den = weight ? static_cast<float>(wts) : static_cast<float>(nv);
     ctl->n_valid = nv;
     ctl->status = any_bad;
-    ctl->scale = reduction_mean ? (nv > 0 ? g / static_cast<float>(nv) : 0.0f) : g;
-    ctl->pad = 0.0f;
+    ctl->wsum = den;
+    ctl->wall = weight ? static_cast<float>(was) : static_cast<float>(v);
+    ctl->scale = reduction_mean ? (den > 0.f ? g / den : 0.0f) : g;
   }
 }
 
@@ -193,6 +216,7 @@ struct FwdArgs {
   float* zt;              // [n] target logit, by packed row
   const Ctl* ctl;         // n_valid: rows of x (packed) that take part
   int64_t row0, cap;      // token chunk: first packed row (pointers above start there), capacity
+  const float* weight;    // [v] class weights or null: part_s then holds sum_v w_v z_v
   float* zs;              // null, or the raw logit tiles of the chunk, stored in register order
   int64_t zs_vt;          // vocabulary tiles per token tile in zs
 };
@@ -272,8 +296,16 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
       }
       if (kSumZ) {
         float sz = 0.f;
+        if (a.weight) {   // class weights: sum_v w_v z_v
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sz += (!kMasked || z[r] != -INFINITY) ? z[r] : 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
+            if (!kMasked || vl < vlim) sz += a.weight[v0 + vl] * z[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sz += (!kMasked || z[r] != -INFINITY) ? z[r] : 0.f;
+        }
         s_run[nb] += sz;
       }
       if (kMasked && mt == -INFINITY) continue;
@@ -437,6 +469,7 @@ struct MergeArgs {
   const Ctl* ctl;
   int64_t row0;         // this launch covers rows [row0, row0 + 256 gridDim.x)
   float* lsep;          // null, or [n] lse by packed row
+  const float* weight;  // [v] class weights or null
 };
 
 // lse = (m + log2 d) ln 2; row loss = lse - (1-eps) z_t - (eps/V) sum z + s lse^2
@@ -454,8 +487,16 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
       s += a.part_s[c * a.n + j];
     }
     const float lse = (m + log2f(d)) * kLn2;
-    const float rl = lse - a.keep_target * a.zt[j] - a.eps_over_v * s + a.zloss * lse * lse;
     const int64_t r = a.rows[j];
+    float rl;
+    if (a.weight) {   // (1-eps) w_t (lse - z_t) + (eps/V)(sum_v w_v lse - sum_v w_v z_v) + s w_t lse^2
+      const int32_t t = a.targets[r];
+      const float wt = (t >= 0 && t < a.v) ? a.weight[t] : 0.f;
+      rl = a.keep_target * wt * (lse - a.zt[j]) + a.eps_over_v * (a.ctl->wall * lse - s) +
+           a.zloss * wt * lse * lse;
+    } else {
+      rl = lse - a.keep_target * a.zt[j] - a.eps_over_v * s + a.zloss * lse * lse;
+    }
     a.lse[r] = lse;
     if (a.lsep) a.lsep[j] = lse;
     if (a.row_loss) a.row_loss[r] = rl;
@@ -541,8 +582,8 @@ __global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ b
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const int32_t nv = ctl->n_valid;
-    loss[0] = static_cast<float>(reduction_mean ? (nv > 0 ? red[0] / nv : 0.0) : red[0]);
+    const double den = ctl->wsum;   // n_valid, or the valid rows' target weights
+    loss[0] = static_cast<float>(reduction_mean ? (den > 0.0 ? red[0] / den : 0.0) : red[0]);
   }
 }
 
@@ -601,6 +642,7 @@ struct GArgs {
   const Ctl* ctl;
   const float* zs;      // null, or the chunk's raw logit tiles (see stored_tile): read, not recomputed
   int64_t zs_vt;        // vocabulary tiles per token tile in zs (the slice is then all of V)
+  const float* weight;  // [v] class weights (with kWeight)
 };
 
 __device__ __forceinline__ void store1(uint16_t* p, float a) {
@@ -693,9 +735,11 @@ __device__ __forceinline__ void store_g_direct(const GArgs<T>& a, const f32x16 (
 
 // One element of G from its logit before bias and softcap; is_t marks the
 // target column.
+// keep_t: (1-eps) times the target's weight; epsw: eps/V times this column's
+// weight (both without weights: 1-eps and eps/V).
 template <bool kBias, bool kSoftcap, typename T>
 __device__ __forceinline__ float g_elem(const GArgs<T>& a, float z, float bv, float lse2, float zfac,
-                                        bool is_t) {
+                                        bool is_t, float keep_t, float epsw) {
   if (kBias) z += bv;
   float dz = 1.0f;
   if (kSoftcap) {
@@ -704,7 +748,7 @@ __device__ __forceinline__ float g_elem(const GArgs<T>& a, float z, float bv, fl
     dz = 1.0f - th * th;
   }
   const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2));
-  const float sub = is_t ? a.eps_over_v + a.keep_target : a.eps_over_v;
+  const float sub = is_t ? epsw + keep_t : epsw;
   float g = __builtin_fmaf(p, zfac, -sub);
   if (kSoftcap) g *= dz;
   return g;
@@ -713,12 +757,12 @@ __device__ __forceinline__ float g_elem(const GArgs<T>& a, float z, float bv, fl
 // bf16 G of one tile, straight from the accumulators into bf16 pairs, then
 // staged out.  kEdge: the tile reaches past n_valid or past the slice, whose
 // entries are 0.
-template <typename T, bool kBias, bool kSoftcap, bool kEdge>
+template <typename T, bool kBias, bool kSoftcap, bool kWeight, bool kEdge>
 __device__ __forceinline__ void g_tile_bf16(const GArgs<T>& a, const f32x16 (&acc)[4][4], char* lds,
                                             int64_t n0, int64_t vl0, int vw, int wn, int lane, int tid,
                                             int64_t nv, int vlim, const float (&lse2)[4],
                                             const float (&zfac)[4], const int (&hit)[4],
-                                            const bool (&valid)[4]) {
+                                            const bool (&valid)[4], const float (&keep_t)[4]) {
   uint32_t gp[4][4][8];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -732,11 +776,17 @@ __device__ __forceinline__ void g_tile_bf16(const GArgs<T>& a, const f32x16 (&ac
         bv0 = in0 ? ld_elem(a.bias, a.v0 + vl0 + vl) : 0.f;
         bv1 = in1 ? ld_elem(a.bias, a.v0 + vl0 + vl + 1) : 0.f;
       }
+      float ew0 = a.eps_over_v, ew1 = a.eps_over_v;
+      if (kWeight) {
+        ew0 *= in0 ? a.weight[a.v0 + vl0 + vl] : 0.f;
+        ew1 *= in1 ? a.weight[a.v0 + vl0 + vl + 1] : 0.f;
+      }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        float g0 = g_elem<kBias, kSoftcap>(a, acc[mb][nb][r], bv0, lse2[nb], zfac[nb], mb * 16 + r == hit[nb]);
+        float g0 = g_elem<kBias, kSoftcap>(a, acc[mb][nb][r], bv0, lse2[nb], zfac[nb], mb * 16 + r == hit[nb],
+                                           keep_t[nb], ew0);
         float g1 = g_elem<kBias, kSoftcap>(a, acc[mb][nb][r + 1], bv1, lse2[nb], zfac[nb],
-                                           mb * 16 + r + 1 == hit[nb]);
+                                           mb * 16 + r + 1 == hit[nb], keep_t[nb], ew1);
         if (kEdge) {
           g0 = (valid[nb] && in0) ? g0 : 0.f;
           g1 = (valid[nb] && in1) ? g1 : 0.f;
@@ -751,7 +801,8 @@ __device__ __forceinline__ void g_tile_bf16(const GArgs<T>& a, const f32x16 (&ac
 // G = [p (1 + 2 s lse) - (1-eps) onehot - eps/V] (1 - (z/c)^2), p = exp(z - lse)
 // (page "Cutting LLM Memory by 84%", "Kernel Implementation", backward:
 // probabilities recomputed from the stored LSE, ground truth subtracted).
-template <typename T, bool kBias, bool kSoftcap>
+// kWeight: class weights (per-token target weight, per-column smoothing weight).
+template <typename T, bool kBias, bool kSoftcap, bool kWeight>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bwd_g(GArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
@@ -802,7 +853,7 @@ void k_bwd_g(GArgs<T> a) {
   const int vlim = a.slice_len - vl0 < tile::kM ? static_cast<int>(a.slice_len - vl0) : tile::kM;
   // Rows past the slice and missing tokens get 0.  Per-token terms first,
   // then one vocabulary row (and its bias) at a time across the token blocks.
-  float lse2[4], zfac[4];
+  float lse2[4], zfac[4], keep_t[4];
   int hit[4];
   bool valid[4];
 #pragma unroll
@@ -812,7 +863,14 @@ void k_bwd_g(GArgs<T> a) {
     valid[nb] = tok < nv;          // packed rows all have a target
     const float l = valid[nb] ? lse_t[nb] : 0.f;
     lse2[nb] = l * kLog2e;
-    zfac[nb] = 1.0f + a.two_s * l;
+    if (kWeight) {   // p [(1-eps) w_t + (eps/V) sum w + 2 s w_t lse] - (1-eps) w_t [v = t] - (eps/V) w_v
+      const float wt = (valid[nb] && t >= 0 && t < a.v) ? a.weight[t] : 0.f;
+      keep_t[nb] = a.keep_target * wt;
+      zfac[nb] = keep_t[nb] + a.eps_over_v * a.ctl->wall + a.two_s * wt * l;
+    } else {
+      keep_t[nb] = a.keep_target;
+      zfac[nb] = 1.0f + a.two_s * l;
+    }
     const int64_t rel64 = static_cast<int64_t>(t) - a.v0 - vl0 - vw;
     hit[nb] = (valid[nb] && rel64 >= 0 && rel64 < 128 && (rel64 & 4) == 0)
                   ? static_cast<int>((rel64 >> 5) * 16 + ((rel64 >> 3) & 3) * 4 + (rel64 & 3))
@@ -820,11 +878,11 @@ void k_bwd_g(GArgs<T> a) {
   }
   if constexpr (sizeof(T) == 2) {
     if (n0 + tile::kN <= nv && vlim == tile::kM)
-      g_tile_bf16<T, kBias, kSoftcap, false>(a, acc, lds, n0, vl0, vw, wn, lane, tid, nv, vlim, lse2,
-                                             zfac, hit, valid);
+      g_tile_bf16<T, kBias, kSoftcap, kWeight, false>(a, acc, lds, n0, vl0, vw, wn, lane, tid, nv, vlim,
+                                                      lse2, zfac, hit, valid, keep_t);
     else
-      g_tile_bf16<T, kBias, kSoftcap, true>(a, acc, lds, n0, vl0, vw, wn, lane, tid, nv, vlim, lse2,
-                                            zfac, hit, valid);
+      g_tile_bf16<T, kBias, kSoftcap, kWeight, true>(a, acc, lds, n0, vl0, vw, wn, lane, tid, nv, vlim,
+                                                     lse2, zfac, hit, valid, keep_t);
   } else {
     // fp32: G replaces the logits in the accumulators, then leaves directly
 #pragma unroll
@@ -834,10 +892,11 @@ void k_bwd_g(GArgs<T> a) {
         const int vl = vw + mb * 32 + 8 * (r >> 2) + (r & 3);
         const bool vin = vl < vlim;
         const float bv = (kBias && vin) ? ld_elem(a.bias, a.v0 + vl0 + vl) : 0.f;
+        const float ew = kWeight ? (vin ? a.eps_over_v * a.weight[a.v0 + vl0 + vl] : 0.f) : a.eps_over_v;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const float g = g_elem<kBias, kSoftcap>(a, acc[mb][nb][r], bv, lse2[nb], zfac[nb],
-                                                  mb * 16 + r == hit[nb]);
+                                                  mb * 16 + r == hit[nb], keep_t[nb], ew);
           acc[mb][nb][r] = (valid[nb] && vin) ? g : 0.f;
         }
       }

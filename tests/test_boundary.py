@@ -222,3 +222,13 @@ def test_token_chunk_and_dw_bf16_params(lib):
     assert b - a < 32768 * (4096 * 2 + 4 * 600) * 1.1
     # a chunk larger than the batch is the whole batch
     assert (_lib.workspace_size(P(token_chunk=1 << 20), True) == _lib.workspace_size(P(), True))
+
+
+def test_class_weight_params(lib):
+    assert fwd(P(class_weight=FAKE + 2)) == INVALID            # weights not 4-byte aligned
+    # the logits path has no class weights
+    assert ce_fwd(P(class_weight=FAKE)) == _lib.FLCE_ERR_UNSUPPORTED
+    assert ce_fused(P(class_weight=FAKE)) == _lib.FLCE_ERR_UNSUPPORTED
+    assert _lib.ce_workspace_size(P(class_weight=FAKE)) == 0
+    # weights change no buffer size
+    assert _lib.workspace_size(P(class_weight=FAKE), True) == _lib.workspace_size(P(), True)

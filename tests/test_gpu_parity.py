@@ -496,3 +496,35 @@ def test_headline_schedules_sampled_rows():
     assert torch.equal(dx1, dx2)
     rel = (torch.linalg.norm(dw2.double() - dw1.double()) / torch.linalg.norm(dw1.double())).item()
     assert rel <= 4e-3, rel
+
+
+# ------------------------------------------------- class weights
+
+@pytest.mark.parametrize("stored", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("feats", [dict(), dict(label_smoothing=0.1), dict(lse_square_scale=1e-3, softcap=5.0),
+                                   dict(label_smoothing=0.2, lse_square_scale=1e-3, softcap=3.0,
+                                        reduction="sum")],
+                         ids=lambda f: "-".join(f"{k}={v}" for k, v in f.items()) or "plain")
+def test_class_weights(feats, dtype, stored):
+    """Per-class weights (torch's weighted cross-entropy): every output of the
+    fused call against the oracle, in both schedules, over several vocabulary
+    slices and a ragged vocabulary."""
+    n, d, v = 600, 136, 1000
+    inp = small_problem(n, d, v, dtype, bias=True, seed=17)
+    cw = np.random.default_rng(5).uniform(0.1, 3.0, v)
+    o = O.LossOptions(class_weight=cw, **feats)
+    banner(f"class weights {dtype} stored={stored} {feats}")
+    kw = dict(stored_logits=True, token_chunk=256) if stored else dict(vocab_slice=256)
+    got = _fused_opts(inp, dtype, o, class_weight=torch.tensor(cw, dtype=torch.float32, device="cuda"),
+                      **kw)
+    U.compare_full(inp, dtype, o, got=got)
+    # the forward alone, and the weighted mean's denominator
+    x = U.dev_tensor(inp["x"], dtype)
+    w = U.dev_tensor(inp["w"], dtype)
+    b = U.dev_tensor(inp["bias"], dtype)
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, rl = api.forward(x, w, t, b, class_weight=torch.tensor(cw, device="cuda"), **U.lib_opts(o))
+    ref = O.forward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+    U.assert_loss(float(loss), ref.loss)
+    assert np.abs(U.host(rl) - ref.row_loss).max() <= 2 * U.LSE_ABS * max(1.0, cw.max())
