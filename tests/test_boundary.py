@@ -232,3 +232,20 @@ def test_class_weight_params(lib):
     assert _lib.ce_workspace_size(P(class_weight=FAKE)) == 0
     # weights change no buffer size
     assert _lib.workspace_size(P(class_weight=FAKE), True) == _lib.workspace_size(P(), True)
+
+
+def test_size_limits(lib):
+    """The documented limits (N <= 2^22, D <= 2^20, V < 2^31; slice and chunk
+    widths) are accepted at the limit and refused one step beyond it."""
+    def ws(**kw):
+        return _lib.workspace_size(P(**kw), True)
+    assert ws(n=1 << 22) > 0 and ws(n=(1 << 22) + 1) == 0
+    assert ws(d=1 << 20) > 0 and ws(d=(1 << 20) + 8) == 0
+    assert ws(v=(1 << 31) - 1) > 0 and ws(v=1 << 31) == 0
+    assert ws(n=1 << 22, d=1 << 20, v=1 << 16) > 0
+    assert ws(vocab_slice=1 << 20) > 0 and ws(vocab_slice=(1 << 20) + 1) == 0
+    assert ws(token_chunk=1 << 22) > 0 and ws(token_chunk=(1 << 22) + 1) == 0
+    assert _lib.stored_workspace_size(P(n=1 << 22)) > 0
+    assert _lib.stored_workspace_size(P(n=(1 << 22) + 1)) == 0
+    assert _lib.ce_workspace_size(P(n=1 << 22, v=(1 << 31) - 1)) > 0
+    assert _lib.ce_workspace_size(P(n=(1 << 22) + 1)) == 0
