@@ -33,7 +33,9 @@
  *    device memory and never synchronises, except flce_check_status().
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    runs asynchronously; results are valid once that stream has reached the
- *    end of the call.
+ *    end of the call.  Kernels run on the calling thread's current HIP
+ *    device: every pointer and the stream must belong to it (hipSetDevice
+ *    first when several devices are visible).
  *  - Tensors are dense row-major.  X, W, dX, bias must be 16-byte aligned;
  *    D must be a multiple of 8.  N and V are arbitrary (ragged tails are
  *    handled in the kernels).  N <= 2^22, D <= 2^20, V < 2^31.

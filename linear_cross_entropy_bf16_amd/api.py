@@ -14,6 +14,7 @@ the same leading shape.
 """
 from __future__ import annotations
 
+import functools
 from typing import Optional, Tuple
 
 import torch
@@ -29,6 +30,19 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _on_tensor_device(fn):
+    """Run ``fn`` with the first argument's GPU as the current device: the
+    library launches on the current HIP device."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        first = args[0] if args else None
+        if isinstance(first, torch.Tensor) and first.device.type == "cuda":
+            with torch.cuda.device(first.device):
+                return fn(*args, **kwargs)
+        return fn(*args, **kwargs)   # the argument checks raise
+    return wrapper
 
 
 def _check(status: int, what: str) -> None:
@@ -95,6 +109,7 @@ def _workspace(params, with_backward, device) -> Tuple[torch.Tensor, int]:
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
+@_on_tensor_device
 def forward(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
             lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
             check_targets=False, return_metrics=False, class_weight=None):
@@ -128,6 +143,7 @@ def forward(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=
     return out + (pred, acc[0]) if return_metrics else out
 
 
+@_on_tensor_device
 def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_index=-100,
              label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0, reduction="mean",
              vocab_slice=0, token_chunk=0, dw_bf16=False, class_weight=None):
@@ -155,6 +171,7 @@ def backward(x, weight, target, lse, grad_output=None, bias=None, *, ignore_inde
     return dx.reshape(x.shape), dw, db
 
 
+@_on_tensor_device
 def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoothing=0.0,
                   lse_square_scale=0.0, softcap=0.0, reduction="mean", vocab_slice=0,
                   token_chunk=0, dw_bf16=False, workspace: Optional[torch.Tensor] = None, out=None,
@@ -265,6 +282,7 @@ def _ce_workspace(p, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
+@_on_tensor_device
 def cross_entropy_forward(logits, target, *, ignore_index=-100, label_smoothing=0.0,
                           lse_square_scale=0.0, softcap=0.0, reduction="mean", check_targets=False,
                           return_metrics=False):
@@ -295,6 +313,7 @@ def cross_entropy_forward(logits, target, *, ignore_index=-100, label_smoothing=
     return out + (pred, acc[0]) if return_metrics else out
 
 
+@_on_tensor_device
 def cross_entropy_backward(logits, target, lse, grad_output=None, *, ignore_index=-100,
                            label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0,
                            reduction="mean", inplace=False):
@@ -314,6 +333,7 @@ def cross_entropy_backward(logits, target, lse, grad_output=None, *, ignore_inde
     return out.reshape(logits.shape)
 
 
+@_on_tensor_device
 def cross_entropy_fused_fwd_bwd(logits, target, *, ignore_index=-100, label_smoothing=0.0,
                                 lse_square_scale=0.0, softcap=0.0, reduction="mean", inplace=False,
                                 workspace: Optional[torch.Tensor] = None, out=None):
