@@ -436,6 +436,14 @@ def bench_ce(args, wl):
     bwd()
     bwd_ms = timed(bwd, max(3, args.steps))
 
+    # practical ceiling for context: a plain device copy (torch's copy kernel)
+    # moving the same bytes, every row read and written once
+    def copy():
+        grad.copy_(r)
+
+    copy()
+    copy_ms = timed(copy, max(3, args.steps))
+
     n_valid = int((inp["targets"] != wl.ignore_index).sum())
     # must-move bytes: the valid rows read once, the gradient written once
     # (ignored rows are written as zeros, never read)
@@ -481,6 +489,12 @@ def bench_ce(args, wl):
             "fwd_gbs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
             "separate_bwd_ms": round(bwd_ms, 4),
             "separate_bwd_gbs": round(step_bytes / (bwd_ms * 1e-3) / 1e9, 1),
+            "copy_reference": {
+                "what": "torch copy_ of all logits into the gradient buffer (every row read and "
+                        "written once)",
+                "ms": round(copy_ms, 4),
+                "gbs": round(2 * wl.n * wl.v * elem / (copy_ms * 1e-3) / 1e9, 1),
+            },
         },
         "cpu_baseline": cpu,
     }

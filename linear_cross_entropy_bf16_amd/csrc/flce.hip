@@ -6,6 +6,7 @@
 // included, belongs to the caller.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -170,14 +171,17 @@ flce_status check_ws(const void* ws, size_t ws_bytes, int64_t need) {
 
 // The kernels are gfx950 code objects only.
 flce_status check_device() {
-  static int known[64];   // 0 unknown, 1 gfx950, 2 other
+  // per device: 0 unknown, 1 gfx950, 2 other (calls from several threads may
+  // race to fill an entry; they all store the same value)
+  static std::atomic<int> known[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FLCE_ERR_DEVICE;
-  if (dev >= 0 && dev < 64 && known[dev]) return known[dev] == 1 ? FLCE_OK : FLCE_ERR_UNSUPPORTED;
+  const int k = dev >= 0 && dev < 64 ? known[dev].load(std::memory_order_relaxed) : 0;
+  if (k) return k == 1 ? FLCE_OK : FLCE_ERR_UNSUPPORTED;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FLCE_ERR_DEVICE;
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev >= 0 && dev < 64) known[dev] = ok ? 1 : 2;
+  if (dev >= 0 && dev < 64) known[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? FLCE_OK : FLCE_ERR_UNSUPPORTED;
 }
 
