@@ -118,8 +118,9 @@ def main():
         print(json.dumps({"copy_bytes": a.numel() * 4}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (each box here "
-              f"has one GPU; the multi-GPU sharding is described in DESIGN.md).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the step is "
+              f"data-parallel over tokens: each GPU would run this measurement on its share of "
+              f"the batch, followed by an all-reduce of dW).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
