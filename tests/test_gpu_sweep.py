@@ -98,3 +98,55 @@ def test_option_sweep(case):
     else:
         assert np.all(got["dx"] == 0.0) and np.all(got["dw"] == 0.0)
     assert np.all(got["dx"][~valid] == 0.0), "ignored rows must have zero dX"
+
+
+def draw_ce_case(seed):
+    """Sizes and options of one cross-entropy-on-logits case (V >= 2)."""
+    rng = np.random.default_rng(seed)
+    return dict(
+        n=int(rng.integers(0, 300)),
+        v=int(rng.integers(2, 5000)),
+        dtype=str(rng.choice(["bf16", "f32"])),
+        label_smoothing=float(rng.choice([0.0, 0.0, 0.1, 0.3])),
+        lse_square_scale=float(rng.choice([0.0, 0.0, 1e-3])),
+        softcap=float(rng.choice([0.0, 0.0, 4.0, 30.0])),
+        reduction=str(rng.choice(["mean", "sum"])),
+        ignore_frac=float(rng.choice([0.0, 0.1, 0.5])),
+        mode=str(rng.choice(["fused", "separate"])),
+        inplace=bool(rng.random() < 0.3),
+        spread=float(rng.choice([1.0, 3.0])),
+    )
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_logits_option_sweep(case):
+    seed = 9000 + case
+    c = draw_ce_case(seed)
+    print(f"\n[gpu-sweep] logits case {case} seed {seed}: {c}", flush=True)
+    rng = np.random.default_rng(seed + 3)
+    n, v = c["n"], c["v"]
+    r = rng.standard_normal((n, v), dtype=np.float32) * np.float32(c["spread"])
+    t = rng.integers(0, v, n).astype(np.int32)
+    k = int(round(c["ignore_frac"] * n))
+    if k:
+        t[rng.choice(n, k, replace=False)] = IGN
+    if c["dtype"] == "bf16":
+        r = W.f32_to_bf16_bits(r)
+    o = O.LossOptions(label_smoothing=c["label_smoothing"], lse_square_scale=c["lse_square_scale"],
+                      softcap=c["softcap"], reduction=c["reduction"])
+    logits = U.dev_tensor(r, c["dtype"])
+    tt = torch.from_numpy(t).to("cuda")
+    if c["mode"] == "fused":
+        loss, lse, g = api.cross_entropy_fused_fwd_bwd(logits, tt, inplace=c["inplace"], **U.lib_opts(o))
+    else:
+        loss, lse, _ = api.cross_entropy_forward(logits, tt, check_targets=True, **U.lib_opts(o))
+        g = api.cross_entropy_backward(logits, tt, lse, None, inplace=c["inplace"], **U.lib_opts(o))
+    torch.cuda.synchronize()
+    ref = O.cross_entropy_on_logits(r, t, o)
+    U.assert_loss(float(loss.item()), ref.loss)
+    valid = t != IGN
+    got_lse, got_g = U.host(lse), U.host(g)
+    U.assert_lse(got_lse[valid], ref.lse[valid])
+    assert np.all(got_lse[~valid] == 0.0) and np.all(got_g[~valid] == 0.0)
+    if valid.any():
+        U.assert_close(got_g, ref.dx, "dlogits")
