@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--stored-logits", action="store_true",
                     help="three-contraction schedule: logits kept per token chunk, not recomputed "
                          "(6 N D V FLOPs; the MFMA fractions are then quoted against 6 N D V)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the CPU oracle baseline runs on (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -171,6 +173,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # one step captured in a HIP graph (the library only launches kernels
+        # on the caller's stream), replayed as the timed step
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        run()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} steps")
@@ -178,7 +197,7 @@ def main():
     wall0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        step()
+        run()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -258,6 +277,7 @@ def main():
                    "ignore_frac": wl.ignore_frac, "reduction": wl.reduction, "bias": wl.bias,
                    "label_smoothing": wl.label_smoothing, "lse_square_scale": wl.lse_square_scale,
                    "softcap": wl.softcap, "vocab_slice": args.vocab_slice or "default",
+                   "launch": "hip graph replay" if args.graph else "eager",
                    "token_chunk": args.token_chunk or ("8192 (default of the schedule)" if args.stored_logits else "whole batch"),
                    "dw_dtype": "bf16" if args.dw_bf16 else "fp32",
                    "schedule": "stored logits, 6NDV" if args.stored_logits else "recompute, 8NDV",
