@@ -250,6 +250,36 @@ def linear_cross_entropy(x, weight, target, bias=None, ignore_index=-100, label_
                                             lse_square_scale, softcap, reduction, class_weight)
 
 
+class LinearCrossEntropyLoss(torch.nn.Module):
+    """Module form of ``linear_cross_entropy`` for an LM head: holds the
+    loss options; ``forward(x, weight, target, bias=None)`` with ``weight``
+    the head's [V, D] matrix (for example ``lm_head.weight``)."""
+
+    def __init__(self, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0,
+                 reduction="mean", class_weight=None):
+        super().__init__()
+        if reduction not in ("mean", "sum", "none"):
+            raise ValueError(f"reduction must be 'mean', 'sum' or 'none', got {reduction!r}")
+        if not 0.0 <= label_smoothing <= 1.0:
+            raise ValueError(f"label_smoothing must lie in [0, 1], got {label_smoothing}")
+        self.ignore_index = ignore_index
+        self.label_smoothing = label_smoothing
+        self.lse_square_scale = lse_square_scale
+        self.softcap = softcap
+        self.reduction = reduction
+        self.register_buffer("class_weight", class_weight, persistent=False)
+
+    def forward(self, x, weight, target, bias=None):
+        return linear_cross_entropy(x, weight, target, bias, self.ignore_index, self.label_smoothing,
+                                    self.lse_square_scale, self.softcap, self.reduction,
+                                    self.class_weight)
+
+    def extra_repr(self):
+        return (f"ignore_index={self.ignore_index}, label_smoothing={self.label_smoothing}, "
+                f"lse_square_scale={self.lse_square_scale}, softcap={self.softcap}, "
+                f"reduction={self.reduction!r}")
+
+
 # ------------------------------------------------- cross-entropy on logits
 
 def _prepare_logits(logits, target):

@@ -287,6 +287,30 @@ def test_autograd_function_and_grad_output():
     U.assert_close(U.host(b.grad), ref.db, "db")
 
 
+def test_loss_module_on_an_lm_head():
+    """The module form on an nn.Linear head: [B, T, D] hidden states, the
+    head's weight and bias, class weights held as a buffer, gradients through
+    autograd into the head's parameters."""
+    inp = small_problem(2 * 150, 96, 700, "bf16", bias=True, seed=21)
+    cw = np.random.default_rng(2).uniform(0.5, 2.0, 700)
+    head = torch.nn.Linear(96, 700, bias=True).to(device="cuda", dtype=torch.bfloat16)
+    with torch.no_grad():
+        head.weight.copy_(U.dev_tensor(inp["w"], "bf16"))
+        head.bias.copy_(U.dev_tensor(inp["bias"], "bf16"))
+    crit = api.LinearCrossEntropyLoss(label_smoothing=0.1, softcap=15.0,
+                                      class_weight=torch.tensor(cw, dtype=torch.float32)).cuda()
+    x = U.dev_tensor(inp["x"], "bf16").view(2, 150, 96).requires_grad_(True)
+    t = torch.from_numpy(inp["targets"]).cuda().view(2, 150)
+    loss = crit(x, head.weight, t, head.bias)
+    loss.backward()
+    o = O.LossOptions(label_smoothing=0.1, softcap=15.0, class_weight=cw)
+    ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+    U.assert_loss(float(loss.item()), ref.loss)
+    U.assert_close(U.host(x.grad).reshape(300, 96), ref.dx, "dX")
+    U.assert_close(U.host(head.weight.grad), ref.dw, "dW")
+    U.assert_close(U.host(head.bias.grad), ref.db, "db")
+
+
 def test_noncontiguous_and_batched_inputs():
     inp = small_problem(240, 64, 800, "bf16", seed=11)
     ref = O.forward(inp["x"], inp["w"], None, inp["targets"], O.LossOptions())
