@@ -38,7 +38,8 @@
  *    first when several devices are visible).
  *  - Tensors are dense row-major.  X, W, dX, bias must be 16-byte aligned;
  *    D must be a multiple of 8.  N and V are arbitrary (ragged tails are
- *    handled in the kernels).  N <= 2^22, D <= 2^20, V < 2^31.
+ *    handled in the kernels).  N <= 2^22, D <= 2^20, V < 2^31, and for the
+ *    fused path ceil(N/256) * ceil(V/256) < 2^31 (one forward tile each).
  *  - Element type of X, W, bias and dX is params->dtype (bf16 or fp32).
  *    Loss, lse, row_loss, dW and db are always fp32.  Accumulation is fp32.
  *  - Every argument is validated on the host before any HIP call, so invalid

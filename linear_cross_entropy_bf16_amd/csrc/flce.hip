@@ -128,7 +128,7 @@ Layout make_layout(const flce_params& p) {
 // ----------------------------------------------------------------- checks
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-flce_status check_params(const flce_params* p) {
+flce_status check_shape(const flce_params* p) {
   if (!p) return FLCE_ERR_INVALID_ARGUMENT;
   if (p->n < 0 || p->n > kMaxDim) return FLCE_ERR_INVALID_ARGUMENT;
   if (p->d <= 0 || p->d > kMaxDim || p->d % 8 != 0) return FLCE_ERR_INVALID_ARGUMENT;
@@ -151,6 +151,15 @@ flce_status check_params(const flce_params* p) {
   const double big = static_cast<double>(p->n) * static_cast<double>(p->v) + p->n * (double)p->d +
                      p->v * (double)p->d;
   if (big > 1e17) return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+// The fused path's launch grids fit in 31 bits; the largest is the forward's,
+// one workgroup per token tile and vocabulary chunk (at most one per tile).
+flce_status check_params(const flce_params* p) {
+  const flce_status st = check_shape(p);
+  if (st != FLCE_OK) return st;
+  if (cdiv(p->n, 256) * cdiv(p->v, 256) > (int64_t{1} << 31) - 8) return FLCE_ERR_INVALID_ARGUMENT;
   return FLCE_OK;
 }
 
@@ -722,7 +731,7 @@ flce_status check_ce_params(const flce_params* p) {
   flce_params q = *p;
   q.d = 8;
   q.vocab_slice = 0;
-  const flce_status st = check_params(&q);
+  const flce_status st = check_shape(&q);
   if (st != FLCE_OK) return st;
   if (p->class_weight) return FLCE_ERR_UNSUPPORTED;   // class weights: fused path only
   if (static_cast<double>(p->n) * static_cast<double>(p->v) > 1e17) return FLCE_ERR_INVALID_ARGUMENT;

@@ -243,6 +243,7 @@ def test_size_limits(lib):
     assert ws(d=1 << 20) > 0 and ws(d=(1 << 20) + 8) == 0
     assert ws(v=(1 << 31) - 1) > 0 and ws(v=1 << 31) == 0
     assert ws(n=1 << 22, d=1 << 20, v=1 << 16) > 0
+    assert ws(n=1 << 22, v=(1 << 31) - 1) == 0          # 2^37 forward tiles
     assert ws(vocab_slice=1 << 20) > 0 and ws(vocab_slice=(1 << 20) + 1) == 0
     assert ws(token_chunk=1 << 22) > 0 and ws(token_chunk=(1 << 22) + 1) == 0
     assert _lib.stored_workspace_size(P(n=1 << 22)) > 0
