@@ -44,7 +44,9 @@
  *    Loss, lse, row_loss, dW and db are always fp32.  Accumulation is fp32.
  *  - Every argument is validated on the host before any HIP call, so invalid
  *    calls return an error without touching the GPU.  Nothing aborts or
- *    throws across this interface.
+ *    throws across this interface.  Just before its launches an entry point
+ *    clears the calling thread's pending HIP error (hipGetLastError), so
+ *    FLCE_ERR_DEVICE reports a failure of its own launches.
  *  - Results are deterministic: every reduction has a fixed order, and there
  *    are no global atomics.
  *  - Concurrent calls that share a workspace race; give each in-flight call

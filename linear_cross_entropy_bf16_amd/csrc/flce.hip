@@ -194,6 +194,15 @@ flce_status check_device() {
   return ok ? FLCE_OK : FLCE_ERR_UNSUPPORTED;
 }
 
+// Last check before an entry point's launches: the device, then a reset of
+// the thread's pending HIP error, so that launched() reports only the
+// failures of this call's own launches.
+flce_status ready_to_launch() {
+  const flce_status st = check_device();
+  if (st == FLCE_OK) (void)hipGetLastError();
+  return st;
+}
+
 flce_status launched() { return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_DEVICE; }
 
 char* at(void* ws, int64_t off) { return static_cast<char*>(ws) + off; }
@@ -886,7 +895,7 @@ flce_status flce_forward(const flce_params* params, const void* x, const void* w
   if (row_loss && !aligned(row_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   const Layout L = make_layout(p);
   if ((st = check_ws(ws, ws_bytes, L.fwd_end)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s);
@@ -907,7 +916,7 @@ flce_status flce_forward_metrics(const flce_params* params, const void* x, const
   if ((pred && !aligned(pred, 4)) || (accuracy && !aligned(accuracy, 4))) return FLCE_ERR_INVALID_ARGUMENT;
   const Layout L = make_layout(p);
   if ((st = check_ws(ws, ws_bytes, L.fwd_end)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s, pred, accuracy);
@@ -935,7 +944,7 @@ flce_status flce_backward(const flce_params* params, const void* x, const void* 
   if (grad_output && !aligned(grad_output, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   const Layout L = make_layout(p);
   if ((st = check_backward_args(p, L, lse, dx, dw, dbias, bias, ws, ws_bytes)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, s,
@@ -954,7 +963,7 @@ flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const v
   if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   const Layout L = make_layout(p);
   if ((st = check_backward_args(p, L, lse, dx, dw, dbias, bias, ws, ws_bytes)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16) {
     st = run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
@@ -986,7 +995,7 @@ flce_status flce_fused_fwd_bwd_stored(const flce_params* params, const void* x, 
   if (bias && (!dbias || !aligned(dbias, 4))) return FLCE_ERR_INVALID_ARGUMENT;
   const StoredLayout S = make_stored_layout(p);
   if ((st = check_ws(ws, ws_bytes, S.end)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_fused_stored<uint16_t>(p, S, x, w, bias, targets, loss, lse, dx, dw, dbias, ws, s);
@@ -1019,7 +1028,7 @@ flce_status flce_ce_forward(const flce_params* params, const void* logits, const
   if (row_loss && !aligned(row_loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   const CeLayout L = make_ce_layout(p);
   if ((st = check_ws(ws, ws_bytes, L.end)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_ce<uint16_t>(p, L, logits, targets, loss, lse, row_loss, nullptr, nullptr, nullptr, ws, s, 0);
@@ -1040,7 +1049,7 @@ flce_status flce_ce_forward_metrics(const flce_params* params, const void* logit
   if ((pred && !aligned(pred, 4)) || (accuracy && !aligned(accuracy, 4))) return FLCE_ERR_INVALID_ARGUMENT;
   const CeLayout L = make_ce_layout(p);
   if ((st = check_ws(ws, ws_bytes, L.end)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_ce<uint16_t>(p, L, logits, targets, loss, lse, row_loss, nullptr, nullptr, nullptr, ws, s, 0,
@@ -1062,7 +1071,7 @@ flce_status flce_ce_backward(const flce_params* params, const void* logits, cons
   if (grad_output && !aligned(grad_output, 4)) return FLCE_ERR_INVALID_ARGUMENT;
   const CeLayout L = make_ce_layout(p);
   if ((st = check_ws(ws, ws_bytes, L.end)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_ce<uint16_t>(p, L, logits, targets, nullptr, nullptr, nullptr, lse, grad_output, dlogits, ws,
@@ -1083,7 +1092,7 @@ flce_status flce_ce_fused_fwd_bwd(const flce_params* params, const void* logits,
   if (p.n > 0 && (!lse || !aligned(lse, 4))) return FLCE_ERR_INVALID_ARGUMENT;
   const CeLayout L = make_ce_layout(p);
   if ((st = check_ws(ws, ws_bytes, L.end)) != FLCE_OK) return st;
-  if ((st = check_device()) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.dtype == FLCE_DTYPE_BF16)
     return run_ce<uint16_t>(p, L, logits, targets, loss, lse, nullptr, nullptr, nullptr, dlogits, ws, s, 2);
