@@ -287,6 +287,37 @@ def test_autograd_function_and_grad_output():
     U.assert_close(U.host(b.grad), ref.db, "db")
 
 
+@pytest.mark.parametrize("stored", [False, True])
+def test_class_weights_with_zeros(stored):
+    """Class weights that are 0 for half the vocabulary (rows whose target
+    has weight 0 add nothing), and all 0: then the weighted mean divides by
+    0, which gives loss 0 and zero gradients, as with no valid row."""
+    n, d, v = 400, 72, 900
+    inp = small_problem(n, d, v, "bf16", bias=True, seed=31)
+    x = U.dev_tensor(inp["x"], "bf16")
+    w = U.dev_tensor(inp["w"], "bf16")
+    b = U.dev_tensor(inp["bias"], "bf16")
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    kw = dict(stored_logits=True, token_chunk=256) if stored else dict(vocab_slice=256)
+    half = np.where(np.arange(v) % 2 == 0, 0.0, 1.5)
+    for cw in (half, np.zeros(v)):
+        o = O.LossOptions(label_smoothing=0.1, class_weight=cw)
+        banner(f"class weights with zeros stored={stored} all_zero={not cw.any()}")
+        loss, lse, dx, dw, db = api.fused_fwd_bwd(x, w, t, b, class_weight=torch.tensor(cw, device="cuda"),
+                                                  **U.lib_opts(o), **kw)
+        torch.cuda.synchronize()
+        ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+        U.assert_lse(U.host(lse), ref.lse)
+        if cw.any():
+            U.assert_loss(float(loss.item()), ref.loss)
+            U.assert_close(U.host(dx), ref.dx, "dX")
+            U.assert_close(U.host(dw), ref.dw, "dW")
+            U.assert_close(U.host(db), ref.db, "db")
+        else:
+            assert ref.loss == 0.0 and float(loss.item()) == 0.0
+            assert torch.all(dx == 0) and torch.all(dw == 0) and torch.all(db == 0)
+
+
 def test_loss_module_on_an_lm_head():
     """The module form on an nn.Linear head: [B, T, D] hidden states, the
     head's weight and bias, class weights held as a buffer, gradients through
