@@ -227,10 +227,10 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
                         lse_square_scale=lse_square_scale, softcap=softcap, reduction=reduction,
                         class_weight=class_weight)
         ctx.mark_non_differentiable(lse)
-        return loss
+        return loss, lse
 
     @staticmethod
-    def backward(ctx, grad_loss):
+    def backward(ctx, grad_loss, grad_lse=None):   # lse is not differentiable
         x, weight, target, bias, lse = ctx.saved_tensors
         if ctx.opts["reduction"] == "none":
             raise RuntimeError("reduction='none' has no backward in the fused kernel; "
@@ -241,13 +241,17 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
 
 
 def linear_cross_entropy(x, weight, target, bias=None, ignore_index=-100, label_smoothing=0.0,
-                         lse_square_scale=0.0, softcap=0.0, reduction="mean", class_weight=None):
+                         lse_square_scale=0.0, softcap=0.0, reduction="mean", class_weight=None,
+                         return_lse=False):
     """Fused LM-head projection + cross-entropy; differentiable in x, weight
     and bias (reduction 'mean' or 'sum'; 'none' is forward-only).
     ``class_weight``: optional [V] per-class weights (torch's weighted
-    cross-entropy; not differentiated)."""
-    return LinearCrossEntropyFunction.apply(x, weight, target, bias, ignore_index, label_smoothing,
-                                            lse_square_scale, softcap, reduction, class_weight)
+    cross-entropy; not differentiated).  ``return_lse``: also return the
+    per-row log-sum-exp (fp32 [N], 0 on ignored rows; not differentiable)."""
+    loss, lse = LinearCrossEntropyFunction.apply(x, weight, target, bias, ignore_index,
+                                                 label_smoothing, lse_square_scale, softcap,
+                                                 reduction, class_weight)
+    return (loss, lse) if return_lse else loss
 
 
 class LinearCrossEntropyLoss(torch.nn.Module):
@@ -405,10 +409,10 @@ class CrossEntropyFunction(torch.autograd.Function):
         ctx.opts = dict(ignore_index=ignore_index, label_smoothing=label_smoothing,
                         lse_square_scale=lse_square_scale, softcap=softcap, reduction=reduction)
         ctx.mark_non_differentiable(lse)
-        return loss
+        return loss, lse
 
     @staticmethod
-    def backward(ctx, grad_loss):
+    def backward(ctx, grad_loss, grad_lse=None):   # lse is not differentiable
         logits, target, lse = ctx.saved_tensors
         if ctx.opts["reduction"] == "none":
             raise RuntimeError("reduction='none' is forward-only; use 'mean' or 'sum'")

@@ -277,11 +277,13 @@ def test_autograd_function_and_grad_output():
     w = U.dev_tensor(inp["w"], "bf16").requires_grad_(True)
     b = U.dev_tensor(inp["bias"], "bf16").requires_grad_(True)
     t = torch.from_numpy(inp["targets"]).cuda()
-    loss = api.linear_cross_entropy(x, w, t, b, label_smoothing=0.1)
+    loss, lse = api.linear_cross_entropy(x, w, t, b, label_smoothing=0.1, return_lse=True)
+    assert not lse.requires_grad
     (2.5 * loss).backward()
     o = O.LossOptions(label_smoothing=0.1)
     ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o, grad_output=2.5)
     U.assert_loss(float(loss.item()), ref.loss)
+    U.assert_lse(U.host(lse), ref.lse)
     U.assert_close(U.host(x.grad), ref.dx, "dX")
     U.assert_close(U.host(w.grad), ref.dw, "dW")
     U.assert_close(U.host(b.grad), ref.db, "db")
