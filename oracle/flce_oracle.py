@@ -54,7 +54,7 @@ pinned by tests in ``tests/test_oracle_pins.py`` except where a docstring says
 from __future__ import annotations
 
 import dataclasses
-from typing import Iterator, Optional, Tuple
+from typing import Optional, Tuple
 
 import numpy as np
 
@@ -297,27 +297,6 @@ def forward_backward(x, w, bias, targets, opts: LossOptions,
             dw += g.T @ x[sl]
         db += g.sum(axis=0)
     return Result(reduce_loss(rl, nv, opts), lse, rl, nv, dx, dw, db)
-
-
-def dw_blocks(x, w, bias, targets, opts: LossOptions, grad_output: float = 1.0,
-              n_valid: Optional[int] = None, vocab_block: int = 16384
-              ) -> Iterator[Tuple[int, int, np.ndarray]]:
-    """dW streamed by vocabulary blocks (v0, v1, dW[v0:v1]) so a large fp64
-    weight gradient is never held whole.  Same arithmetic as
-    ``forward_backward``; the LSE is taken over the full vocabulary first."""
-    x, w, bias = to_f64(x), to_f64(w), to_f64(bias)
-    targets = np.asarray(targets)
-    valid = valid_rows(targets, opts)
-    nv = mean_denominator(targets, opts) if n_valid is None else n_valid
-    scale = grad_scale(opts, nv, grad_output)
-    v = w.shape[0]
-    z = logits(x, w, bias, opts.softcap)
-    l = log_sum_exp(z)
-    g = grad_logits(z, l, targets, opts) * scale
-    del z
-    for v0 in range(0, v, vocab_block):
-        v1 = min(v, v0 + vocab_block)
-        yield v0, v1, g[:, v0:v1].T @ x
 
 
 # ------------------------------------------------- cross-entropy on logits

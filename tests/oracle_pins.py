@@ -581,6 +581,28 @@ def pin_class_weight_unit_and_fd(O, directions=8, seed=29):
             assert abs(fd - an) <= 1e-7 * gn + 1e-12, (feats, k, fd, an)
 
 
+def pin_bf16_widening(O):
+    """The exact widening of stored bf16 bit patterns (uint16) agrees with
+    torch's bfloat16 -> float64 conversion on random values and on zeros,
+    infinities, the largest and smallest normals and subnormals; fp32 arrays
+    widen unchanged."""
+    import torch
+    g = torch.Generator().manual_seed(13)
+    vals = torch.cat([torch.randn(4096, generator=g) * 10.0 ** torch.randint(-30, 30, (4096,), generator=g),
+                      torch.tensor([0.0, -0.0, float("inf"), float("-inf"), 3.3895e38, -3.3895e38,
+                                    1.1755e-38, 9.2e-41, -9.2e-41, 1.0, -2.0])])
+    b = vals.to(torch.bfloat16)
+    bits = b.view(torch.int16).numpy().view(np.uint16)
+    got = O.to_f64(bits)
+    want = b.to(torch.float64).numpy()
+    assert got.dtype == np.float64
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    f = np.random.default_rng(3).standard_normal(100).astype(np.float32)
+    assert np.array_equal(O.to_f64(f), f.astype(np.float64))
+    assert O.to_f64(None) is None
+
+
 ALL_PINS = [
     pin_uniform_logits, pin_single_class, pin_two_classes, pin_gradient_row_sums,
     pin_shift_invariance, pin_batch_additivity, pin_vocab_permutation,
@@ -588,5 +610,5 @@ ALL_PINS = [
     pin_torch_cross_entropy, pin_finite_differences, pin_brute_force,
     pin_gaussian_lse_level, pin_logits_identity_linear, pin_logits_torch,
     pin_logits_finite_differences, pin_megatron_smoothing, pin_predicted_tokens,
-    pin_class_weight_torch, pin_class_weight_unit_and_fd,
+    pin_class_weight_torch, pin_class_weight_unit_and_fd, pin_bf16_widening,
 ]

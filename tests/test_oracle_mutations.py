@@ -194,12 +194,22 @@ def mut_weighted_smoothing_unweighted(m):
     m.grad_logits = grad_logits
 
 
+def mut_bf16_as_fp16(m):
+    orig = m.to_f64
+
+    def to_f64(a):
+        if a is not None and a.dtype == np.uint16:
+            return a.view(np.float16).astype(np.float64)          # the bits read as IEEE half
+        return orig(a)
+    m.to_f64 = to_f64
+
+
 MUTATIONS = [mut_drop_smoothing_sum, mut_zloss_grad_sign, mut_no_softcap_derivative,
              mut_target_off_by_one, mut_lse_missing_max, mut_mean_over_all_rows,
              mut_online_no_rescale, mut_smoothing_over_v_minus_1, mut_transposed_dw,
              mut_logits_ignore_softcap, mut_logits_unscaled_grad, mut_megatron_plain_eps,
              mut_argmax_last_tie, mut_accuracy_over_all_rows, mut_weighted_mean_over_rows,
-             mut_weighted_smoothing_unweighted]
+             mut_weighted_smoothing_unweighted, mut_bf16_as_fp16]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
