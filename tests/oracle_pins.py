@@ -581,6 +581,27 @@ def pin_class_weight_unit_and_fd(O, directions=8, seed=29):
             assert abs(fd - an) <= 1e-7 * gn + 1e-12, (feats, k, fd, an)
 
 
+def pin_target_validation(O):
+    """Targets outside [0, V) that are not ignore_index are refused; the
+    ignore index itself is accepted even when it lies inside [0, V), and then
+    those rows are the ignored ones."""
+    x, w, b, t = _problem(n=12, d=8, v=10, seed=4, ignore=0)
+    for bad in (10, -3):
+        tb = t.copy()
+        tb[5] = bad
+        try:
+            O.forward(x, w, b, tb, _opts(O))
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"target {bad} accepted")
+    o = _opts(O, ignore_index=3)
+    t2 = t.copy()
+    t2[:4] = 3
+    r = O.forward(x, w, b, t2, o)
+    assert np.all(r.row_loss[t2 == 3] == 0.0) and r.n_valid == int((t2 != 3).sum())
+
+
 def pin_bf16_widening(O):
     """The exact widening of stored bf16 bit patterns (uint16) agrees with
     torch's bfloat16 -> float64 conversion on random values and on zeros,
@@ -611,4 +632,5 @@ ALL_PINS = [
     pin_gaussian_lse_level, pin_logits_identity_linear, pin_logits_torch,
     pin_logits_finite_differences, pin_megatron_smoothing, pin_predicted_tokens,
     pin_class_weight_torch, pin_class_weight_unit_and_fd, pin_bf16_widening,
+    pin_target_validation,
 ]
