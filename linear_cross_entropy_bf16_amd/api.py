@@ -421,8 +421,10 @@ class CrossEntropyFunction(torch.autograd.Function):
 
 
 def cross_entropy(logits, target, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0,
-                  softcap=0.0, reduction="mean"):
+                  softcap=0.0, reduction="mean", return_lse=False):
     """Cross-entropy of given logits [..., V]; differentiable in the logits
-    (reduction 'mean' or 'sum'; 'none' is forward-only)."""
-    return CrossEntropyFunction.apply(logits, target, ignore_index, label_smoothing,
-                                      lse_square_scale, softcap, reduction)
+    (reduction 'mean' or 'sum'; 'none' is forward-only).  ``return_lse``: also
+    return the per-row log-sum-exp (fp32 [N], not differentiable)."""
+    loss, lse = CrossEntropyFunction.apply(logits, target, ignore_index, label_smoothing,
+                                           lse_square_scale, softcap, reduction)
+    return (loss, lse) if return_lse else loss

@@ -162,6 +162,9 @@ def test_autograd_function_and_grad_output():
     torch.cuda.synchronize()
     ref = O.cross_entropy_on_logits(inp["logits"], inp["targets"], o, grad_output=3.0)
     U.assert_loss(float(loss.item()), ref.loss)
+    loss2, lse = api.cross_entropy(r.detach(), t, return_lse=True, **U.lib_opts(o))
+    assert float(loss2) == float(loss.detach()) and not lse.requires_grad
+    U.assert_lse(U.host(lse), ref.lse)
     U.assert_close(U.host(r.grad), ref.dx, "dlogits via autograd")
 
 
