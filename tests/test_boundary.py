@@ -250,3 +250,31 @@ def test_size_limits(lib):
     assert _lib.stored_workspace_size(P(n=(1 << 22) + 1)) == 0
     assert _lib.ce_workspace_size(P(n=1 << 22, v=(1 << 31) - 1)) > 0
     assert _lib.ce_workspace_size(P(n=(1 << 22) + 1)) == 0
+
+
+def test_loss_module_options():
+    """The module form validates its options on construction (no GPU)."""
+    import torch
+    from linear_cross_entropy_bf16_amd import LinearCrossEntropyLoss
+    m = LinearCrossEntropyLoss(label_smoothing=0.1, softcap=30.0, reduction="sum",
+                               class_weight=torch.ones(7))
+    assert "softcap=30.0" in repr(m) and m.class_weight.shape == (7,)
+    assert "class_weight" not in m.state_dict()      # not saved with a model
+    with pytest.raises(ValueError):
+        LinearCrossEntropyLoss(reduction="avg")
+    with pytest.raises(ValueError):
+        LinearCrossEntropyLoss(label_smoothing=1.5)
+
+
+def test_binding_refuses_host_tensors():
+    """Every entry point of the binding needs GPU tensors; host tensors are
+    refused before the library is called."""
+    import torch
+    from linear_cross_entropy_bf16_amd import api
+    x, w, t = torch.zeros(4, 8), torch.zeros(16, 8), torch.zeros(4, dtype=torch.int32)
+    for call in (lambda: api.forward(x, w, t), lambda: api.fused_fwd_bwd(x, w, t),
+                 lambda: api.linear_cross_entropy(x, w, t),
+                 lambda: api.cross_entropy(torch.zeros(4, 16), t),
+                 lambda: api.cross_entropy_fused_fwd_bwd(torch.zeros(4, 16), t)):
+        with pytest.raises(ValueError):
+            call()
