@@ -129,17 +129,19 @@ def test_large_sampled_rows(name):
         assert colsum.abs().max().item() <= 1e-3 * dw.double().abs().max().item() * 64
 
 
-def test_ragged_vocab_with_multi_tile_chunks():
-    """Enough tiles for four vocabulary tiles per forward workgroup, and V not
-    a multiple of 256: the whole tiles and the partial last tile come from two
-    launches whose partials are merged.  256 sampled rows of LSE, row loss and
-    dX against the oracle; bias, softcap and label smoothing on."""
-    n, d, v = 16384, 256, 65535
-    banner(f"ragged vocabulary, multi-tile chunks n={n} d={d} v={v}")
-    inp = small_problem(n, d, v, bias=True, seed=11)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_vocab_with_multi_tile_chunks(dtype):
+    """Enough tiles for four vocabulary tiles per forward workgroup (bf16; the
+    fp32 register-staged path at this size runs two), and V not a multiple of
+    256: the whole tiles and the partial last tile come from two launches
+    whose partials are merged.  256 sampled rows of LSE, row loss and dX
+    against the oracle; bias, softcap and label smoothing on."""
+    n, d, v = (16384, 256, 65535) if dtype == "bf16" else (8192, 64, 65537)
+    banner(f"ragged vocabulary, multi-tile chunks {dtype} n={n} d={d} v={v}")
+    inp = small_problem(n, d, v, dtype, bias=True, seed=11)
     o = O.LossOptions(IGN, 0.1, 1e-4, 20.0, "mean")
-    x, w = U.dev_tensor(inp["x"], "bf16"), U.dev_tensor(inp["w"], "bf16")
-    b = U.dev_tensor(inp["bias"], "bf16")
+    x, w = U.dev_tensor(inp["x"], dtype), U.dev_tensor(inp["w"], dtype)
+    b = U.dev_tensor(inp["bias"], dtype)
     t = torch.from_numpy(inp["targets"]).to("cuda")
     loss, lse, row_loss = api.forward(x, w, t, b, check_targets=True, **U.lib_opts(o))
     dx, dw, db = api.backward(x, w, t, lse, None, b, **U.lib_opts(o))
