@@ -414,6 +414,35 @@ def test_forward_metrics_exact_ties():
         assert p[0] == 300
 
 
+@pytest.mark.timeout(900)
+def test_forward_metrics_full_size():
+    """8192 x 4096 x 128256 (one data-parallel share of the headline batch):
+    the predicted tokens of 256 sampled rows against the argmax of the fp64
+    logits (near-ties allowed), ignored rows -1 everywhere, the accuracy equal
+    to the hits of the whole returned prediction array, and the forward's
+    other outputs unchanged by the metrics."""
+    wl = W.WORKLOADS["llama3_8b_seq"]
+    banner(f"forward metrics {wl}")
+    inp = W.generate(wl)
+    inp["targets"][::17] = IGN                        # some ignored rows as well
+    o = U.options(wl)
+    x = U.dev_tensor(inp["x"], wl.dtype)
+    w = U.dev_tensor(inp["w"], wl.dtype)
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, rl, pred, acc = api.forward(x, w, t, None, return_metrics=True, **U.lib_opts(o))
+    loss0, lse0, rl0 = api.forward(x, w, t, None, **U.lib_opts(o))
+    torch.cuda.synchronize()
+    assert torch.equal(lse, lse0) and torch.equal(rl, rl0) and float(loss) == float(loss0)
+    p = pred.cpu().numpy()
+    valid = inp["targets"] != IGN
+    assert np.all(p[~valid] == -1) and np.all((p[valid] >= 0) & (p[valid] < wl.v))
+    hits = int(((p == inp["targets"]) & valid).sum())
+    assert abs(float(acc) - hits / int(valid.sum())) <= 1e-6
+    rows = W.sample_rows(wl, 256, salt=9)
+    z = O.logits(O.to_f64(inp["x"][rows]), O.to_f64(inp["w"]), None, o.softcap)
+    U.check_predictions(p[rows], float(acc), z, inp["targets"][rows], o, n_valid=int(valid.sum()))
+
+
 # ------------------------------------------------- token chunks, bf16 dW
 
 def _fused_opts(inp, dtype, o, to_host=True, **kw):
