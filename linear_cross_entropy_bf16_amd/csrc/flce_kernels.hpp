@@ -373,7 +373,7 @@ void k_fwd(FwdArgs<T> a) {
   for (int64_t vt = vt_first; vt < vt_end; ++vt) {
     const int64_t v0 = vt * tile::kM;
     f32x16 acc[4][4];
-    gemm_tile<T, true>(A, B, v0, n0, a.d, lds, acc);
+    gemm_tile<T, true, false>(A, B, v0, n0, a.d, lds, acc);   // one masked loop (see gemm_tile_dma)
     if (vt + 1 < vt_end) gemm_prefetch(A, B, v0 + tile::kM, n0, lds);
     // tile-local vocabulary row of (mb, r) = vw + mb*32 + 8(r/4) + r%4
     const int vw = wm * 128 + 4 * (lane >> 5);
