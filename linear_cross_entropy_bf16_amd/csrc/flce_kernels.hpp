@@ -279,9 +279,14 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
         for (int r = 0; r < 16; ++r) zt = r == idx ? z[r] : zt;
         a.zt[n0 + wn * 128 + nb * 32 + (lane & 31)] = zt;
       }
-      float mt = z[0];
+      // block maximum as a tree of v_max_f32 (a compare-select chain here
+      // cost three issue slots and a hazard wait per element, in series)
+      float m8[8], m4[4];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmax_fast(mt, z[r]);
+      for (int k = 0; k < 8; ++k) m8[k] = __builtin_fmaxf(z[2 * k], z[2 * k + 1]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m4[k] = __builtin_fmaxf(m8[2 * k], m8[2 * k + 1]);
+      const float mt = __builtin_fmaxf(__builtin_fmaxf(m4[0], m4[1]), __builtin_fmaxf(m4[2], m4[3]));
       if (kArgmax) {
         // r ascends with the vocabulary index: the first r holding the block
         // maximum is its lowest index; blocks and tiles arrive in ascending
