@@ -114,11 +114,22 @@ struct RowStats {
   float m, d, s;
 };
 
+// maximum of N (a power of two) values as a tree of v_max_f32
+template <int N>
+__device__ __forceinline__ float tree_max(const float (&z)[N]) {
+  if constexpr (N == 1) {
+    return z[0];
+  } else {
+    float h[N / 2];
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) h[k] = __builtin_fmaxf(z[2 * k], z[2 * k + 1]);
+    return tree_max<N / 2>(h);
+  }
+}
+
 template <int N, bool kSumZ>
 __device__ __forceinline__ void stats_add(RowStats& st, const float (&z)[N]) {
-  float mx = z[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) mx = fmax_fast(mx, z[i]);
+  const float mx = tree_max<N>(z);
   if (kSumZ) {
 #pragma unroll
     for (int i = 0; i < N; ++i) st.s += z[i];
