@@ -194,6 +194,36 @@ def test_ragged_shapes(dtype, n, d, v, slice_):
                    vocab_slice=slice_)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("n,d,v", [(40, 1 << 20, 300), (1 << 22, 8, 20)])
+def test_maximum_sizes(n, d, v):
+    """The largest hidden size and batch the library accepts (D = 2^20: the
+    K-major row offsets of a tile reach 2^29 bytes; N = 2^22: the largest
+    packed-row and token-tile counts), with small other dimensions so the
+    oracle stays quick: loss, LSE, dX and dW against the oracle (sampled rows
+    for N = 2^22)."""
+    banner(f"maximum sizes n={n} d={d} v={v}")
+    inp = small_problem(n, d, v, "bf16", bias=True, seed=n % 97 + d % 89, ignore_frac=0.1)
+    o = O.LossOptions(label_smoothing=0.1, lse_square_scale=1e-3)
+    if n <= 4096:
+        U.compare_full(inp, "bf16", o)
+        return
+    x = U.dev_tensor(inp["x"], "bf16")
+    w = U.dev_tensor(inp["w"], "bf16")
+    b = U.dev_tensor(inp["bias"], "bf16")
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    loss, lse, dx, dw, db = api.fused_fwd_bwd(x, w, t, b, **U.lib_opts(o))
+    torch.cuda.synchronize()
+    ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+    U.assert_loss(float(loss), ref.loss)
+    rows = np.random.default_rng(1).choice(n, 4096, replace=False)
+    rows_d = torch.from_numpy(rows).cuda()
+    U.assert_lse(U.host(lse[rows_d]), ref.lse[rows])
+    U.assert_close(U.host(dx[rows_d]), ref.dx[rows], "dX rows")
+    U.assert_close(U.host(dw), ref.dw, "dW")
+    U.assert_close(U.host(db), ref.db, "db")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_empty_batch(dtype):
     inp = small_problem(0, 64, 100, dtype, bias=True)
