@@ -96,6 +96,19 @@ def test_row_split_residues(dtype, v):
 
 
 @pytest.mark.parametrize("mode", ["fused", "separate"])
+@pytest.mark.parametrize("dtype,v", [("bf16", 256000), ("f32", 200003)])
+def test_rows_longer_than_the_register_cache(dtype, v, mode):
+    """Rows longer than what the fused kernel holds in registers (129024 bf16
+    or 64512 fp32 entries per row): the rest of the row streams through its
+    second loop in both passes; fp32 with an odd V also leaves most rows
+    unaligned.  Every output against the oracle."""
+    inp = logits_problem(24, v, dtype, seed=v % 101, spread=2.0)
+    banner(f"long rows {dtype} v={v} {mode}")
+    compare(inp, dtype, O.LossOptions(label_smoothing=0.1, lse_square_scale=1e-3, softcap=8.0), mode=mode)
+    compare(inp, dtype, O.LossOptions(), mode=mode, inplace=True)
+
+
+@pytest.mark.parametrize("mode", ["fused", "separate"])
 def test_in_place_gradient(mode):
     inp = logits_problem(129, 999, "bf16", seed=5)
     banner(f"in place {mode}")
