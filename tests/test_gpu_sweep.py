@@ -2,8 +2,8 @@
 
 Each case draws its sizes and options from its own seed: ragged N, D and V,
 bf16 or fp32, bias, label smoothing, z-loss, softcap, mean or sum, a share of
-ignored rows, class weights, and the schedule (recompute with a vocabulary
-slice, token chunks and bf16 dW, or stored logits).  Every output of the fused
+ignored rows, class weights, bf16 dW, and the schedule (recompute with a
+vocabulary slice and token chunks, or stored logits).  Every output of the fused
 call is compared with the fp64 oracle element by element, at the same bars as
 the other parity tests."""
 import numpy as np
@@ -78,7 +78,7 @@ def test_option_sweep(case):
     if cw is not None:
         kw["class_weight"] = torch.tensor(cw, dtype=torch.float32, device="cuda")
     if c["schedule"] == "stored":
-        kw.update(stored_logits=True, token_chunk=c["token_chunk"])
+        kw.update(stored_logits=True, token_chunk=c["token_chunk"], dw_bf16=c["dw_bf16"])
     else:
         kw.update(vocab_slice=c["vocab_slice"], token_chunk=c["token_chunk"], dw_bf16=c["dw_bf16"])
     loss, lse, dx, dw, db = api.fused_fwd_bwd(x, w, t, b, **kw)
