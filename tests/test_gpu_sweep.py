@@ -150,3 +150,48 @@ def test_logits_option_sweep(case):
     assert np.all(got_lse[~valid] == 0.0) and np.all(got_g[~valid] == 0.0)
     if valid.any():
         U.assert_close(got_g, ref.dx, "dlogits")
+
+
+@pytest.mark.parametrize("case", range(60))
+def test_separate_calls_sweep(case):
+    """flce_forward (with predicted tokens and accuracy in half the cases)
+    then flce_backward with an upstream gradient other than 1, over the same
+    kinds of random options as the fused sweep (token chunks, bf16 dW, class
+    weights): every output against the oracle."""
+    seed = 7000 + case
+    c = draw_case(seed)
+    rng = np.random.default_rng(seed + 11)
+    metrics = bool(rng.random() < 0.5)
+    g_out = float(rng.choice([0.5, 2.0, -1.5]))
+    print(f"\n[gpu-sweep] separate calls case {case} seed {seed}: {c} metrics={metrics} g={g_out}",
+          flush=True)
+    inp, cw = make_inputs(c, seed)
+    o = O.LossOptions(label_smoothing=c["label_smoothing"], lse_square_scale=c["lse_square_scale"],
+                      softcap=c["softcap"], reduction=c["reduction"], class_weight=cw)
+    dtype = c["dtype"]
+    x = U.dev_tensor(inp["x"], dtype)
+    w = U.dev_tensor(inp["w"], dtype)
+    b = U.dev_tensor(inp["bias"], dtype) if inp["bias"] is not None else None
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    cwt = torch.tensor(cw, dtype=torch.float32, device="cuda") if cw is not None else None
+    opts = U.lib_opts(o)
+    out = api.forward(x, w, t, b, return_metrics=metrics, class_weight=cwt, **opts)
+    loss, lse, row_loss = out[:3]
+    go = torch.tensor([g_out], dtype=torch.float32, device="cuda")
+    dx, dw, db = api.backward(x, w, t, lse, go, b, vocab_slice=c["vocab_slice"],
+                              token_chunk=c["token_chunk"], dw_bf16=c["dw_bf16"], class_weight=cwt,
+                              **opts)
+    torch.cuda.synchronize()
+    ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o, grad_output=g_out)
+    U.assert_loss(float(loss.item()), ref.loss)
+    valid = inp["targets"] != IGN
+    U.assert_lse(U.host(lse)[valid], ref.lse[valid])
+    if valid.any():
+        U.assert_close(U.host(dx), ref.dx, "dX")
+        U.assert_close(U.host(dw), ref.dw, "dW")
+        if c["bias"]:
+            U.assert_close(U.host(db), ref.db, "db")
+    if metrics:
+        pred, acc = out[3], out[4]
+        z = O.logits(O.to_f64(inp["x"]), O.to_f64(inp["w"]), O.to_f64(inp["bias"]), o.softcap)
+        U.check_predictions(pred.cpu().numpy(), float(acc), z, inp["targets"], o)
