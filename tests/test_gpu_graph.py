@@ -117,3 +117,24 @@ def test_logits_step_graph():
 
     g = capture(step)
     check_replays(g, out, eager, (r,), (r2,))
+
+
+def test_calls_follow_the_current_stream():
+    """A call made while a side stream is current is enqueued there: its
+    results, read after that stream is synchronised, equal a call on the
+    default stream bit for bit."""
+    print("\n[gpu-graph] side stream", flush=True)
+    n, d, v = 600, 72, 2000
+    x, w, b, t = problem(n, d, v, seed=21)
+    opts = dict(label_smoothing=0.1, softcap=12.0)
+    want = api.fused_fwd_bwd(x, w, t, b, **opts)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = api.fused_fwd_bwd(x, w, t, b, **opts)
+        lse_side = api.forward(x, w, t, b, **opts)[1]
+    side.synchronize()
+    for a, c in zip(got, want):
+        assert torch.equal(a, c)
+    assert torch.equal(lse_side, want[1])
