@@ -104,12 +104,21 @@ def fused(p, ws_bytes=1 << 40, **kw):
                               None)
 
 
+def stored(p, ws_bytes=1 << 40, **kw):
+    args = dict(x=FAKE, w=FAKE, bias=None, t=FAKE, loss=FAKE, lse=FAKE, dx=FAKE, dw=FAKE, db=None,
+                ws=FAKE)
+    args.update(kw)
+    return _lib.fused_fwd_bwd_stored(p, args["x"], args["w"], args["bias"], args["t"], args["loss"],
+                                     args["lse"], args["dx"], args["dw"], args["db"], args["ws"],
+                                     ws_bytes, None)
+
+
 INVALID = _lib.FLCE_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("call", ["forward", "backward", "fused"])
+@pytest.mark.parametrize("call", ["forward", "backward", "fused", "stored"])
 def test_host_validation(lib, call):
-    f = {"forward": fwd, "backward": bwd, "fused": fused}[call]
+    f = {"forward": fwd, "backward": bwd, "fused": fused, "stored": stored}[call]
     assert f(P(d=12)) == INVALID                    # D not a multiple of 8
     assert f(P(v=0)) == INVALID
     assert f(P(n=-5)) == INVALID
@@ -125,7 +134,8 @@ def test_host_validation(lib, call):
     assert f(P(), ws=FAKE + 64) == INVALID          # workspace not 256-byte aligned
     assert f(P(), ws=None) == INVALID
     assert f(P(), ws_bytes=16) == _lib.FLCE_ERR_WORKSPACE_TOO_SMALL
-    need = _lib.workspace_size(P(), call != "forward")
+    need = (_lib.stored_workspace_size(P()) if call == "stored"
+            else _lib.workspace_size(P(), call != "forward"))
     assert f(P(), ws_bytes=need - 1) == _lib.FLCE_ERR_WORKSPACE_TOO_SMALL
     if call == "forward":
         assert f(P(), loss=None) == INVALID
@@ -140,6 +150,7 @@ def test_backward_refuses_reduction_none(lib):
     p = P(reduction=2)
     assert bwd(p) == _lib.FLCE_ERR_UNSUPPORTED
     assert fused(p) == _lib.FLCE_ERR_UNSUPPORTED
+    assert stored(p) == _lib.FLCE_ERR_UNSUPPORTED
 
 
 def test_null_params(lib):
