@@ -43,6 +43,24 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def timed_steps(run, steps: int, stream):
+    """Runs ``steps`` calls of ``run`` on ``stream`` between K + 1 events, one
+    before each step and one after the last, and returns the mean over the
+    whole timed region with the median and the fastest single step (ms)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mid = steps // 2
+    p50 = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return ev[0].elapsed_time(ev[steps]) / steps, p50, per[0]
+
+
 def kernel_source_hash(kernel: str = "k_fwd") -> str:
     h = hashlib.sha256()
     for name in TRAFFIC[kernel][1]:
@@ -65,26 +83,52 @@ def measured_traffic(workload: str, kernel: str = "k_fwd"):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, max_rows: int):
-    """The fp64 oracle as it stands on a bounded row sample of the workload
-    (full D and V, dW included)."""
-    import numpy as np
-    from oracle import flce_oracle as O
+def blas_threads() -> int:
+    """Threads the BLAS behind numpy will use (what the oracle's products run on)."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+        info = threadpool_info()
+        return max((i.get("num_threads") or 1) for i in info) if info else 1
     except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def one_thread_rate(fn, rows: int):
+    """tokens/s of fn() over `rows` rows with the BLAS held to one thread, or
+    None where the thread count cannot be limited."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        return None
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+    return {"value": round(rows / dt, 3), "rows": rows, "seconds": round(dt, 2)}
+
+
+def cpu_baseline(wl, inp, max_rows: int):
+    """The fp64 oracle as it stands on a bounded row sample of the workload
+    (full D and V, dW included), on all the threads its BLAS uses, and on a
+    sixteenth of the sample with one thread.  Its cost is linear in the rows
+    at fixed D and V, so tokens/s carries over to the whole batch."""
+    import numpy as np
+    from oracle import flce_oracle as O
+    threads = blas_threads()
     rows = np.arange(min(max_rows, wl.n))
     o = O.LossOptions(wl.ignore_index, wl.label_smoothing, wl.lse_square_scale, wl.softcap,
                       wl.reduction)
     t0 = time.perf_counter()
     O.forward_backward(inp["x"][rows], inp["w"], inp["bias"], inp["targets"][rows], o)
     dt = time.perf_counter() - t0
+    r1 = rows[:max(16, len(rows) // 16)]
+    one = one_thread_rate(lambda: O.forward_backward(inp["x"][r1], inp["w"], inp["bias"],
+                                                     inp["targets"][r1], o), len(r1))
     return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "nproc": os.cpu_count(), "one_thread": one,
             "sample": f"first {len(rows)} of {wl.n} rows of {wl.name} (full D={wl.d}, V={wl.v}, dW "
-                      f"included), fp64 numpy, {dt:.1f} s"}
+                      f"included), fp64 numpy, {dt:.1f} s; tokens/s is per row, so it holds for "
+                      f"the whole batch (cost linear in N)"}
 
 
 def main():
@@ -195,13 +239,8 @@ def main():
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        run()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms, ms_p50, ms_min = timed_steps(run, args.steps, stream)
     wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1) / args.steps
     peak_bytes = torch.cuda.max_memory_allocated(dev)
     loss = float(out[0].item())
     log(f"{ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}), loss {loss:.6f}")
@@ -266,6 +305,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_p50": round(ms_p50, 3),
+        "ms_min": round(ms_min, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tokens_per_s / PAGES_TOKENS_PER_S, 4) if wl.name == "llama3_8b_batch8" else None,
@@ -334,20 +375,14 @@ def bench_stored_variant(args, wl, x, w, t, b, opts, dev, n_valid):
     step()
     steps = max(3, args.steps // 2)
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, ms_p50, ms_min = timed_steps(step, steps, stream)
     peak = PEAK_BF16_TFLOPS
     tflops = 6.0 * wl.n * wl.d * wl.v / (ms * 1e-3) / 1e12
     tflops_valid = 6.0 * n_valid * wl.d * wl.v / (ms * 1e-3) / 1e12
     log(f"stored-logits schedule: {ms:.3f} ms/step")
     res = {"schedule": "stored logits (6 N D V: forward GEMM keeps each 8192-token chunk's logits, "
                        "no recompute)", "steps": steps, "ms_per_step": round(ms, 3),
+           "ms_p50": round(ms_p50, 3), "ms_min": round(ms_min, 3),
            "tokens_per_s": round(wl.n / (ms * 1e-3), 1),
            "vs_baseline": round(wl.n / (ms * 1e-3) / PAGES_TOKENS_PER_S, 4)
            if wl.name == "llama3_8b_batch8" else None,
@@ -362,19 +397,17 @@ def bench_stored_variant(args, wl, x, w, t, b, opts, dev, n_valid):
 def cpu_baseline_ce(wl, inp, max_rows: int):
     """The fp64 oracle on the first rows of a logits workload (full V)."""
     from oracle import flce_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     rows = min(max_rows, wl.n)
     o = O.LossOptions(wl.ignore_index, wl.label_smoothing, wl.lse_square_scale, wl.softcap,
                       wl.reduction)
     t0 = time.perf_counter()
     O.cross_entropy_on_logits(inp["logits"][:rows], inp["targets"][:rows], o)
     dt = time.perf_counter() - t0
+    r1 = max(1, rows // 4)
+    one = one_thread_rate(lambda: O.cross_entropy_on_logits(inp["logits"][:r1], inp["targets"][:r1], o), r1)
     return {"value": round(rows / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "nproc": os.cpu_count(), "one_thread": one,
             "sample": f"first {rows} of {wl.n} rows of {wl.name} (full V={wl.v}, loss and "
                       f"dL/dlogits), fp64 numpy, {dt:.1f} s"}
 
@@ -428,7 +461,7 @@ def bench_ce(args, wl):
         step()
     log(f"timing {args.steps} steps")
     wall0 = time.perf_counter()
-    ms = timed(step, args.steps)
+    ms, ms_p50, ms_min = timed_steps(step, args.steps, stream)
     wall = time.perf_counter() - wall0
     peak_bytes = torch.cuda.max_memory_allocated(dev)
     loss = float(out[0].item())
@@ -481,6 +514,8 @@ def bench_ce(args, wl):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_p50": round(ms_p50, 4),
+        "ms_min": round(ms_min, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

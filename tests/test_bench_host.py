@@ -1,6 +1,7 @@
 """bench.py's host-side logic on the CPU: the one-GPU refusal, the guard that
 drops committed HBM-traffic counters taken on other kernel sources or another
-workload, and the shape of the CPU oracle baseline record."""
+workload, and the shape of the CPU oracle baseline record (all threads and
+one thread)."""
 import json
 import os
 import subprocess
@@ -64,6 +65,8 @@ def test_cpu_baseline_record():
     assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
     assert "first 32 of" in rec["sample"]
+    assert rec["nproc"] >= 1
+    assert rec["one_thread"]["rows"] == 16 and rec["one_thread"]["value"] > 0
 
 
 def test_cpu_baseline_record_logits():
@@ -72,3 +75,4 @@ def test_cpu_baseline_record_logits():
     rec = bench.cpu_baseline_ce(wl, inp, 4)
     assert rec["kind"] == "oracle" and rec["value"] > 0
     assert "first 4 of" in rec["sample"]
+    assert rec["one_thread"]["rows"] == 1 and rec["one_thread"]["value"] > 0
