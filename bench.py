@@ -134,8 +134,8 @@ def cpu_baseline(wl, inp, max_rows: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b_batch8")
     ap.add_argument("--vocab-slice", type=int, default=0)
     ap.add_argument("--token-chunk", type=int, default=0,
