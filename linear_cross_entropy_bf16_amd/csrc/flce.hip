@@ -13,8 +13,7 @@
 #include <type_traits>
 
 #include "flce.h"
-#include "flce_kernels.hpp"
-#include "flce_ce.hpp"
+#include "flce_launch.hpp"
 
 namespace {
 
@@ -216,43 +215,23 @@ void fill(float* p, int64_t count, float value, hipStream_t s) {
 int64_t grid8(int64_t tiles) { return round_up(tiles, 8); }
 
 // ----------------------------------------------------------------- forward
-template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kArgmax, bool kStore>
-void launch_fwd(const flce::FwdArgs<T>& a, const Layout& L, hipStream_t s) {
-  if (L.main_chunks > 0) {
-    flce::FwdArgs<T> m = a;
-    m.vt_base = 0;
-    m.vt_end = L.v_full;
-    m.chunk_base = 0;
-    m.n_chunks = L.main_chunks;
-    m.tiles_per_chunk = L.tiles_per_chunk;
-    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, false, kArgmax, kStore>),
-                       dim3(static_cast<unsigned>(grid8(L.n_tiles * m.n_chunks))),
-                       dim3(tile::kThreads), 0, s, m);
-  }
-  if (L.v_full < L.v_tiles) {
-    flce::FwdArgs<T> t = a;
-    t.vt_base = L.v_full;
-    t.vt_end = L.v_tiles;
-    t.chunk_base = L.main_chunks;
-    t.n_chunks = 1;
-    t.tiles_per_chunk = 1;
-    hipLaunchKernelGGL((flce::k_fwd<T, kBias, kSoftcap, kSumZ, true, kArgmax, kStore>),
-                       dim3(static_cast<unsigned>(grid8(L.n_tiles))), dim3(tile::kThreads), 0, s, t);
-  }
+flce::FwdGrid fwd_grid(const Layout& L) {
+  return flce::FwdGrid{L.n_tiles, L.v_full, L.v_tiles, L.main_chunks, L.tiles_per_chunk};
 }
 
-// kStore (the stored-logits schedule) requires a.zs; it never combines with kArgmax.
-template <typename T, bool kArgmax, bool kStore = false>
-void dispatch_fwd(const flce::FwdArgs<T>& a, const Layout& L, int key, hipStream_t s) {
+// key: bit 0 bias, bit 1 softcap, bit 2 sum of z (label smoothing)
+template <typename T>
+void dispatch_fwd(const flce::FwdArgs<T>& a, const flce::FwdGrid& g, int key, flce::FwdMode mode,
+                  hipStream_t s) {
   switch (key) {
-    case 0: launch_fwd<T, false, false, false, kArgmax, kStore>(a, L, s); break;
-    case 1: launch_fwd<T, true, false, false, kArgmax, kStore>(a, L, s); break;
-    case 2: launch_fwd<T, false, true, false, kArgmax, kStore>(a, L, s); break;
-    case 3: launch_fwd<T, true, true, false, kArgmax, kStore>(a, L, s); break;
-    case 4: launch_fwd<T, false, false, true, kArgmax, kStore>(a, L, s); break;
-    case 5: launch_fwd<T, true, false, true, kArgmax, kStore>(a, L, s); break;
-    case 6: launch_fwd<T, false, true, true, kArgmax, kStore>(a, L, s); break;
-    default: launch_fwd<T, true, true, true, kArgmax, kStore>(a, L, s); break;
+    case 0: flce::launch_fwd<T, 0>(a, g, mode, s); break;
+    case 1: flce::launch_fwd<T, 1>(a, g, mode, s); break;
+    case 2: flce::launch_fwd<T, 2>(a, g, mode, s); break;
+    case 3: flce::launch_fwd<T, 3>(a, g, mode, s); break;
+    case 4: flce::launch_fwd<T, 4>(a, g, mode, s); break;
+    case 5: flce::launch_fwd<T, 5>(a, g, mode, s); break;
+    case 6: flce::launch_fwd<T, 6>(a, g, mode, s); break;
+    default: flce::launch_fwd<T, 7>(a, g, mode, s); break;
   }
 }
 
@@ -302,10 +281,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.weight = p.class_weight;
   const bool b = bias != nullptr, c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
   const int key = (b ? 1 : 0) | (c ? 2 : 0) | (z ? 4 : 0);
-  if (metrics)
-    dispatch_fwd<T, true>(a, L, key, s);
-  else
-    dispatch_fwd<T, false>(a, L, key, s);
+  dispatch_fwd<T>(a, fwd_grid(L), key, metrics ? flce::FwdMode::kArgmax : flce::FwdMode::kPlain, s);
   flce::MergeArgs m{};
   m.part_m = a.part_m;
   m.part_d = a.part_d;
@@ -347,23 +323,18 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
 }
 
 // ----------------------------------------------------------------- backward
-template <typename T, bool kBias, bool kSoftcap, bool kWeight>
-void launch_g(const flce::GArgs<T>& a, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((flce::k_bwd_g<T, kBias, kSoftcap, kWeight>), dim3(static_cast<unsigned>(grid)),
-                     dim3(tile::kThreads), 0, s, a);
-}
-
+// key: bit 0 bias, bit 1 softcap, bit 2 class weights
 template <typename T>
 void dispatch_g(const flce::GArgs<T>& a, int64_t grid, bool bias, bool softcap, hipStream_t s) {
   switch ((bias ? 1 : 0) | (softcap ? 2 : 0) | (a.weight ? 4 : 0)) {
-    case 0: launch_g<T, false, false, false>(a, grid, s); break;
-    case 1: launch_g<T, true, false, false>(a, grid, s); break;
-    case 2: launch_g<T, false, true, false>(a, grid, s); break;
-    case 3: launch_g<T, true, true, false>(a, grid, s); break;
-    case 4: launch_g<T, false, false, true>(a, grid, s); break;
-    case 5: launch_g<T, true, false, true>(a, grid, s); break;
-    case 6: launch_g<T, false, true, true>(a, grid, s); break;
-    default: launch_g<T, true, true, true>(a, grid, s); break;
+    case 0: flce::launch_g<T, 0>(a, grid, s); break;
+    case 1: flce::launch_g<T, 1>(a, grid, s); break;
+    case 2: flce::launch_g<T, 2>(a, grid, s); break;
+    case 3: flce::launch_g<T, 3>(a, grid, s); break;
+    case 4: flce::launch_g<T, 4>(a, grid, s); break;
+    case 5: flce::launch_g<T, 5>(a, grid, s); break;
+    case 6: flce::launch_g<T, 6>(a, grid, s); break;
+    default: flce::launch_g<T, 7>(a, grid, s); break;
   }
 }
 
@@ -378,7 +349,7 @@ void transpose(const T* in, int64_t rows, int64_t cols, int64_t ld_in, T* out, i
 }
 
 template <typename T, typename DW>
-void launch_dw(const T* xt, const T* gt, const flce_params& p, const Layout& L, int64_t v0, int64_t len,
+void run_dw(const T* xt, const T* gt, const flce_params& p, const Layout& L, int64_t v0, int64_t len,
                int64_t gcols, int64_t d_tiles, int64_t s_tiles, int64_t c0, bool accumulate,
                const Ctl* ctl, DW* dw, hipStream_t s) {
   flce::DwArgs<T, DW> wa{};
@@ -396,8 +367,7 @@ void launch_dw(const T* xt, const T* gt, const flce_params& p, const Layout& L, 
   wa.row0 = c0;
   wa.cap = L.chunk;
   wa.accumulate = accumulate ? 1 : 0;
-  hipLaunchKernelGGL((flce::k_dw<T, DW>), dim3(static_cast<unsigned>(grid8(d_tiles * s_tiles))),
-                     dim3(tile::kThreads), 0, s, wa);
+  flce::launch_dw<T, DW>(wa, grid8(d_tiles * s_tiles), s);
 }
 
 template <typename T>
@@ -475,10 +445,10 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
         dispatch_g<T>(ga, g_grid, has_bias, p.softcap > 0.f, s);
       }
       if (p.dw_bf16)
-        launch_dw<T, uint16_t>(xt, gt, p, L, v0, len, gcols, d_tiles, s_tiles, c0, ci > 0, ctl,
+        run_dw<T, uint16_t>(xt, gt, p, L, v0, len, gcols, d_tiles, s_tiles, c0, ci > 0, ctl,
                                static_cast<uint16_t*>(dw), s);
       else
-        launch_dw<T, float>(xt, gt, p, L, v0, len, gcols, d_tiles, s_tiles, c0, ci > 0, ctl,
+        run_dw<T, float>(xt, gt, p, L, v0, len, gcols, d_tiles, s_tiles, c0, ci > 0, ctl,
                             static_cast<float*>(dw), s);
       if (p.n > 0) {
         flce::DxArgs<T> xa{};
@@ -496,12 +466,7 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
         xa.first = si == 0;
         xa.d_tiles = d_tiles;
         const int64_t x_grid = grid8(d_tiles * c_tiles);   // upper bound: all rows valid
-        if (si + 1 == n_slices)
-          hipLaunchKernelGGL((flce::k_dx<T, true>), dim3(static_cast<unsigned>(x_grid)),
-                             dim3(tile::kThreads), 0, s, xa);
-        else
-          hipLaunchKernelGGL((flce::k_dx<T, false>), dim3(static_cast<unsigned>(x_grid)),
-                             dim3(tile::kThreads), 0, s, xa);
+        flce::launch_dx<T>(xa, x_grid, si + 1 == n_slices, s);
       }
       if (has_bias)
         hipLaunchKernelGGL((flce::k_db<T>), dim3(static_cast<unsigned>(cdiv(len, 4))), dim3(256), 0, s,
@@ -610,7 +575,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       a.weight = p.class_weight;
       Layout Lc = L;                     // the chunk's token tiles only
       Lc.n_tiles = c_tiles;
-      dispatch_fwd<T, false, true>(a, Lc, fkey, s);
+      dispatch_fwd<T>(a, fwd_grid(Lc), fkey, flce::FwdMode::kStore, s);
       // lse, packed lse and row losses of the chunk's rows
       flce::MergeArgs m{};
       m.part_m = reinterpret_cast<float*>(at(ws, L.part_m));
@@ -671,10 +636,10 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
     Lw.ldt = S.ldt;
     Lw.chunk = S.chunk;
     if (p.dw_bf16)
-      launch_dw<T, uint16_t>(xt, gt, p, Lw, 0, p.v, S.vpad, d_tiles, S.v_tiles, c0, ci > 0, ctl,
+      run_dw<T, uint16_t>(xt, gt, p, Lw, 0, p.v, S.vpad, d_tiles, S.v_tiles, c0, ci > 0, ctl,
                              static_cast<uint16_t*>(dw), s);
     else
-      launch_dw<T, float>(xt, gt, p, Lw, 0, p.v, S.vpad, d_tiles, S.v_tiles, c0, ci > 0, ctl,
+      run_dw<T, float>(xt, gt, p, Lw, 0, p.v, S.vpad, d_tiles, S.v_tiles, c0, ci > 0, ctl,
                           static_cast<float*>(dw), s);
     if (p.n > 0) {
       // dX of the chunk in one contraction over the whole vocabulary
@@ -692,8 +657,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       xa.dx = static_cast<T*>(dx);
       xa.first = 1;
       xa.d_tiles = d_tiles;
-      hipLaunchKernelGGL((flce::k_dx<T, true>), dim3(static_cast<unsigned>(grid8(d_tiles * c_tiles))),
-                         dim3(tile::kThreads), 0, s, xa);
+      flce::launch_dx<T>(xa, grid8(d_tiles * c_tiles), true, s);
     }
     if (has_bias)
       hipLaunchKernelGGL((flce::k_db<T>), dim3(static_cast<unsigned>(cdiv(p.v, 4))), dim3(256), 0, s,
@@ -799,21 +763,6 @@ void ce_reduce(const flce_params& p, const CeLayout& L, float* loss, void* ws, h
                      p.reduction == FLCE_REDUCTION_MEAN ? 1 : 0, loss);
 }
 
-template <typename T, bool kSoftcap, bool kSumZ>
-void launch_ce_fwd(const flce::CeArgs<T>& a, hipStream_t s) {
-  if (a.pred)
-    hipLaunchKernelGGL((flce::k_ce_fwd<T, kSoftcap, kSumZ, true>), dim3(static_cast<unsigned>(a.n)),
-                       dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((flce::k_ce_fwd<T, kSoftcap, kSumZ, false>), dim3(static_cast<unsigned>(a.n)),
-                       dim3(256), 0, s, a);
-}
-template <typename T, bool kSoftcap, bool kSumZ>
-void launch_ce_fused(const flce::CeArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((flce::k_ce_fused<T, kSoftcap, kSumZ>), dim3(static_cast<unsigned>(a.n)),
-                     dim3(flce::kCeThreads), 0, s, a);
-}
-
 template <typename T>
 flce_status run_ce(const flce_params& p, const CeLayout& L, const void* logits, const int32_t* targets,
                    float* loss, float* lse, float* row_loss, const float* lse_in,
@@ -833,29 +782,8 @@ flce_status run_ce(const flce_params& p, const CeLayout& L, const void* logits, 
   }
   const bool c = p.softcap > 0.f, z = p.label_smoothing > 0.f;
   if (p.n > 0) {
-    if (mode == 1) {
-      if (c)
-        hipLaunchKernelGGL((flce::k_ce_bwd<T, true>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((flce::k_ce_bwd<T, false>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s, a);
-      return launched();
-    }
-    const int key = (c ? 1 : 0) | (z ? 2 : 0);
-    if (mode == 0) {
-      switch (key) {
-        case 0: launch_ce_fwd<T, false, false>(a, s); break;
-        case 1: launch_ce_fwd<T, true, false>(a, s); break;
-        case 2: launch_ce_fwd<T, false, true>(a, s); break;
-        default: launch_ce_fwd<T, true, true>(a, s); break;
-      }
-    } else {
-      switch (key) {
-        case 0: launch_ce_fused<T, false, false>(a, s); break;
-        case 1: launch_ce_fused<T, true, false>(a, s); break;
-        case 2: launch_ce_fused<T, false, true>(a, s); break;
-        default: launch_ce_fused<T, true, true>(a, s); break;
-      }
-    }
+    flce::launch_ce<T>(a, mode, (c ? 1 : 0) | (z ? 2 : 0), a.pred != nullptr, s);
+    if (mode == 1) return launched();
   } else if (mode == 1) {
     return launched();
   }

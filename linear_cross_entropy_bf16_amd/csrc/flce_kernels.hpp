@@ -83,7 +83,7 @@ __device__ __forceinline__ void lse_merge(float& m, float& d, float m2, float d2
 }
 
 // ------------------------------------------------------------------- prep
-__global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targets, int64_t n,
+static __global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targets, int64_t n,
                                                int64_t v, int32_t ignore_index,
                                                const float* __restrict__ grad_output,
                                                int32_t reduction_mean, Ctl* __restrict__ ctl,
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ x, in
 
 // lse of each valid row in packed-row order, so the backward's per-token loads
 // are independent of the row map.
-__global__ __launch_bounds__(256) void k_pack_lse(const float* __restrict__ lse,
+static __global__ __launch_bounds__(256) void k_pack_lse(const float* __restrict__ lse,
                                                   const int32_t* __restrict__ rows,
                                                   const Ctl* __restrict__ ctl,
                                                   float* __restrict__ lsep) {
@@ -479,7 +479,7 @@ struct MergeArgs {
 
 // lse = (m + log2 d) ln 2; row loss = lse - (1-eps) z_t - (eps/V) sum z + s lse^2
 // on valid rows, 0 elsewhere.
-__global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
+static __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   __shared__ double red[256];
   if (a.row0 + static_cast<int64_t>(blockIdx.x) * 256 >= a.n) return;   // whole block past the batch
   const int64_t j = a.row0 + static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
 }
 
 // block_sums[b] = sum of vals [256 b, 256 b + 256) in double, fixed order.
-__global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ vals, int64_t n,
+static __global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ vals, int64_t n,
                                                     double* __restrict__ block_sums) {
   __shared__ double red[256];
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ va
 }
 
 // Token accuracy: the block sums of the per-row hits over n_valid (0 if none).
-__global__ __launch_bounds__(256) void k_accuracy_final(const double* __restrict__ block_sums,
+static __global__ __launch_bounds__(256) void k_accuracy_final(const double* __restrict__ block_sums,
                                                         int64_t nblocks, const Ctl* __restrict__ ctl,
                                                         float* __restrict__ accuracy) {
   __shared__ double red[256];
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(256) void k_accuracy_final(const double* __restrict
   }
 }
 
-__global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ block_sums,
+static __global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ block_sums,
                                                     int64_t nblocks, const Ctl* __restrict__ ctl,
                                                     int32_t reduction_mean, float* __restrict__ loss) {
   __shared__ double red[256];
@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(256) void k_db(const T* __restrict__ gt, int64_t ld
   if (lane == 0) db[v0 + v] = ctl->scale * s + (accumulate ? db[v0 + v] : 0.f);
 }
 
-__global__ __launch_bounds__(256) void k_fill(float* __restrict__ p, int64_t count, float value) {
+static __global__ __launch_bounds__(256) void k_fill(float* __restrict__ p, int64_t count, float value) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < count) p[i] = value;
 }

@@ -21,8 +21,7 @@ FAKE = 0x7f0000000000
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(LIB_PATH):
-        build()
+    build(force=False)          # rebuild when any source is newer than the library
     return _lib.load()
 
 
