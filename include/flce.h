@@ -40,6 +40,10 @@
  *    D must be a multiple of 8.  N and V are arbitrary (ragged tails are
  *    handled in the kernels).  N <= 2^22, D <= 2^20, V < 2^31, and for the
  *    fused path ceil(N/256) * ceil(V/256) < 2^31 (one forward tile each).
+ *    In bf16 every K-major buffer the backward builds must have a row pitch
+ *    p with 510 p + 112 < 2^31 (the tile engine's 32-bit buffer offsets):
+ *    vocab_slice <= 2^20 and N <= 2^22 always satisfy it; the stored-logits
+ *    schedule, whose G rows span the whole vocabulary, needs V <= 4210432.
  *  - Element type of X, W, bias and dX is params->dtype (bf16 or fp32).
  *    Loss, lse, row_loss, dW and db are always fp32.  Accumulation is fp32.
  *  - Every argument is validated on the host before any HIP call, so invalid
@@ -122,7 +126,14 @@ typedef struct flce_params {
  * constant in the sequence length). */
 size_t flce_workspace_size(const flce_params* params, int with_backward);
 
-/* Forward: loss and per-row LSE.
+/* Forward: loss and per-row LSE.  The cross-entropy of a one-hot target
+ * reduces to the row's log-sum-exp minus its target logit, evaluated with the
+ * running row maximum subtracted (page "Cutting LLM Memory by 84%",
+ * "Definition and Forward Pass"); the logits GEMM keeps only per-row
+ * online-softmax partials and the target logit, never the logits (page
+ * "[CuteDSL] FLCE", Summary: a store-free forward).  The row loss is formed as
+ * (m - z_t) + ln sum_v e^(z_v - m) with m the row maximum, so a confidently
+ * predicted row keeps the accuracy of that sum (a few ulp of 1) whatever |z|.
  *  x        [n, d] dtype          w   [v, d] dtype        bias [v] dtype or NULL
  *  targets  [n] int32
  *  loss     fp32 [1] for MEAN/SUM, fp32 [n] (per-row losses) for NONE
@@ -255,16 +266,23 @@ flce_status flce_fused_fwd_bwd_stored(const flce_params* params, const void* x, 
                                       float* lse, void* dx, void* dw, float* dbias, void* ws,
                                       size_t ws_bytes, void* stream);
 
-/* Synchronises `stream`, then reports the device-side target check of the
- * last call that used this workspace: FLCE_OK or FLCE_ERR_TARGET_OUT_OF_RANGE
+/* The host-side validation contract of the page "[CuteDSL] FLCE",
+ * Correctness, for the one check that needs the targets' values: synchronises
+ * `stream`, then reports the device-side target check of the last call that
+ * used this workspace: FLCE_OK or FLCE_ERR_TARGET_OUT_OF_RANGE
  * (FLCE_ERR_DEVICE if the synchronisation or copy fails).  When it reports an
  * out-of-range target, that call's numeric results are undefined. */
 flce_status flce_check_status(const void* ws, void* stream);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code: the reason a call was
+ * refused (the host-side validation and by-design refusal contracts of the
+ * page "[CuteDSL] FLCE", Correctness, e.g. reduction NONE with a backward). */
 const char* flce_status_string(flce_status status);
 
-/* Library version as major * 10000 + minor * 100 + patch. */
+/* Library version as major * 10000 + minor * 100 + patch.  Not an operation
+ * of the method: it names the build of the option set above (page
+ * "[CuteDSL] FLCE", Summary); 1.1.0 forms the row loss from the row maximum
+ * (see flce_forward). */
 int flce_version(void);
 
 #ifdef __cplusplus

@@ -76,6 +76,20 @@ def _prepare(x, weight, target, bias):
     return x2, w2, t2, b2
 
 
+def _check_buffer(t, name, shape, dtype, device):
+    """A caller-supplied buffer must match what the library will write."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def make_params(n, d, v, dtype, ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0,
                 softcap=0.0, reduction="mean", vocab_slice=0, token_chunk=0,
                 dw_bf16=False, class_weight=None) -> _lib.Params:
@@ -189,22 +203,32 @@ def fused_fwd_bwd(x, weight, target, bias=None, *, ignore_index=-100, label_smoo
                     reduction, vocab_slice, token_chunk, dw_bf16, cw)
     dev = x2.device
     nbytes = _lib.stored_workspace_size(p) if stored_logits else _lib.workspace_size(p, True)
+    if nbytes == 0:
+        raise _lib.FLCEError(_lib.FLCE_ERR_INVALID_ARGUMENT, "workspace size")
     if workspace is None:
-        if nbytes == 0:
-            raise _lib.FLCEError(_lib.FLCE_ERR_INVALID_ARGUMENT, "workspace size")
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    elif workspace.numel() < nbytes:
-        raise _lib.FLCEError(_lib.FLCE_ERR_WORKSPACE_TOO_SMALL, "fused_fwd_bwd")
     else:
+        _check_buffer(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+        if workspace.numel() < nbytes:
+            raise _lib.FLCEError(_lib.FLCE_ERR_WORKSPACE_TOO_SMALL, "fused_fwd_bwd")
         nbytes = workspace.numel()
+    dw_dtype = torch.bfloat16 if dw_bf16 else torch.float32
     if out is None:
         loss = torch.empty(1, dtype=torch.float32, device=dev)
         lse = torch.empty(n, dtype=torch.float32, device=dev)
         dx = torch.empty((n, d), dtype=x2.dtype, device=dev)
-        dw = torch.empty((v, d), dtype=torch.bfloat16 if dw_bf16 else torch.float32, device=dev)
+        dw = torch.empty((v, d), dtype=dw_dtype, device=dev)
         db = torch.empty(v, dtype=torch.float32, device=dev) if b2 is not None else None
     else:
         loss, lse, dx, dw, db = out
+        # the library writes through these pointers with the sizes above: a
+        # short or mistyped buffer would be overrun on the device
+        _check_buffer(loss, "out loss", (1,), torch.float32, dev)
+        _check_buffer(lse, "out lse", (n,), torch.float32, dev)
+        _check_buffer(dx, "out dx", (n, d), x2.dtype, dev)
+        _check_buffer(dw, "out dw", (v, d), dw_dtype, dev)
+        if b2 is not None:
+            _check_buffer(db, "out db", (v,), torch.float32, dev)
     call = _lib.fused_fwd_bwd_stored if stored_logits else _lib.fused_fwd_bwd
     _check(call(p, _ptr(x2), _ptr(w2), _ptr(b2), _ptr(t2), _ptr(loss), _ptr(lse), _ptr(dx), _ptr(dw),
                 _ptr(db), _ptr(workspace), nbytes, _stream(dev)),
@@ -235,7 +259,10 @@ class LinearCrossEntropyFunction(torch.autograd.Function):
         if ctx.opts["reduction"] == "none":
             raise RuntimeError("reduction='none' has no backward in the fused kernel; "
                                "use 'mean' or 'sum'")
-        dx, dw, db = backward(x, weight, target, lse, grad_output=grad_loss, bias=bias, **ctx.opts)
+        # a bf16 weight gets its gradient in bf16 straight from the dW kernel
+        # (one rounding of the fp32 sum, as a cast would do, without the fp32 copy)
+        dx, dw, db = backward(x, weight, target, lse, grad_output=grad_loss, bias=bias,
+                              dw_bf16=weight.dtype == torch.bfloat16, **ctx.opts)
         return (dx.to(x.dtype), dw.to(weight.dtype), None,
                 db.to(bias.dtype) if db is not None else None, None, None, None, None, None, None)
 

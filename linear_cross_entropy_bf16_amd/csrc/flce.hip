@@ -13,6 +13,8 @@
 #include <type_traits>
 
 #include "flce.h"
+// the small kernels of flce_kernels.hpp are compiled in this file only
+#define FLCE_HOST_KERNELS 1
 #include "flce_launch.hpp"
 
 namespace {
@@ -162,6 +164,16 @@ flce_status check_params(const flce_params* p) {
   return FLCE_OK;
 }
 
+// The bf16 tile engine addresses a 256-row slab of a K-major operand with
+// 32-bit buffer offsets: row * pitch * 2 + 112 must stay below 2^31 for every
+// row < 256 (rows past the operand use the out-of-range marker 2^31).  The
+// library's own K-major buffers have pitches slice + 128 (G), N or the token
+// chunk + 128 (X^T, G^T), and V rounded up to 256, + 128 (the stored-logits
+// schedule's G and W^T); X and W have pitch D <= 2^20.
+bool pitch_ok(const flce_params& p, int64_t pitch) {
+  return p.dtype != FLCE_DTYPE_BF16 || 255 * pitch * 2 + 112 < (int64_t{1} << 31);
+}
+
 flce_status check_inputs(const flce_params& p, const void* x, const void* w, const void* bias,
                          const int32_t* targets) {
   if (!w || !aligned(w, 16)) return FLCE_ERR_INVALID_ARGUMENT;
@@ -293,6 +305,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   m.n_chunks = L.n_chunks;
   m.ignore_index = p.ignore_index;
   m.keep_target = 1.0f - p.label_smoothing;
+  m.eps = p.label_smoothing;
   m.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
   m.zloss = p.lse_square_scale;
   m.lse = lse;
@@ -588,6 +601,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       m.n_chunks = L.n_chunks;
       m.ignore_index = p.ignore_index;
       m.keep_target = 1.0f - p.label_smoothing;
+      m.eps = p.label_smoothing;
       m.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
       m.zloss = p.lse_square_scale;
       m.lse = lse;
@@ -736,6 +750,7 @@ flce::CeArgs<T> ce_args(const flce_params& p, const CeLayout& L, const void* log
   a.softcap = p.softcap;
   a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
   a.keep_target = 1.0f - p.label_smoothing;
+  a.eps = p.label_smoothing;
   a.eps_over_v = static_cast<float>(static_cast<double>(p.label_smoothing) / static_cast<double>(p.v));
   a.zloss = p.lse_square_scale;
   a.two_s = 2.0f * p.lse_square_scale;
@@ -807,6 +822,7 @@ extern "C" {
 size_t flce_workspace_size(const flce_params* params, int with_backward) {
   if (check_params(params) != FLCE_OK) return 0;
   const Layout L = make_layout(*params);
+  if (!pitch_ok(*params, L.ldg) || !pitch_ok(*params, L.ldt)) return 0;
   const int64_t need = with_backward ? (L.bwd_end > L.fwd_end ? L.bwd_end : L.fwd_end) : L.fwd_end;
   return static_cast<size_t>(need);
 }
@@ -858,6 +874,7 @@ static flce_status check_backward_args(const flce_params& p, const Layout& L, co
   if (p.n > 0 && (!lse || !aligned(lse, 4) || !dx || !aligned(dx, 16))) return FLCE_ERR_INVALID_ARGUMENT;
   if (!dw || !aligned(dw, 16)) return FLCE_ERR_INVALID_ARGUMENT;
   if (bias && (!dbias || !aligned(dbias, 4))) return FLCE_ERR_INVALID_ARGUMENT;
+  if (!pitch_ok(p, L.ldg) || !pitch_ok(p, L.ldt)) return FLCE_ERR_INVALID_ARGUMENT;
   const int64_t need = L.bwd_end > L.fwd_end ? L.bwd_end : L.fwd_end;
   return check_ws(ws, ws_bytes, need);
 }
@@ -905,7 +922,9 @@ flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const v
 
 size_t flce_stored_workspace_size(const flce_params* params) {
   if (check_params(params) != FLCE_OK) return 0;
-  return static_cast<size_t>(make_stored_layout(*params).end);
+  const StoredLayout S = make_stored_layout(*params);
+  if (!pitch_ok(*params, S.ldg) || !pitch_ok(*params, S.ldt)) return 0;
+  return static_cast<size_t>(S.end);
 }
 
 flce_status flce_fused_fwd_bwd_stored(const flce_params* params, const void* x, const void* w,
@@ -922,6 +941,7 @@ flce_status flce_fused_fwd_bwd_stored(const flce_params* params, const void* x, 
   if (!dw || !aligned(dw, 16)) return FLCE_ERR_INVALID_ARGUMENT;
   if (bias && (!dbias || !aligned(dbias, 4))) return FLCE_ERR_INVALID_ARGUMENT;
   const StoredLayout S = make_stored_layout(p);
+  if (!pitch_ok(p, S.ldg) || !pitch_ok(p, S.ldt)) return FLCE_ERR_INVALID_ARGUMENT;
   if ((st = check_ws(ws, ws_bytes, S.end)) != FLCE_OK) return st;
   if ((st = ready_to_launch()) != FLCE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1039,6 +1059,6 @@ const char* flce_status_string(flce_status status) {
   return "unknown status";
 }
 
-int flce_version(void) { return 100; }
+int flce_version(void) { return 10100; }
 
 }  // extern "C"

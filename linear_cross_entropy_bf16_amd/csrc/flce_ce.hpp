@@ -33,6 +33,7 @@ struct CeArgs {
   int32_t ignore_index;
   float softcap, inv_softcap;
   float keep_target;        // 1 - eps
+  float eps;                // eps
   float eps_over_v;         // eps / V
   float zloss;              // s
   float two_s;              // 2 s
@@ -107,9 +108,9 @@ __device__ __forceinline__ float softcapped(float r, float c, float inv_c, bool 
   return on ? c * fast_tanh(r * inv_c) : r;
 }
 
-// Running row statistics of one thread: m = max z in log2 units, d = sum of
-// 2^(z log2e - m), s = sum z (online-softmax recurrence, page "Cutting LLM
-// Memory by 84%", "Definition and Forward Pass").
+// Running row statistics of one thread: m = max z, d = sum of
+// 2^(z log2e - h(m)) (see lse_merge), s = sum z (online-softmax recurrence,
+// page "Cutting LLM Memory by 84%", "Definition and Forward Pass").
 struct RowStats {
   float m, d, s;
 };
@@ -135,11 +136,12 @@ __device__ __forceinline__ void stats_add(RowStats& st, const float (&z)[N]) {
     for (int i = 0; i < N; ++i) st.s += z[i];
   }
   if (mx == -INFINITY) return;          // only masked (-inf) logits here
-  const float m_new = fmax_fast(st.m, mx * kLog2e);
+  const float m_new = fmax_fast(st.m, mx);
+  const float h_new = log2_units(m_new);
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) sum += fast_exp2(__builtin_fmaf(z[i], kLog2e, -m_new));
-  st.d = st.d * fast_exp2(st.m - m_new) + sum;   // st.m = -inf: the old sum is 0
+  for (int i = 0; i < N; ++i) sum += fast_exp2(__builtin_fmaf(z[i], kLog2e, -h_new));
+  st.d = st.d * fast_exp2(log2_units(st.m) - h_new) + sum;   // st.m = -inf: the old sum is 0
   st.m = m_new;
 }
 
@@ -251,9 +253,10 @@ __device__ __forceinline__ float ce_grad(float r, bool is_t, float lse2, float z
                                          float keep, float eps_v, float c, float inv_c) {
   float z = r, dz = 1.f;
   if (kSoftcap) {
-    const float th = fast_tanh(r * inv_c);
-    z = c * th;
-    dz = 1.f - th * th;
+    const float x = r * inv_c;
+    const float q = tanh_q(x);
+    z = c * tanh_from_q(x, q);
+    dz = q * (2.0f - q);          // 1 - tanh^2, accurate where tanh saturates
   }
   const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2));
   float g = __builtin_fmaf(p, zfac, -(is_t ? keep + eps_v : eps_v));
@@ -317,11 +320,15 @@ __device__ __forceinline__ void row_grad(const CeArgs<T>& a, const T* row, T* gr
 template <typename T, bool kSoftcap>
 __device__ __forceinline__ float row_finish(const CeArgs<T>& a, const T* row, int64_t r, int64_t t,
                                             const RowStats& st) {
-  const float lse = (st.m + log2f(st.d)) * kLn2;
+  // lse = m + lam; the row loss from m - z_t, exact where the target holds the
+  // row's maximum (see k_merge)
+  const float lam = log_rel_sum(st.m, st.d);
+  const float lse = st.m + lam;
   // a target outside [0, V) is reported by the status word; never read past the row
   const float zt = (t >= 0 && t < a.v) ? softcapped(ld_elem(row, t), a.softcap, a.inv_softcap, kSoftcap)
                                        : 0.f;
-  const float rl = lse - a.keep_target * zt - a.eps_over_v * st.s + a.zloss * lse * lse;
+  const float rl = a.keep_target * (st.m - zt) + lam + (a.eps * st.m - a.eps_over_v * st.s) +
+                   a.zloss * lse * lse;
   a.lse[r] = lse;
   a.row_loss_ws[r] = rl;
   if (a.row_loss) a.row_loss[r] = rl;

@@ -65,23 +65,48 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// tanh(x) = 1 - 2 / (exp(2x) + 1); absolute error a few ulp of 1, which the
-// softcap scales by c.  Saturates correctly: exp2 -> inf gives 1, -> 0 gives -1.
-__device__ __forceinline__ float fast_tanh(float x) {
-  const float e = fast_exp2(x * (2.0f * kLog2e));
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+// tanh(x) and its derivative 1 - tanh(x)^2 from q = 2 / (e^(2|x|) + 1), which
+// lies in (0, 1]: tanh = sign(x) (1 - q) and 1 - tanh^2 = q (2 - q).  Both keep
+// their relative accuracy where tanh saturates (1 - tanh^2 formed from tanh
+// would cancel to 0 there); exp2 -> inf gives q = 0, tanh = +-1, derivative 0.
+__device__ __forceinline__ float tanh_q(float x) {
+  const float e = fast_exp2(__builtin_fabsf(x) * (2.0f * kLog2e));
+  return __builtin_amdgcn_rcpf(__builtin_fmaf(e, 0.5f, 0.5f));
+}
+__device__ __forceinline__ float tanh_from_q(float x, float q) { return __builtin_copysignf(1.0f - q, x); }
+__device__ __forceinline__ float fast_tanh(float x) { return tanh_from_q(x, tanh_q(x)); }
+
+// m log2e rounded to fp32 on its own, never fused with a neighbouring add or
+// subtract (the compiler contracts a*b - c into an fma by default): the
+// reference point h(m) of the running sums below.
+__device__ __forceinline__ float log2_units(float m) {
+#pragma clang fp contract(off)
+  return m * kLog2e;
 }
 
-// (m, d) <- (m, d) merged with (m2, d2), both in log2 units: running maximum
-// and sum of 2^(z - m) (page "Cutting LLM Memory by 84%", "Definition and
-// Forward Pass": the online-softmax update).
+// Online softmax state of a set of logits (page "Cutting LLM Memory by 84%",
+// "Definition and Forward Pass": a running maximum and a running sum of
+// exponentials rescaled whenever the maximum grows): m = max z in natural
+// units and d = sum of 2^(z log2e - h(m)).  (m, d) <- merged with (m2, d2).
 __device__ __forceinline__ void lse_merge(float& m, float& d, float m2, float d2) {
   const float mx = fmaxf(m, m2);
   if (mx == -INFINITY) return;
-  d = d * fast_exp2(m - mx) + d2 * fast_exp2(m2 - mx);
+  const float h = log2_units(mx);
+  d = d * fast_exp2(log2_units(m) - h) + d2 * fast_exp2(log2_units(m2) - h);
   m = mx;
 }
 
+// ln sum_v e^(z_v - m) of a state (m, d).  h(m) = m log2e - lo, where lo (the
+// rounding error of that product, exact by the fma) corrects the reference
+// point.  lse = m + this; the row loss is formed as (m - z_t) + this, which
+// stays exact where the target is the row's maximum.
+__device__ __forceinline__ float log_rel_sum(float m, float d) {
+  const float h = log2_units(m);
+  const float lo = __builtin_fmaf(m, kLog2e, -h);
+  return (log2f(d) - lo) * kLn2;
+}
+
+#ifdef FLCE_HOST_KERNELS
 // ------------------------------------------------------------------- prep
 static __global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targets, int64_t n,
                                                int64_t v, int32_t ignore_index,
@@ -154,6 +179,7 @@ static __global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict_
     ctl->scale = reduction_mean ? (den > 0.f ? g / den : 0.0f) : g;
   }
 }
+#endif  // FLCE_HOST_KERNELS
 
 // Valid rows of X (and their targets) packed to the front, in row order: every
 // GEMM below runs on n_valid rows only (ignored rows have zero loss and zero
@@ -174,6 +200,7 @@ __global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ x, in
   if (threadIdx.x == 0) tc[j] = targets[r];
 }
 
+#ifdef FLCE_HOST_KERNELS
 // lse of each valid row in packed-row order, so the backward's per-token loads
 // are independent of the row map.
 static __global__ __launch_bounds__(256) void k_pack_lse(const float* __restrict__ lse,
@@ -183,6 +210,7 @@ static __global__ __launch_bounds__(256) void k_pack_lse(const float* __restrict
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (j < ctl->n_valid) lsep[j] = lse[rows[j]];
 }
+#endif  // FLCE_HOST_KERNELS
 
 // Rows of dX whose target is ignore_index are zero.
 template <typename T>
@@ -208,8 +236,8 @@ struct FwdArgs {
   int64_t n_chunks, tiles_per_chunk, group;   // chunks of this launch; tiles per chunk
   int64_t vt_base, vt_end;   // vocabulary tiles [vt_base, vt_end) of this launch
   int64_t chunk_base;        // partials row of this launch's first chunk
-  float* part_m;          // [n_chunks, n] running max, log2 units
-  float* part_d;          // [n_chunks, n] sum of 2^(z log2e - m)
+  float* part_m;          // [n_chunks, n] running max of z
+  float* part_d;          // [n_chunks, n] sum of 2^(z log2e - h(max)), see lse_merge
   float* part_s;          // [n_chunks, n] sum of z
   float* part_b;          // [n_chunks, n] largest z (predicted tokens only)
   int32_t* part_i;        // [n_chunks, n] its lowest vocabulary index
@@ -314,11 +342,13 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
         s_run[nb] += sz;
       }
       if (kMasked && mt == -INFINITY) continue;
-      const float m_new = fmax_fast(m_run[nb], mt * kLog2e);
+      // running maximum in natural units, sums relative to h(max) (see lse_merge)
+      const float m_new = fmax_fast(m_run[nb], mt);
+      const float h_new = log2_units(m_new);
       float sum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(z[r], kLog2e, -m_new));
-      d_run[nb] = d_run[nb] * fast_exp2(m_run[nb] - m_new) + sum;
+      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(z[r], kLog2e, -h_new));
+      d_run[nb] = d_run[nb] * fast_exp2(log2_units(m_run[nb]) - h_new) + sum;
       m_run[nb] = m_new;
     }
   }
@@ -475,10 +505,16 @@ struct MergeArgs {
   int64_t row0;         // this launch covers rows [row0, row0 + 256 gridDim.x)
   float* lsep;          // null, or [n] lse by packed row
   const float* weight;  // [v] class weights or null
+  float eps;            // eps itself (keep_target = 1 - eps)
 };
 
-// lse = (m + log2 d) ln 2; row loss = lse - (1-eps) z_t - (eps/V) sum z + s lse^2
-// on valid rows, 0 elsewhere.
+#ifdef FLCE_HOST_KERNELS
+// lse = m + lam with lam = ln sum_v e^(z_v - m); row loss on valid rows
+//   lse - (1-eps) z_t - (eps/V) sum z + s lse^2
+//     = (1-eps)(m - z_t) + lam + eps m - (eps/V) sum z + s lse^2,
+// 0 elsewhere.  Formed from m - z_t (exact where the target holds the row's
+// maximum) rather than lse - z_t, so a confidently predicted row keeps the
+// accuracy of lam (a few ulp of 1) instead of the ulp of lse.
 static __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   __shared__ double red[256];
   if (a.row0 + static_cast<int64_t>(blockIdx.x) * 256 >= a.n) return;   // whole block past the batch
@@ -491,16 +527,17 @@ static __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
       lse_merge(m, d, a.part_m[c * a.n + j], a.part_d[c * a.n + j]);
       s += a.part_s[c * a.n + j];
     }
-    const float lse = (m + log2f(d)) * kLn2;
+    const float lam = log_rel_sum(m, d);
+    const float lse = m + lam;
+    const float gap = (m - a.zt[j]) + lam;   // lse - z_t
     const int64_t r = a.rows[j];
     float rl;
     if (a.weight) {   // (1-eps) w_t (lse - z_t) + (eps/V)(sum_v w_v lse - sum_v w_v z_v) + s w_t lse^2
       const int32_t t = a.targets[r];
       const float wt = (t >= 0 && t < a.v) ? a.weight[t] : 0.f;
-      rl = a.keep_target * wt * (lse - a.zt[j]) + a.eps_over_v * (a.ctl->wall * lse - s) +
-           a.zloss * wt * lse * lse;
+      rl = a.keep_target * wt * gap + a.eps_over_v * (a.ctl->wall * lse - s) + a.zloss * wt * lse * lse;
     } else {
-      rl = lse - a.keep_target * a.zt[j] - a.eps_over_v * s + a.zloss * lse * lse;
+      rl = a.keep_target * (m - a.zt[j]) + lam + (a.eps * m - a.eps_over_v * s) + a.zloss * lse * lse;
     }
     a.lse[r] = lse;
     if (a.lsep) a.lsep[j] = lse;
@@ -540,7 +577,9 @@ static __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   }
   if (threadIdx.x == 0) a.block_sums[a.row0 / 256 + blockIdx.x] = red[0];
 }
+#endif  // FLCE_HOST_KERNELS
 
+#ifdef FLCE_HOST_KERNELS
 // block_sums[b] = sum of vals [256 b, 256 b + 256) in double, fixed order.
 static __global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ vals, int64_t n,
                                                     double* __restrict__ block_sums) {
@@ -554,7 +593,9 @@ static __global__ __launch_bounds__(256) void k_block_sums(const float* __restri
   }
   if (threadIdx.x == 0) block_sums[blockIdx.x] = red[0];
 }
+#endif  // FLCE_HOST_KERNELS
 
+#ifdef FLCE_HOST_KERNELS
 // Token accuracy: the block sums of the per-row hits over n_valid (0 if none).
 static __global__ __launch_bounds__(256) void k_accuracy_final(const double* __restrict__ block_sums,
                                                         int64_t nblocks, const Ctl* __restrict__ ctl,
@@ -573,7 +614,9 @@ static __global__ __launch_bounds__(256) void k_accuracy_final(const double* __r
     accuracy[0] = nv > 0 ? static_cast<float>(red[0] / nv) : 0.f;
   }
 }
+#endif  // FLCE_HOST_KERNELS
 
+#ifdef FLCE_HOST_KERNELS
 static __global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ block_sums,
                                                     int64_t nblocks, const Ctl* __restrict__ ctl,
                                                     int32_t reduction_mean, float* __restrict__ loss) {
@@ -591,6 +634,7 @@ static __global__ __launch_bounds__(256) void k_loss_final(const double* __restr
     loss[0] = static_cast<float>(reduction_mean ? (den > 0.0 ? red[0] / den : 0.0) : red[0]);
   }
 }
+#endif  // FLCE_HOST_KERNELS
 
 // ------------------------------------------------------------------- backward
 // Every backward contraction reads both operands K-major (K contiguous), the
@@ -748,9 +792,10 @@ __device__ __forceinline__ float g_elem(const GArgs<T>& a, float z, float bv, fl
   if (kBias) z += bv;
   float dz = 1.0f;
   if (kSoftcap) {
-    const float th = fast_tanh(z * a.inv_softcap);
-    z = a.softcap * th;
-    dz = 1.0f - th * th;
+    const float x = z * a.inv_softcap;
+    const float q = tanh_q(x);
+    z = a.softcap * tanh_from_q(x, q);
+    dz = q * (2.0f - q);          // 1 - tanh^2, accurate where tanh saturates
   }
   const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lse2));
   const float sub = is_t ? epsw + keep_t : epsw;
@@ -1128,9 +1173,11 @@ __global__ __launch_bounds__(256) void k_db(const T* __restrict__ gt, int64_t ld
   if (lane == 0) db[v0 + v] = ctl->scale * s + (accumulate ? db[v0 + v] : 0.f);
 }
 
+#ifdef FLCE_HOST_KERNELS
 static __global__ __launch_bounds__(256) void k_fill(float* __restrict__ p, int64_t count, float value) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < count) p[i] = value;
 }
+#endif  // FLCE_HOST_KERNELS
 
 }  // namespace flce

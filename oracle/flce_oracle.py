@@ -210,6 +210,40 @@ def grad_logits(z: np.ndarray, lse: np.ndarray, targets: np.ndarray,
     return g
 
 
+def grad_logits_columns(z_cols: np.ndarray, cols: np.ndarray, v: int, lse: np.ndarray,
+                        targets: np.ndarray, opts: LossOptions) -> np.ndarray:
+    """Columns ``cols`` of ``grad_logits`` when only those columns of the
+    rows' final logits are held: ``z_cols = z[:, cols]``, ``lse`` the rows'
+    full LSE and ``v`` the vocabulary size.  The same formula column by
+    column: p_c = exp(z_c - lse) times (1 + 2 s lse), less (1 - eps) where
+    c is the target, less eps / V, times 1 - (z_c / c)^2 under the softcap;
+    with class weights the weighted form of ``grad_logits``.  Lets a test
+    check a few rows of dW = G^T X over a whole batch without the [N, V]
+    logits.  Pinned: equals the columns of ``grad_logits`` and of torch's
+    autograd gradient."""
+    cols = np.asarray(cols)
+    n = z_cols.shape[0]
+    valid = valid_rows(targets, opts)
+    t = np.where(valid, targets, -1)
+    hit = t[:, None] == cols[None, :]
+    p = np.exp(z_cols - lse[:, None])
+    s = opts.lse_square_scale
+    eps = opts.label_smoothing
+    if opts.class_weight is not None:
+        w = np.asarray(opts.class_weight, dtype=np.float64)
+        wt = w[np.where(valid, targets, 0)]
+        fac = (1.0 - eps) * wt + (eps / v) * w.sum() + 2.0 * s * wt * lse
+        g = p * fac[:, None] - np.where(hit, ((1.0 - eps) * wt)[:, None], 0.0)
+        g = g - (eps / v) * w[cols][None, :]
+    else:
+        g = p * (1.0 + 2.0 * s * lse)[:, None] - np.where(hit, 1.0 - eps, 0.0) - eps / v
+    if opts.softcap > 0.0:
+        g = g * (1.0 - (z_cols / opts.softcap) ** 2)
+    g[~valid] = 0.0
+    assert g.shape == (n, len(cols))
+    return g
+
+
 def grad_scale(opts: LossOptions, n_valid: int, grad_output: float) -> float:
     """Scale from the unscaled per-row gradient to d(loss): g / n_valid for
     mean (0 when no row is valid), g for sum.  reduction 'none' has no

@@ -581,6 +581,35 @@ def pin_class_weight_unit_and_fd(O, directions=8, seed=29):
             assert abs(fd - an) <= 1e-7 * gn + 1e-12, (feats, k, fd, an)
 
 
+def pin_gradient_columns(O):
+    """Columns of G from only those columns of the logits equal the columns
+    of the full G (every feature set, class weights, unsorted and repeated
+    target columns) and torch's autograd gradient of its cross-entropy."""
+    import torch
+    import torch.nn.functional as F
+
+    x, w, b, t = _problem(n=30, d=12, v=37, seed=17, bias=True)
+    v = w.shape[0]
+    cols = np.array([0, 5, int(t[t >= 0][0]), 36, 11, int(t[t >= 0][1])])
+    cw = np.random.default_rng(4).uniform(0.2, 2.0, v)
+    for feats in FEATURE_SETS + [dict(class_weight=cw), dict(class_weight=cw, label_smoothing=0.1,
+                                                             lse_square_scale=1e-2, softcap=2.0)]:
+        o = _opts(O, **{k: val for k, val in feats.items() if k != "reduction"})
+        z = O.logits(x, w, b, o.softcap)
+        lse = O.log_sum_exp(z)
+        full = O.grad_logits(z, lse, t, o)
+        part = O.grad_logits_columns(z[:, cols], cols, v, lse, t, o)
+        assert np.allclose(part, full[:, cols], rtol=1e-13, atol=1e-15), feats
+    for eps in (0.0, 0.15):
+        o = _opts(O, label_smoothing=eps)
+        z = O.logits(x, w, b, 0.0)
+        zt = torch.tensor(z, requires_grad=True)
+        tt = torch.tensor(t, dtype=torch.long)
+        F.cross_entropy(zt, tt, ignore_index=IGN, label_smoothing=eps, reduction="sum").backward()
+        part = O.grad_logits_columns(z[:, cols], cols, v, O.log_sum_exp(z), t, o)
+        assert np.allclose(part, zt.grad.numpy()[:, cols], rtol=1e-12, atol=1e-14), eps
+
+
 def pin_target_validation(O):
     """Targets outside [0, V) that are not ignore_index are refused; the
     ignore index itself is accepted even when it lies inside [0, V), and then
@@ -632,5 +661,5 @@ ALL_PINS = [
     pin_gaussian_lse_level, pin_logits_identity_linear, pin_logits_torch,
     pin_logits_finite_differences, pin_megatron_smoothing, pin_predicted_tokens,
     pin_class_weight_torch, pin_class_weight_unit_and_fd, pin_bf16_widening,
-    pin_target_validation,
+    pin_target_validation, pin_gradient_columns,
 ]

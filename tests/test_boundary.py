@@ -260,6 +260,17 @@ def test_size_limits(lib):
     assert _lib.stored_workspace_size(P(n=(1 << 22) + 1)) == 0
     assert _lib.ce_workspace_size(P(n=1 << 22, v=(1 << 31) - 1)) > 0
     assert _lib.ce_workspace_size(P(n=(1 << 22) + 1)) == 0
+    # bf16 K-major pitches: the stored schedule's G rows span V (rounded up to
+    # 256, + 128): 510 * pitch + 112 < 2^31 holds up to V = 4210432
+    bf = _lib.DTYPE_BF16
+    assert _lib.stored_workspace_size(P(dtype=bf, v=4210432)) > 0
+    assert _lib.stored_workspace_size(P(dtype=bf, v=4210433)) == 0
+    assert _lib.stored_workspace_size(P(v=4210561)) > 0            # fp32: 64-bit addressing
+    assert ws(dtype=bf, n=1 << 22) > 0 and ws(dtype=bf, vocab_slice=1 << 20, v=1 << 21) > 0
+    # the entry point refuses it on the host too, before any HIP call
+    st = lib.flce_fused_fwd_bwd_stored(ctypes.byref(P(dtype=bf, v=4210433)), FAKE, FAKE, None, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert st == _lib.FLCE_ERR_INVALID_ARGUMENT
 
 
 def test_loss_module_options():
@@ -288,3 +299,22 @@ def test_binding_refuses_host_tensors():
                  lambda: api.cross_entropy_fused_fwd_bwd(torch.zeros(4, 16), t)):
         with pytest.raises(ValueError):
             call()
+
+
+def test_binding_checks_caller_buffers():
+    """Caller-supplied output buffers and workspace must match what the
+    library writes (shape, dtype, device, contiguity): a short or mistyped
+    buffer is refused on the host instead of being overrun on the device."""
+    import torch
+    from linear_cross_entropy_bf16_amd import api
+    cpu = torch.device("cpu")
+    api._check_buffer(torch.zeros(4, 8), "dx", (4, 8), torch.float32, cpu)
+    bad = [(torch.zeros(3, 8), (4, 8), torch.float32),               # short
+           (torch.zeros(4, 8), (4, 8), torch.bfloat16),              # mistyped (bf16 dW requested)
+           (torch.zeros(8, 4).t(), (4, 8), torch.float32),           # not contiguous
+           (torch.zeros(32), (4, 8), torch.float32)]                 # flat
+    for t, shape, dtype in bad:
+        with pytest.raises(ValueError):
+            api._check_buffer(t, "dx", shape, dtype, cpu)
+    with pytest.raises(ValueError):
+        api._check_buffer(torch.zeros(4, 8), "dx", (4, 8), torch.float32, torch.device("cuda", 0))

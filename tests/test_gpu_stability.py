@@ -1,0 +1,235 @@
+"""The numerically stable softmax on the GPU (needs an MI355X).
+
+The log-sum-exp of page "Cutting LLM Memory by 84%", "Definition and Forward
+Pass" subtracts the running maximum before exponentiating.  These cases drive
+the logits far past the point where an unshifted fp32 exp overflows
+(e^88.7 is fp32's largest value): W scaled so the logits spread over
++-500 .. +-2000, a bias of +-500 on a few classes, and a softcap of 30 under
+raw logits of several hundred (every logit saturated or nearly so).  Every
+path is covered: the fused call, the separate forward and backward calls,
+the stored-logits schedule and the cross-entropy on given logits, in bf16 and
+fp32, each compared element by element with the fp64 oracle at the
+acceptance bars.
+
+Confidently predicted rows (target = the row's largest logit) are where the
+row loss lse - z_t cancels: a row loss of 1e-2 next to an lse of 1000.  The
+kernels form it as (m - z_t) + ln sum_v e^(z_v - m) with m the row maximum,
+which is exact where the target holds the maximum; the per-row bound asserted
+below (|error| <= 2e-4 |row loss| + 1e-6, independent of |z|) fails with the
+lse - z_t form, whose error is an ulp of the lse (3e-5 at |z| = 1000).
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_cross_entropy_bf16_amd import api, workloads as W
+from oracle import flce_oracle as O
+from tests import gpu_utils as U
+
+pytestmark = pytest.mark.gpu
+
+IGN = -100
+EXP_OVERFLOW = 88.73   # ln of fp32's largest finite value
+
+
+def banner(msg):
+    print(f"\n[gpu-stable] {msg}", flush=True)
+
+
+def scaled_problem(n, d, v, dtype, sigma_z, seed, spikes=0.0, offset=0.0, ignore_frac=0.1,
+                   confident=False):
+    """X ~ N(0, 1), W ~ N(0, sigma_z^2 / d) so the logits have standard
+    deviation ~sigma_z; bias N(0, 0.3^2) plus +-`spikes` on 7 classes and a
+    common `offset` on every class; targets uniform, or the fp64 argmax of
+    each row (`confident`); `ignore_frac` of the rows ignored."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, d), dtype=np.float32)
+    w = rng.standard_normal((v, d), dtype=np.float32) * np.float32(sigma_z / np.sqrt(d))
+    b = rng.standard_normal(v, dtype=np.float32) * np.float32(0.3)
+    if spikes:
+        cls = rng.choice(v, 7, replace=False)
+        b[cls] = np.where(np.arange(7) % 2 == 0, spikes, -spikes)
+    b = b + np.float32(offset)
+    if dtype == "bf16":
+        x, w, b = W.f32_to_bf16_bits(x), W.f32_to_bf16_bits(w), W.f32_to_bf16_bits(b)
+    z = O.logits(O.to_f64(x), O.to_f64(w), O.to_f64(b), 0.0)
+    t = np.argmax(z, axis=1).astype(np.int32) if confident else rng.integers(0, v, n).astype(np.int32)
+    k = int(round(ignore_frac * n))
+    if k:
+        t[rng.choice(n, k, replace=False)] = IGN
+    return dict(x=x, w=w, bias=b, targets=t), z
+
+
+def run_path(inp, dtype, o, path):
+    """(loss, lse, dx, dw, db, row_loss or None) from one path of the library."""
+    x = U.dev_tensor(inp["x"], dtype)
+    w = U.dev_tensor(inp["w"], dtype)
+    b = U.dev_tensor(inp["bias"], dtype)
+    t = torch.from_numpy(inp["targets"]).to("cuda")
+    kw = U.lib_opts(o)
+    rl = None
+    if path == "fused":
+        loss, lse, dx, dw, db = api.fused_fwd_bwd(x, w, t, b, vocab_slice=256, **kw)
+    elif path == "stored":
+        loss, lse, dx, dw, db = api.fused_fwd_bwd(x, w, t, b, stored_logits=True, token_chunk=256, **kw)
+    else:
+        loss, lse, rl = api.forward(x, w, t, b, check_targets=True, **kw)
+        dx, dw, db = api.backward(x, w, t, lse, None, b, vocab_slice=256, **kw)
+    torch.cuda.synchronize()
+    return dict(loss=float(loss.item()), lse=U.host(lse), dx=U.host(dx), dw=U.host(dw), db=U.host(db),
+                row_loss=None if rl is None else U.host(rl))
+
+
+def logits_inputs(z, dtype):
+    """The fp64 logits rounded to the logits path's dtype (bf16 bits or fp32)."""
+    z32 = z.astype(np.float32)
+    return W.f32_to_bf16_bits(z32) if dtype == "bf16" else z32
+
+
+def run_logits(r, targets, dtype, o, fused):
+    rt = U.dev_tensor(r, dtype)
+    t = torch.from_numpy(targets).to("cuda")
+    kw = U.lib_opts(o)
+    if fused:
+        loss, lse, g = api.cross_entropy_fused_fwd_bwd(rt, t, **kw)
+        rl = None
+    else:
+        loss, lse, rl = api.cross_entropy_forward(rt, t, check_targets=True, **kw)
+        g = api.cross_entropy_backward(rt, t, lse, None, **kw)
+    torch.cuda.synchronize()
+    return dict(loss=float(loss.item()), lse=U.host(lse), grad=U.host(g),
+                row_loss=None if rl is None else U.host(rl))
+
+
+CASES = {
+    # name: (sigma_z, bias spikes, softcap)
+    "spread150": (150.0, 0.0, 0.0),
+    "spread600": (600.0, 0.0, 0.0),
+    "bias500": (20.0, 500.0, 0.0),
+    "softcap30": (300.0, 0.0, 30.0),
+}
+
+
+@pytest.mark.parametrize("path", ["fused", "separate", "stored", "logits"])
+@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_logits(dtype, case, path):
+    """Loss, LSE and every gradient against the fp64 oracle with logits far
+    beyond exp's fp32 range (random targets, 10% ignored rows, 4 vocabulary
+    slices or 3 token chunks, a ragged last vocabulary tile)."""
+    sigma, spikes, cap = CASES[case]
+    n, d, v = 600, 136, 1000
+    seed = 10 * list(CASES).index(case) + (dtype == "f32")
+    inp, z = scaled_problem(n, d, v, dtype, sigma, seed=seed, spikes=spikes)
+    assert np.abs(z).max() > 4 * EXP_OVERFLOW          # the regime this test is about
+    o = O.LossOptions(softcap=cap, label_smoothing=0.05 if case == "spread150" else 0.0)
+    banner(f"large logits {dtype} {case} {path}: max|z| {np.abs(z).max():.0f}")
+    if path == "logits":
+        r = logits_inputs(z, dtype)      # raw logits: the logits path applies the softcap itself
+        ref = O.cross_entropy_on_logits(r, inp["targets"], o)
+        for fused in (True, False):
+            got = run_logits(r, inp["targets"], dtype, o, fused)
+            U.assert_loss(got["loss"], ref.loss)
+            U.assert_lse(got["lse"], ref.lse)
+            U.assert_close(got["grad"], ref.dx, "dlogits")
+        return
+    got = run_path(inp, dtype, o, path)
+    ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+    U.assert_loss(got["loss"], ref.loss)
+    U.assert_lse(got["lse"], ref.lse)
+    U.assert_close(got["dx"], ref.dx, "dX")
+    U.assert_close(got["dw"], ref.dw, "dW")
+    U.assert_close(got["db"], ref.db, "db")
+    assert np.isfinite(got["lse"]).all() and np.isfinite(got["dx"]).all()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_logits_long_contraction(dtype):
+    """The same regime with a 2048-long contraction per logit (fp32
+    accumulation error grows with |z| and with D) and 16 vocabulary slices."""
+    n, d, v = 512, 2048, 4097
+    inp, z = scaled_problem(n, d, v, dtype, 300.0, seed=77, spikes=500.0)
+    assert np.abs(z).max() > 4 * EXP_OVERFLOW
+    banner(f"large logits, D = {d} {dtype}: max|z| {np.abs(z).max():.0f}")
+    o = O.LossOptions(label_smoothing=0.1, lse_square_scale=1e-4)
+    got = run_path(inp, dtype, o, "fused")
+    ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+    U.assert_loss(got["loss"], ref.loss)
+    U.assert_lse(got["lse"], ref.lse)
+    for k in ("dx", "dw", "db"):
+        U.assert_close(got[k], getattr(ref, k), k)
+
+
+def assert_row_losses(got, ref, what):
+    """Per-row bound of the confident regime: |error| <= 2e-4 |row| + 1e-6."""
+    err = np.abs(got - ref)
+    bound = 2e-4 * np.abs(ref) + 1e-6
+    worst = int(np.argmax(err - bound))
+    assert np.all(err <= bound), (f"{what}: row {worst} loss {got[worst]!r} vs oracle {ref[worst]!r} "
+                                  f"(error {err[worst]:.3e}, bound {bound[worst]:.3e})")
+
+
+@pytest.mark.parametrize("path", ["fused", "separate", "stored"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_confident_targets_at_large_logits(dtype, path):
+    """Target = the row's largest logit, logits shifted by +1000 on every
+    class (a per-row constant, which leaves loss and gradients unchanged),
+    spread 12: row losses of 1e-4 .. 1 next to an LSE of ~1030.  Loss at the
+    1e-4 bar, every row loss within 2e-4 of itself + 1e-6, gradients at the
+    acceptance bars."""
+    n, d, v = 600, 136, 1000
+    inp, z = scaled_problem(n, d, v, dtype, 12.0, seed=5, offset=1000.0, confident=True)
+    o = O.LossOptions()
+    ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+    assert 1e-3 < ref.loss < 1.0 and z.max() > 1000       # confident rows, large logits
+    banner(f"confident targets {dtype} {path}: oracle loss {ref.loss:.4e}, lse ~{ref.lse.max():.0f}")
+    got = run_path(inp, dtype, o, path)
+    U.assert_loss(got["loss"], ref.loss)
+    U.assert_lse(got["lse"], ref.lse)
+    if got["row_loss"] is not None:
+        assert_row_losses(got["row_loss"], ref.row_loss, "row losses")
+    for k in ("dx", "dw", "db"):
+        U.assert_close(got[k], getattr(ref, k), k)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("offset", [0.0, 1000.0, -1500.0])
+def test_confident_targets_on_logits(offset, fused):
+    """Cross-entropy on given fp32 logits (exact inputs, so the only error is
+    the kernel's own): target = argmax, spread 12, shifted by `offset`.  The
+    loss meets the 1e-4 bar and every row loss the per-row bound at any
+    shift."""
+    n, v = 512, 4099
+    rng = np.random.default_rng(41)
+    r = (rng.standard_normal((n, v)) * 12.0 + offset).astype(np.float32)
+    t = np.argmax(r, axis=1).astype(np.int32)
+    t[rng.choice(n, 40, replace=False)] = IGN
+    o = O.LossOptions()
+    ref = O.cross_entropy_on_logits(r, t, o)
+    assert 1e-3 < ref.loss < 1.0
+    banner(f"confident targets on logits, offset {offset}, fused={fused}: oracle loss {ref.loss:.4e}")
+    got = run_logits(r, t, "f32", o, fused)
+    U.assert_loss(got["loss"], ref.loss)
+    U.assert_lse(got["lse"], ref.lse)
+    U.assert_close(got["grad"], ref.dx, "dlogits")
+    if got["row_loss"] is not None:
+        assert_row_losses(got["row_loss"], ref.row_loss, "row losses")
+
+
+def test_softcap_saturated_rows():
+    """Softcap 30 under raw logits of +-3000: every logit saturated, the
+    softcap derivative 1 - tanh^2 down to ~1e-80 (formed without cancellation
+    on the GPU); the loss and LSE against the oracle, gradients finite and at
+    the bars where the oracle's are not negligible."""
+    n, d, v = 300, 136, 1000
+    inp, z = scaled_problem(n, d, v, "f32", 1000.0, seed=9)
+    o = O.LossOptions(softcap=30.0)
+    ref = O.forward_backward(inp["x"], inp["w"], inp["bias"], inp["targets"], o)
+    banner(f"saturated softcap: max|r| {np.abs(z).max():.0f}")
+    got = run_path(inp, "f32", o, "fused")
+    U.assert_loss(got["loss"], ref.loss)
+    U.assert_lse(got["lse"], ref.lse)
+    for k in ("dx", "dw", "db"):
+        assert np.isfinite(got[k]).all(), k
+        U.assert_close(got[k], getattr(ref, k), k)

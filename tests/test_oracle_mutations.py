@@ -204,12 +204,29 @@ def mut_bf16_as_fp16(m):
     m.to_f64 = to_f64
 
 
+def mut_columns_smoothing_over_held(m):
+    orig = m.grad_logits_columns
+
+    def grad_logits_columns(z_cols, cols, v, lse, targets, opts):
+        return orig(z_cols, cols, len(cols), lse, targets, opts)   # eps / (columns held), not eps / V
+    m.grad_logits_columns = grad_logits_columns
+
+
+def mut_columns_target_by_position(m):
+    orig = m.grad_logits_columns
+
+    def grad_logits_columns(z_cols, cols, v, lse, targets, opts):
+        return orig(z_cols, np.arange(len(cols)), v, lse, targets, opts)   # one-hot by position
+    m.grad_logits_columns = grad_logits_columns
+
+
 MUTATIONS = [mut_drop_smoothing_sum, mut_zloss_grad_sign, mut_no_softcap_derivative,
              mut_target_off_by_one, mut_lse_missing_max, mut_mean_over_all_rows,
              mut_online_no_rescale, mut_smoothing_over_v_minus_1, mut_transposed_dw,
              mut_logits_ignore_softcap, mut_logits_unscaled_grad, mut_megatron_plain_eps,
              mut_argmax_last_tie, mut_accuracy_over_all_rows, mut_weighted_mean_over_rows,
-             mut_weighted_smoothing_unweighted, mut_bf16_as_fp16]
+             mut_weighted_smoothing_unweighted, mut_bf16_as_fp16,
+             mut_columns_smoothing_over_held, mut_columns_target_by_position]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
