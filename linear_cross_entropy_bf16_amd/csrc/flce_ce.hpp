@@ -108,9 +108,9 @@ __device__ __forceinline__ float softcapped(float r, float c, float inv_c, bool 
   return on ? c * fast_tanh(r * inv_c) : r;
 }
 
-// Running row statistics of one thread: m = max z, d = sum of
-// 2^(z log2e - h(m)) (see lse_merge), s = sum z (online-softmax recurrence,
-// page "Cutting LLM Memory by 84%", "Definition and Forward Pass").
+// Running row statistics of one thread: m = max z, d = sum of e^(z - m)
+// (see lse_merge), s = sum z (online-softmax recurrence, page "Cutting LLM
+// Memory by 84%", "Definition and Forward Pass").
 struct RowStats {
   float m, d, s;
 };
@@ -137,11 +137,10 @@ __device__ __forceinline__ void stats_add(RowStats& st, const float (&z)[N]) {
   }
   if (mx == -INFINITY) return;          // only masked (-inf) logits here
   const float m_new = fmax_fast(st.m, mx);
-  const float h_new = log2_units(m_new);
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) sum += fast_exp2(__builtin_fmaf(z[i], kLog2e, -h_new));
-  st.d = st.d * fast_exp2(log2_units(st.m) - h_new) + sum;   // st.m = -inf: the old sum is 0
+  for (int i = 0; i < N; ++i) sum += fast_exp2((z[i] - m_new) * kLog2e);
+  st.d = rescale_add(st.d, (st.m - m_new) * kLog2e, sum);   // st.m = -inf: the old sum is 0
   st.m = m_new;
 }
 
@@ -320,15 +319,11 @@ __device__ __forceinline__ void row_grad(const CeArgs<T>& a, const T* row, T* gr
 template <typename T, bool kSoftcap>
 __device__ __forceinline__ float row_finish(const CeArgs<T>& a, const T* row, int64_t r, int64_t t,
                                             const RowStats& st) {
-  // lse = m + lam; the row loss from m - z_t, exact where the target holds the
-  // row's maximum (see k_merge)
-  const float lam = log_rel_sum(st.m, st.d);
-  const float lse = st.m + lam;
   // a target outside [0, V) is reported by the status word; never read past the row
   const float zt = (t >= 0 && t < a.v) ? softcapped(ld_elem(row, t), a.softcap, a.inv_softcap, kSoftcap)
                                        : 0.f;
-  const float rl = a.keep_target * (st.m - zt) + lam + (a.eps * st.m - a.eps_over_v * st.s) +
-                   a.zloss * lse * lse;
+  const RowResult res = finish_row(st.m, st.d, zt, st.s, a.keep_target, a.eps, a.eps_over_v, a.zloss);
+  const float lse = res.lse, rl = res.loss;
   a.lse[r] = lse;
   a.row_loss_ws[r] = rl;
   if (a.row_loss) a.row_loss[r] = rl;

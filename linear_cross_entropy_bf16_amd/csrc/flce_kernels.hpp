@@ -76,34 +76,48 @@ __device__ __forceinline__ float tanh_q(float x) {
 __device__ __forceinline__ float tanh_from_q(float x, float q) { return __builtin_copysignf(1.0f - q, x); }
 __device__ __forceinline__ float fast_tanh(float x) { return tanh_from_q(x, tanh_q(x)); }
 
-// m log2e rounded to fp32 on its own, never fused with a neighbouring add or
-// subtract (the compiler contracts a*b - c into an fma by default): the
-// reference point h(m) of the running sums below.
-__device__ __forceinline__ float log2_units(float m) {
-#pragma clang fp contract(off)
-  return m * kLog2e;
-}
-
 // Online softmax state of a set of logits (page "Cutting LLM Memory by 84%",
 // "Definition and Forward Pass": a running maximum and a running sum of
-// exponentials rescaled whenever the maximum grows): m = max z in natural
-// units and d = sum of 2^(z log2e - h(m)).  (m, d) <- merged with (m2, d2).
+// exponentials rescaled whenever the maximum grows): m = max z and
+// d = sum of e^(z - m), each term evaluated as 2^((z - m) log2e).  z - m is
+// exact near the maximum, so the maximum's own term is exactly 1 and d holds
+// ln sum_v e^(z_v - m) to a few ulp of 1 whatever the size of |z|.
+// (m, d) <- merged with (m2, d2).  Contraction into fmas is off so that every
+// kernel (and every instantiation of one) rounds the merge identically.
 __device__ __forceinline__ void lse_merge(float& m, float& d, float m2, float d2) {
+#pragma clang fp contract(off)
   const float mx = fmaxf(m, m2);
   if (mx == -INFINITY) return;
-  const float h = log2_units(mx);
-  d = d * fast_exp2(log2_units(m) - h) + d2 * fast_exp2(log2_units(m2) - h);
+  d = d * fast_exp2((m - mx) * kLog2e) + d2 * fast_exp2((m2 - mx) * kLog2e);
   m = mx;
 }
 
-// ln sum_v e^(z_v - m) of a state (m, d).  h(m) = m log2e - lo, where lo (the
-// rounding error of that product, exact by the fma) corrects the reference
-// point.  lse = m + this; the row loss is formed as (m - z_t) + this, which
-// stays exact where the target is the row's maximum.
-__device__ __forceinline__ float log_rel_sum(float m, float d) {
-  const float h = log2_units(m);
-  const float lo = __builtin_fmaf(m, kLog2e, -h);
-  return (log2f(d) - lo) * kLn2;
+// d 2^x + sum, rounded the same way wherever the online update runs
+__device__ __forceinline__ float rescale_add(float d, float x, float sum) {
+#pragma clang fp contract(off)
+  return d * fast_exp2(x) + sum;
+}
+
+// lse and the row loss of a valid row from its merged state (m, d), target
+// logit z_t and sum of logits sz (page "Cutting LLM Memory by 84%",
+// "Definition and Forward Pass": lse - z_t; smoothing and z-loss terms of
+// the option set):
+//   lse  = m + lam,  lam = ln d = ln sum_v e^(z_v - m)
+//   loss = lse - (1-eps) z_t - (eps/V) sz + s lse^2
+//        = (1-eps)(m - z_t) + lam + (eps m - (eps/V) sz) + s lse^2
+// formed from m - z_t rather than lse - z_t: where the target holds the row's
+// maximum m - z_t is exactly 0 and the loss keeps the accuracy of lam, not the
+// ulp of lse.  Contraction off: identical rounding in every kernel.
+struct RowResult {
+  float lse, loss, gap;    // gap = lse - z_t, formed as (m - z_t) + lam
+};
+__device__ __forceinline__ RowResult finish_row(float m, float d, float zt, float sz, float keep,
+                                                float eps, float eps_over_v, float zloss) {
+#pragma clang fp contract(off)
+  const float lam = log2f(d) * kLn2;
+  const float lse = m + lam;
+  const float loss = keep * (m - zt) + lam + (eps * m - eps_over_v * sz) + zloss * lse * lse;
+  return RowResult{lse, loss, (m - zt) + lam};
 }
 
 #ifdef FLCE_HOST_KERNELS
@@ -237,7 +251,7 @@ struct FwdArgs {
   int64_t vt_base, vt_end;   // vocabulary tiles [vt_base, vt_end) of this launch
   int64_t chunk_base;        // partials row of this launch's first chunk
   float* part_m;          // [n_chunks, n] running max of z
-  float* part_d;          // [n_chunks, n] sum of 2^(z log2e - h(max)), see lse_merge
+  float* part_d;          // [n_chunks, n] sum of e^(z - max), see lse_merge
   float* part_s;          // [n_chunks, n] sum of z
   float* part_b;          // [n_chunks, n] largest z (predicted tokens only)
   int32_t* part_i;        // [n_chunks, n] its lowest vocabulary index
@@ -342,13 +356,12 @@ __device__ __forceinline__ void fwd_tile_epilogue(const FwdArgs<T>& a, const f32
         s_run[nb] += sz;
       }
       if (kMasked && mt == -INFINITY) continue;
-      // running maximum in natural units, sums relative to h(max) (see lse_merge)
+      // running maximum and sum of e^(z - max) (see lse_merge)
       const float m_new = fmax_fast(m_run[nb], mt);
-      const float h_new = log2_units(m_new);
       float sum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += fast_exp2(__builtin_fmaf(z[r], kLog2e, -h_new));
-      d_run[nb] = d_run[nb] * fast_exp2(log2_units(m_run[nb]) - h_new) + sum;
+      for (int r = 0; r < 16; ++r) sum += fast_exp2((z[r] - m_new) * kLog2e);
+      d_run[nb] = rescale_add(d_run[nb], (m_run[nb] - m_new) * kLog2e, sum);
       m_run[nb] = m_new;
     }
   }
@@ -509,12 +522,8 @@ struct MergeArgs {
 };
 
 #ifdef FLCE_HOST_KERNELS
-// lse = m + lam with lam = ln sum_v e^(z_v - m); row loss on valid rows
-//   lse - (1-eps) z_t - (eps/V) sum z + s lse^2
-//     = (1-eps)(m - z_t) + lam + eps m - (eps/V) sum z + s lse^2,
-// 0 elsewhere.  Formed from m - z_t (exact where the target holds the row's
-// maximum) rather than lse - z_t, so a confidently predicted row keeps the
-// accuracy of lam (a few ulp of 1) instead of the ulp of lse.
+// Partials merged in a fixed order -> lse and row loss (finish_row) on valid
+// rows, 0 elsewhere.
 static __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
   __shared__ double red[256];
   if (a.row0 + static_cast<int64_t>(blockIdx.x) * 256 >= a.n) return;   // whole block past the batch
@@ -527,17 +536,14 @@ static __global__ __launch_bounds__(256) void k_merge(MergeArgs a) {
       lse_merge(m, d, a.part_m[c * a.n + j], a.part_d[c * a.n + j]);
       s += a.part_s[c * a.n + j];
     }
-    const float lam = log_rel_sum(m, d);
-    const float lse = m + lam;
-    const float gap = (m - a.zt[j]) + lam;   // lse - z_t
+    const RowResult res = finish_row(m, d, a.zt[j], s, a.keep_target, a.eps, a.eps_over_v, a.zloss);
+    const float lse = res.lse;
     const int64_t r = a.rows[j];
-    float rl;
+    float rl = res.loss;
     if (a.weight) {   // (1-eps) w_t (lse - z_t) + (eps/V)(sum_v w_v lse - sum_v w_v z_v) + s w_t lse^2
       const int32_t t = a.targets[r];
       const float wt = (t >= 0 && t < a.v) ? a.weight[t] : 0.f;
-      rl = a.keep_target * wt * gap + a.eps_over_v * (a.ctl->wall * lse - s) + a.zloss * wt * lse * lse;
-    } else {
-      rl = a.keep_target * (m - a.zt[j]) + lam + (a.eps * m - a.eps_over_v * s) + a.zloss * lse * lse;
+      rl = a.keep_target * wt * res.gap + a.eps_over_v * (a.ctl->wall * lse - s) + a.zloss * wt * lse * lse;
     }
     a.lse[r] = lse;
     if (a.lsep) a.lsep[j] = lse;
