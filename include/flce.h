@@ -190,6 +190,20 @@ flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const v
                                float* lse, void* dx, void* dw, float* dbias, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* flce_fused_fwd_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results without the
+ * workspace arguments.  Its workspace is a 128 MiB array inside the library
+ * (one per GPU, held until the process ends); the call allocates nothing.
+ * Parameters whose flce_workspace_size(params, 1) exceeds 128 MiB return
+ * FLCE_ERR_WORKSPACE_TOO_SMALL before any HIP call (a smaller
+ * params->vocab_slice or params->token_chunk reduces the size).  Every call
+ * on one GPU uses the same array: calls that overlap on a GPU (other streams,
+ * other threads) race and must be serialised by the caller. */
+flce_status flce_fused_fwd_bwd_noalloc(const flce_params* params, const void* x, const void* w,
+                                       const void* bias, const int32_t* targets, float* loss,
+                                       float* lse, void* dx, void* dw, float* dbias, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Cross-entropy on logits given directly (no linear layer): the workload of
  * the cross-entropy kernels of the page "Add efficient Cross-Entropy by cuda

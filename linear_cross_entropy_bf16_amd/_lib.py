@@ -25,7 +25,7 @@ REDUCTIONS = {"mean": 0, "sum": 1, "none": 2}
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_forward_metrics", "flce_backward",
            "flce_fused_fwd_bwd", "flce_ce_workspace_size", "flce_ce_forward", "flce_ce_forward_metrics",
            "flce_ce_backward", "flce_ce_fused_fwd_bwd", "flce_stored_workspace_size",
-           "flce_fused_fwd_bwd_stored",
+           "flce_fused_fwd_bwd_stored", "flce_fused_fwd_bwd_noalloc",
            "flce_check_status", "flce_status_string", "flce_version")
 
 
@@ -84,6 +84,8 @@ def load():
     lib.flce_fused_fwd_bwd_stored.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                               _P]
     lib.flce_fused_fwd_bwd_stored.restype = ctypes.c_int
+    lib.flce_fused_fwd_bwd_noalloc.argtypes = [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.flce_fused_fwd_bwd_noalloc.restype = ctypes.c_int
     lib.flce_ce_workspace_size.argtypes = [pp]
     lib.flce_ce_workspace_size.restype = ctypes.c_size_t
     lib.flce_ce_forward.argtypes = [pp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -162,6 +164,14 @@ def fused_fwd_bwd_stored(params, x, w, bias, targets, loss, lse, dx, dw, dbias, 
                          stream) -> int:
     return load().flce_fused_fwd_bwd_stored(ctypes.byref(params), x, w, bias, targets, loss, lse, dx,
                                             dw, dbias, ws, ws_bytes, stream)
+
+
+NOALLOC_MAX_BYTES = 128 << 20   # the library's scratch array (include/flce.h)
+
+
+def fused_fwd_bwd_noalloc(params, x, w, bias, targets, loss, lse, dx, dw, dbias, stream) -> int:
+    return load().flce_fused_fwd_bwd_noalloc(ctypes.byref(params), x, w, bias, targets, loss, lse, dx,
+                                             dw, dbias, stream)
 
 
 def ce_workspace_size(params: Params) -> int:

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "flce.h"
@@ -225,6 +226,35 @@ void fill(float* p, int64_t count, float value, hipStream_t s) {
 }
 
 int64_t grid8(int64_t tiles) { return round_up(tiles, 8); }
+
+// ----------------------------------------------------------------- scratch
+// Device memory for callers that cannot allocate any (code under HIP graph
+// capture, serving loops or harnesses that forbid hipMalloc): a fixed array in
+// this library's code object, used by flce_fused_fwd_bwd_noalloc in place of
+// the caller's workspace.  Every GPU that loads the library holds its own copy
+// until the process ends.  In host code `scratch` names only a host-side
+// stand-in; its device address is looked up once per device (with that device
+// current) and only that address is handed to kernels.  The fused path writes
+// every byte of its workspace before reading it, so the array needs no
+// clearing between calls; calls that overlap on one GPU share it and race.
+constexpr size_t kScratchBytes = size_t{128} << 20;   // 128 MiB
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex scratch_mutex;
+void* scratch_ptr[64];                                 // per device ordinal
+
+flce_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FLCE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FLCE_ERR_DEVICE;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return FLCE_OK;
+}
 
 // ----------------------------------------------------------------- forward
 flce::FwdGrid fwd_grid(const Layout& L) {
@@ -867,14 +897,21 @@ flce_status flce_forward_metrics(const flce_params* params, const void* x, const
   return run_forward<float>(p, L, x, w, bias, targets, loss, lse, row_loss, ws, s, pred, accuracy);
 }
 
-static flce_status check_backward_args(const flce_params& p, const Layout& L, const float* lse,
-                                       void* dx, void* dw, float* dbias, const void* bias,
-                                       const void* ws, size_t ws_bytes) {
+static flce_status check_backward_outputs(const flce_params& p, const Layout& L, const float* lse,
+                                          void* dx, void* dw, float* dbias, const void* bias) {
   if (p.reduction == FLCE_REDUCTION_NONE) return FLCE_ERR_UNSUPPORTED;
   if (p.n > 0 && (!lse || !aligned(lse, 4) || !dx || !aligned(dx, 16))) return FLCE_ERR_INVALID_ARGUMENT;
   if (!dw || !aligned(dw, 16)) return FLCE_ERR_INVALID_ARGUMENT;
   if (bias && (!dbias || !aligned(dbias, 4))) return FLCE_ERR_INVALID_ARGUMENT;
   if (!pitch_ok(p, L.ldg) || !pitch_ok(p, L.ldt)) return FLCE_ERR_INVALID_ARGUMENT;
+  return FLCE_OK;
+}
+
+static flce_status check_backward_args(const flce_params& p, const Layout& L, const float* lse,
+                                       void* dx, void* dw, float* dbias, const void* bias,
+                                       const void* ws, size_t ws_bytes) {
+  const flce_status st = check_backward_outputs(p, L, lse, dx, dw, dbias, bias);
+  if (st != FLCE_OK) return st;
   const int64_t need = L.bwd_end > L.fwd_end ? L.bwd_end : L.fwd_end;
   return check_ws(ws, ws_bytes, need);
 }
@@ -897,6 +934,20 @@ flce_status flce_backward(const flce_params* params, const void* x, const void* 
   return run_backward<float>(p, L, x, w, bias, targets, lse, grad_output, dx, dw, dbias, ws, s, false);
 }
 
+static flce_status run_fused(const flce_params& p, const Layout& L, const void* x, const void* w,
+                             const void* bias, const int32_t* targets, float* loss, float* lse,
+                             void* dx, void* dw, float* dbias, void* ws, hipStream_t s) {
+  flce_status st;
+  if (p.dtype == FLCE_DTYPE_BF16) {
+    st = run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
+    if (st != FLCE_OK) return st;
+    return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s, true);
+  }
+  st = run_forward<float>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
+  if (st != FLCE_OK) return st;
+  return run_backward<float>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s, true);
+}
+
 flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const void* w,
                                const void* bias, const int32_t* targets, float* loss, float* lse,
                                void* dx, void* dw, float* dbias, void* ws, size_t ws_bytes,
@@ -909,15 +960,26 @@ flce_status flce_fused_fwd_bwd(const flce_params* params, const void* x, const v
   const Layout L = make_layout(p);
   if ((st = check_backward_args(p, L, lse, dx, dw, dbias, bias, ws, ws_bytes)) != FLCE_OK) return st;
   if ((st = ready_to_launch()) != FLCE_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.dtype == FLCE_DTYPE_BF16) {
-    st = run_forward<uint16_t>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
-    if (st != FLCE_OK) return st;
-    return run_backward<uint16_t>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s, true);
-  }
-  st = run_forward<float>(p, L, x, w, bias, targets, loss, lse, nullptr, ws, s);
+  return run_fused(p, L, x, w, bias, targets, loss, lse, dx, dw, dbias, ws, static_cast<hipStream_t>(stream));
+}
+
+flce_status flce_fused_fwd_bwd_noalloc(const flce_params* params, const void* x, const void* w,
+                                       const void* bias, const int32_t* targets, float* loss,
+                                       float* lse, void* dx, void* dw, float* dbias, void* stream) {
+  flce_status st = check_params(params);
   if (st != FLCE_OK) return st;
-  return run_backward<float>(p, L, x, w, bias, targets, lse, nullptr, dx, dw, dbias, ws, s, true);
+  const flce_params& p = *params;
+  if ((st = check_inputs(p, x, w, bias, targets)) != FLCE_OK) return st;
+  if (!loss || !aligned(loss, 4)) return FLCE_ERR_INVALID_ARGUMENT;
+  const Layout L = make_layout(p);
+  if ((st = check_backward_outputs(p, L, lse, dx, dw, dbias, bias)) != FLCE_OK) return st;
+  const int64_t need = L.bwd_end > L.fwd_end ? L.bwd_end : L.fwd_end;
+  if (need > static_cast<int64_t>(kScratchBytes)) return FLCE_ERR_WORKSPACE_TOO_SMALL;
+  if ((st = check_device()) != FLCE_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != FLCE_OK) return st;
+  if ((st = ready_to_launch()) != FLCE_OK) return st;
+  return run_fused(p, L, x, w, bias, targets, loss, lse, dx, dw, dbias, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t flce_stored_workspace_size(const flce_params* params) {

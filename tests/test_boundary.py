@@ -318,3 +318,24 @@ def test_binding_checks_caller_buffers():
             api._check_buffer(t, "dx", shape, dtype, cpu)
     with pytest.raises(ValueError):
         api._check_buffer(torch.zeros(4, 8), "dx", (4, 8), torch.float32, torch.device("cuda", 0))
+
+
+def test_noalloc_entry_point_validates_on_the_host(lib):
+    """flce_fused_fwd_bwd_noalloc refuses, before any HIP call, what the
+    workspace call refuses and any problem whose workspace exceeds the
+    library's scratch array."""
+    bf = _lib.DTYPE_BF16
+
+    def call(p, **kw):
+        a = dict(x=FAKE, w=FAKE, bias=None, t=FAKE, loss=FAKE, lse=FAKE, dx=FAKE, dw=FAKE, db=None)
+        a.update(kw)
+        return lib.flce_fused_fwd_bwd_noalloc(ctypes.byref(p), a["x"], a["w"], a["bias"], a["t"], a["loss"],
+                                              a["lse"], a["dx"], a["dw"], a["db"], None)
+
+    big = P(dtype=bf, n=4096, d=2048, v=32000)
+    assert _lib.workspace_size(big, True) > _lib.NOALLOC_MAX_BYTES
+    assert call(big) == _lib.FLCE_ERR_WORKSPACE_TOO_SMALL
+    assert call(P(dtype=bf, reduction="none")) == _lib.FLCE_ERR_UNSUPPORTED
+    assert call(P(dtype=bf, d=12)) == _lib.FLCE_ERR_INVALID_ARGUMENT
+    assert call(P(dtype=bf), dx=FAKE + 4) == _lib.FLCE_ERR_INVALID_ARGUMENT      # misaligned dX
+    assert call(P(dtype=bf), bias=FAKE) == _lib.FLCE_ERR_INVALID_ARGUMENT        # bias without dbias
