@@ -280,15 +280,20 @@ __device__ __forceinline__ void frags(u32x4 (&f)[4], const char* src, int base, 
     f[b] = *reinterpret_cast<const u32x4*>(src + kmaj_off(base + b * 32 + (lane & 31), chunk));
 }
 
-// Scheduling groups (masks: 0x008 MFMA, 0x100 DS read, 0x020 VMEM read): a
-// fragment read and, in the steps that carry them, a slab load after each of
-// the step's 16 MFMAs.
+// Scheduling groups (masks: 0x008 MFMA, 0x100 DS read, 0x020 VMEM read): the
+// next step's 8 fragment reads after the step's first 8 MFMAs, one each, and,
+// in the steps that carry them, the 8 slab loads after its last 8 MFMAs.
+// The fragment reads must come before the slab loads in program order: a
+// buffer_load ... lds writes LDS, and the compiler cannot tell that it writes
+// a slot no read of this step touches, so reads placed after the loads were
+// held behind all of them (into the step's last MFMAs, where the next step
+// then waited for them).
 template <bool kLoads, int I = 0>
 __device__ __forceinline__ void interleave() {
   if constexpr (I < 16) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if constexpr (kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if constexpr (I < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (kLoads && I >= 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     interleave<kLoads, I + 1>();
   }
 }
@@ -367,8 +372,8 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
   load_frags(a0, b0, 0, 0);
   // One slab of the loop; `issue` sends out the slabs two ahead.
   auto slab = [&](int64_t s, auto issue) {
+    load_frags(a1, b1, 0, 1);                       // reads first (see interleave)
     issue(sa, (s + 2) * kBK, slot(4));              // B(s-1)'s slot
-    load_frags(a1, b1, 0, 1);
     mfmas(a0, b0);
     interleave<true>();
     load_frags(a0, b0, 0, 2);
@@ -386,8 +391,8 @@ __device__ __forceinline__ void gemm_tile_dma(const Operand<uint16_t>& A,
     // own reads of slab s done; after the barrier both hold for every wave
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
     __builtin_amdgcn_s_barrier();
-    issue(sb, (s + 2) * kBK, slot(5));              // A(s)'s slot
     load_frags(a0, b0, 2, 0);
+    issue(sb, (s + 2) * kBK, slot(5));              // A(s)'s slot
     mfmas(a1, b1);
     interleave<true>();
     p = p >= 3 ? p - 3 : p + 2;
