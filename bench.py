@@ -142,7 +142,7 @@ def main():
                     help="backward over this many packed rows at a time (0 = whole batch)")
     ap.add_argument("--dw-bf16", action="store_true", help="dW in bf16 instead of fp32")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the extra measurement of the stored-logits schedule")
+                    help="skip the extra measurements (stored-logits schedule, token sweep)")
     ap.add_argument("--stored-logits", action="store_true",
                     help="three-contraction schedule: logits kept per token chunk, not recomputed "
                          "(6 N D V FLOPs; the MFMA fractions are then quoted against 6 N D V)")
@@ -291,6 +291,9 @@ def main():
     variants = None
     if not args.no_variants and not args.stored_logits and wl.dtype == "bf16":
         variants = {"stored_logits": bench_stored_variant(args, wl, x, w, t, b, opts, dev, n_valid)}
+        if wl.name == "llama3_8b_batch8" and not args.graph:
+            variants["token_sweep"] = bench_token_sweep(args, wl, x, w, t, dev)
+            variants["llama3_8b_seq"] = bench_workload_variant(args, W.WORKLOADS["llama3_8b_seq"], dev)
 
     cpu = None
     if args.cpu_rows > 0:
@@ -348,6 +351,85 @@ def main():
     if variants:
         result["variants"] = variants
     print(json.dumps(result), flush=True)
+
+
+def _time_fused(args, n, d, v, x, w, t, b, opts, dev, steps):
+    """(mean, p50, min ms per fused step, peak bytes of the step's own
+    buffers on top of the inputs, workspace bytes) of one configuration."""
+    import torch
+    from linear_cross_entropy_bf16_amd import api
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    nbytes = api.workspace_bytes(n, d, v, x.dtype, True, **opts)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = (torch.empty(1, dtype=torch.float32, device=dev), torch.empty(n, dtype=torch.float32, device=dev),
+           torch.empty((n, d), dtype=x.dtype, device=dev), torch.empty((v, d), dtype=torch.float32, device=dev),
+           torch.empty(v, dtype=torch.float32, device=dev) if b is not None else None)
+
+    def step():
+        api.fused_fwd_bwd(x, w, t, b, workspace=ws, out=out, **opts)
+
+    for _ in range(max(1, min(args.warmup, 2))):
+        step()
+    ms, ms_p50, ms_min = timed_steps(step, steps, torch.cuda.current_stream(dev))
+    extra = torch.cuda.max_memory_allocated(dev) - base
+    loss = float(out[0].item())
+    del ws, out
+    return ms, ms_p50, ms_min, int(extra), int(nbytes), loss
+
+
+def _fused_record(wl_name, n, d, v, n_valid, ms, ms_p50, ms_min, extra, nbytes, inputs, loss, steps):
+    flops = 8.0 * n * d * v
+    return {"workload": wl_name, "n": n, "d": d, "v": v, "steps": steps, "ms_per_step": round(ms, 3),
+            "ms_p50": round(ms_p50, 3), "ms_min": round(ms_min, 3),
+            "tokens_per_s": round(n / (ms * 1e-3), 1),
+            "mfma_frac_8ndv": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "mfma_frac_8ndv_valid_rows": round(8.0 * n_valid * d * v / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "n_valid": int(n_valid), "peak_hbm_bytes": int(extra + inputs), "workspace_bytes": nbytes,
+            "loss": loss}
+
+
+def bench_token_sweep(args, wl, x, w, t, dev):
+    """Tokens-per-step sweep at V = 128256, D = 4096 (the pages' BT sweep at
+    this vocabulary): the fused step on the first N rows of the headline
+    batch (same recipe, 10% ignored), N = 8192, 16384, 32768; the headline
+    itself is N = 65536.  Reported beside the headline, never as it."""
+    res = []
+    ign = wl.ignore_index
+    for n in (8192, 16384, 32768):
+        steps = max(3, min(args.steps, 10))
+        xs, ts = x[:n], t[:n]
+        n_valid = int((ts != ign).sum().item())
+        ms, p50, mn, extra, nbytes, loss = _time_fused(
+            args, n, wl.d, wl.v, xs, w, ts, None,
+            dict(ignore_index=ign, reduction=wl.reduction), dev, steps)
+        inputs = xs.numel() * 2 + w.numel() * 2 + ts.numel() * 4
+        log(f"token sweep N={n}: {ms:.3f} ms/step")
+        res.append(_fused_record(f"first {n} rows of {wl.name}", n, wl.d, wl.v, n_valid, ms, p50, mn,
+                                 extra, nbytes, inputs, loss, steps))
+    return res
+
+
+def bench_workload_variant(args, wl, dev):
+    """Another workload's fused step (its own seeded inputs), reported beside
+    the headline: one 8-way data-parallel share of the headline batch."""
+    import torch
+    from linear_cross_entropy_bf16_amd import workloads as W
+    inp = W.generate(wl)
+    x = torch.from_numpy(inp["x"]).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(inp["w"]).view(torch.bfloat16).to(dev)
+    t = torch.from_numpy(inp["targets"]).to(dev)
+    n_valid = int((inp["targets"] != wl.ignore_index).sum())
+    steps = max(3, min(args.steps, 10))
+    ms, p50, mn, extra, nbytes, loss = _time_fused(
+        args, wl.n, wl.d, wl.v, x, w, t, None, dict(ignore_index=wl.ignore_index, reduction=wl.reduction),
+        dev, steps)
+    log(f"{wl.name}: {ms:.3f} ms/step")
+    inputs = x.numel() * 2 + w.numel() * 2 + t.numel() * 4
+    rec = _fused_record(wl.name, wl.n, wl.d, wl.v, n_valid, ms, p50, mn, extra, nbytes, inputs, loss, steps)
+    del x, w, t
+    return rec
 
 
 def bench_stored_variant(args, wl, x, w, t, b, opts, dev, n_valid):

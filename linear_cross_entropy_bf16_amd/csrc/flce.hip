@@ -31,9 +31,11 @@ constexpr int64_t kSliceBytes = 1ll << 30;   // ... shrunk until one G slice fit
 // 1 GiB each) makes the step 4.5% faster than 4096, 16384 only 1% more.
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 // Output tiles per raster group along the token dimension: consecutive
-// workgroups on one XCD share W tiles in that XCD's L2 (4 measured ~2% faster
-// than 2 or 8 at 65536 x 4096 x 128256, and far faster than 16 or 32).
+// workgroups on one XCD share W tiles in that XCD's L2.  Measured at
+// 65536 x 4096 x 128256 on one box: the G kernel is fastest with 4 (8: 2.7%
+// slower; 16 and 32 far slower), the forward with 8 (1.8% faster than 4).
 constexpr int kRasterGroup = 4;
+constexpr int kFwdRasterGroup = 8;
 // Extra elements in the row pitch of the backward's internal K-major buffers.
 // A 256-row slab read with a pitch of a large power of two (N = 65536 tokens:
 // 128 KiB) lands on few L2 channels; 256 more bytes per row spread it (the
@@ -311,7 +313,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.v = p.v;
   a.softcap = p.softcap;
   a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
-  a.group = kRasterGroup;
+  a.group = kFwdRasterGroup;
   a.part_m = reinterpret_cast<float*>(at(ws, L.part_m));
   a.part_d = reinterpret_cast<float*>(at(ws, L.part_d));
   a.part_s = reinterpret_cast<float*>(at(ws, L.part_s));
@@ -606,7 +608,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       a.v = p.v;
       a.softcap = p.softcap;
       a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
-      a.group = kRasterGroup;
+      a.group = kFwdRasterGroup;
       a.part_m = reinterpret_cast<float*>(at(ws, L.part_m)) + c0;
       a.part_d = reinterpret_cast<float*>(at(ws, L.part_d)) + c0;
       a.part_s = reinterpret_cast<float*>(at(ws, L.part_s)) + c0;
