@@ -33,9 +33,9 @@ _CSRC = os.path.join(ROOT, "linear_cross_entropy_bf16_amd", "csrc")
 # committed counter summaries, and the sources each measured kernel is built from
 TRAFFIC = {
     "k_fwd": (os.path.join(ROOT, "profiles", "k_fwd_llama3_8b_batch8_traffic.json"),
-              ("flce_gemm.hpp", "flce_kernels.hpp", "flce.hip")),
+              ("flce_gemm.hpp", "flce_kernels.hpp", "flce_launch.hpp", "flce_fwd.hip", "flce.hip")),
     "k_ce_fused": (os.path.join(ROOT, "profiles", "k_ce_fused_ce_logits_llama3_8b_seq_traffic.json"),
-                   ("flce_kernels.hpp", "flce_ce.hpp", "flce.hip")),
+                   ("flce_kernels.hpp", "flce_ce.hpp", "flce_launch.hpp", "flce_ce.hip", "flce.hip")),
 }
 
 

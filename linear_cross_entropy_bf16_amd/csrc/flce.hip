@@ -45,6 +45,10 @@ constexpr int64_t kPitchPad = 128;
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// blocks of the target scan and the bytes of their partials
+int64_t prep_blocks(int64_t n) { return n > 0 ? cdiv(n, flce::kPrepRows) : 1; }
+int64_t prep_bytes(int64_t n) { return prep_blocks(n) * static_cast<int64_t>(sizeof(flce::PrepPart)); }
+
 // ----------------------------------------------------------------- layout
 struct Layout {
   int64_t elem;           // bytes per X/W element
@@ -55,7 +59,7 @@ struct Layout {
   int64_t ldt;            // token pitch of X^T and G^T (chunk, plus kPitchPad)
   int64_t n_merge_blocks;
   // byte offsets from the workspace base
-  int64_t ctl, rows, tc, xc;   // shared by forward and backward
+  int64_t ctl, prep, rows, tc, xc;   // shared by forward and backward
   int64_t zt, part_m, part_d, part_s, block_sums;
   int64_t part_b, part_i, pred, hits, hit_sums, fwd_end;   // predicted tokens / accuracy
   int64_t g, gt, xt, wt, dx_acc, lsep, bwd_end;
@@ -98,6 +102,7 @@ Layout make_layout(const flce_params& p) {
   int64_t off = 0;
   L.ctl = off;
   off += kAlign;
+  L.prep = off;        off = round_up(off + prep_bytes(p.n), kAlign);
   // valid rows packed to the front: row map, targets and rows of X
   L.rows = off;        off = round_up(off + 4 * p.n, kAlign);
   L.tc = off;          off = round_up(off + 4 * p.n, kAlign);
@@ -229,6 +234,20 @@ void fill(float* p, int64_t count, float value, hipStream_t s) {
 
 int64_t grid8(int64_t tiles) { return round_up(tiles, 8); }
 
+// Target scan: range check, the ordered map of the valid rows, n_valid, the
+// class-weight sums and the gradient scale in the control block.
+void prep(const flce_params& p, void* ws, int64_t ctl_off, int64_t prep_off, int64_t rows_off,
+          const int32_t* targets, const float* grad_output, const float* weight, hipStream_t s) {
+  const unsigned nb = static_cast<unsigned>(prep_blocks(p.n));
+  auto* part = reinterpret_cast<flce::PrepPart*>(at(ws, prep_off));
+  hipLaunchKernelGGL(flce::k_prep_count, dim3(nb), dim3(flce::kPrepRows), 0, s, targets, p.n, p.v,
+                     p.ignore_index, weight, part);
+  hipLaunchKernelGGL(flce::k_prep_scatter, dim3(nb), dim3(flce::kPrepRows), 0, s, targets, p.n, p.v,
+                     p.ignore_index, grad_output, p.reduction == FLCE_REDUCTION_MEAN ? 1 : 0, weight,
+                     static_cast<const flce::PrepPart*>(part), reinterpret_cast<Ctl*>(at(ws, ctl_off)),
+                     reinterpret_cast<int32_t*>(at(ws, rows_off)));
+}
+
 // ----------------------------------------------------------------- scratch
 // Device memory for callers that cannot allocate any (code under HIP graph
 // capture, serving loops or harnesses that forbid hipMalloc): a fixed array in
@@ -292,8 +311,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   int32_t* rows = reinterpret_cast<int32_t*>(at(ws, L.rows));
   int32_t* tc = reinterpret_cast<int32_t*>(at(ws, L.tc));
   T* xc = reinterpret_cast<T*>(at(ws, L.xc));
-  hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows, p.class_weight);
+  prep(p, ws, L.ctl, L.prep, L.rows, targets, nullptr, p.class_weight, s);
   if (p.n == 0) {
     if (p.reduction != FLCE_REDUCTION_NONE) fill(loss, 1, 0.f, s);
     if (accuracy) fill(accuracy, 1, 0.f, s);
@@ -421,17 +439,17 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
                          const float* grad_output, void* dx, void* dw, float* dbias, void* ws,
                          hipStream_t s, bool packed) {
   Ctl* ctl = reinterpret_cast<Ctl*>(at(ws, L.ctl));
-  const bool mean = p.reduction == FLCE_REDUCTION_MEAN;
   int32_t* rows = reinterpret_cast<int32_t*>(at(ws, L.rows));
   int32_t* tc = reinterpret_cast<int32_t*>(at(ws, L.tc));
   T* xc = reinterpret_cast<T*>(at(ws, L.xc));
-  hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     grad_output, mean ? 1 : 0, ctl, rows, p.class_weight);
-  // the fused call reuses the forward's packed rows
-  if (!packed && p.n > 0)
-    hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
-                       static_cast<const T*>(x), p.d, targets, static_cast<const int32_t*>(rows),
-                       static_cast<const Ctl*>(ctl), xc, tc);
+  // the fused call reuses the forward's scan (grad_output 1 there as well) and packed rows
+  if (!packed) {
+    prep(p, ws, L.ctl, L.prep, L.rows, targets, grad_output, p.class_weight, s);
+    if (p.n > 0)
+      hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
+                         static_cast<const T*>(x), p.d, targets, static_cast<const int32_t*>(rows),
+                         static_cast<const Ctl*>(ctl), xc, tc);
+  }
   T* g = reinterpret_cast<T*>(at(ws, L.g));
   T* gt = reinterpret_cast<T*>(at(ws, L.gt));
   T* xt = reinterpret_cast<T*>(at(ws, L.xt));
@@ -580,8 +598,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
   T* wt = reinterpret_cast<T*>(at(ws, S.wt));
   float* lsep = reinterpret_cast<float*>(at(ws, S.lsep));
   const T* W = static_cast<const T*>(w);
-  hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     static_cast<const float*>(nullptr), mean ? 1 : 0, ctl, rows, p.class_weight);
+  prep(p, ws, L.ctl, L.prep, L.rows, targets, nullptr, p.class_weight, s);
   if (p.n > 0)
     hipLaunchKernelGGL((flce::k_gather_rows<T>), dim3(static_cast<unsigned>(p.n)), dim3(256), 0, s,
                        static_cast<const T*>(x), p.d, targets, static_cast<const int32_t*>(rows),
@@ -724,7 +741,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
 // ------------------------------------------------- cross-entropy on logits
 struct CeLayout {
   int64_t elem;
-  int64_t ctl, rows, row_loss, block_sums, pred, hits, hit_sums, end;
+  int64_t ctl, prep, rows, row_loss, block_sums, pred, hits, hit_sums, end;
   int64_t n_blocks;
 };
 
@@ -734,6 +751,7 @@ CeLayout make_ce_layout(const flce_params& p) {
   L.n_blocks = cdiv(p.n, 256);
   int64_t off = 0;
   L.ctl = off;         off += kAlign;
+  L.prep = off;        off = round_up(off + prep_bytes(p.n), kAlign);
   L.rows = off;        off = round_up(off + 4 * p.n, kAlign);
   L.row_loss = off;    off = round_up(off + 4 * p.n, kAlign);
   L.block_sums = off;  off = round_up(off + 8 * L.n_blocks, kAlign);
@@ -793,10 +811,7 @@ flce::CeArgs<T> ce_args(const flce_params& p, const CeLayout& L, const void* log
 
 void ce_prep(const flce_params& p, const CeLayout& L, const int32_t* targets,
              const float* grad_output, void* ws, hipStream_t s) {
-  hipLaunchKernelGGL(flce::k_prep, dim3(1), dim3(1024), 0, s, targets, p.n, p.v, p.ignore_index,
-                     grad_output, p.reduction == FLCE_REDUCTION_MEAN ? 1 : 0,
-                     reinterpret_cast<Ctl*>(at(ws, L.ctl)), reinterpret_cast<int32_t*>(at(ws, L.rows)),
-                     static_cast<const float*>(nullptr));
+  prep(p, ws, L.ctl, L.prep, L.rows, targets, grad_output, nullptr, s);
 }
 
 void ce_reduce(const flce_params& p, const CeLayout& L, float* loss, void* ws, hipStream_t s) {

@@ -1,6 +1,7 @@
 // HIP kernels of the fused linear cross-entropy hot path (gfx950).
 //
-//   k_prep        target range check, n_valid, gradient scale
+//   k_prep_count, k_prep_scatter  target range check, ordered map of the valid
+//                 rows, n_valid, gradient scale (two passes over row blocks)
 //   k_fwd         logits tile by tile (MFMA) with an online-softmax epilogue:
 //                 per (row, vocabulary chunk) partial max / sum-exp / sum-z,
 //                 target logit captured by the one tile that holds it
@@ -120,73 +121,122 @@ __device__ __forceinline__ RowResult finish_row(float m, float d, float zt, floa
   return RowResult{lse, loss, (m - zt) + lam};
 }
 
-#ifdef FLCE_HOST_KERNELS
 // ------------------------------------------------------------------- prep
-static __global__ __launch_bounds__(1024) void k_prep(const int32_t* __restrict__ targets, int64_t n,
-                                               int64_t v, int32_t ignore_index,
-                                               const float* __restrict__ grad_output,
-                                               int32_t reduction_mean, Ctl* __restrict__ ctl,
-                                               int32_t* __restrict__ rows,
-                                               const float* __restrict__ weight) {
-  // Wave w owns the contiguous rows [w * per, (w + 1) * per) and walks them 64
-  // at a time (coalesced); a ballot gives each valid row its place, so the
-  // valid rows land in `rows` in row order.  With class weights, the valid
-  // rows' target weights and all the weights are summed too (fixed order).
-  __shared__ int32_t s_cnt[16];
-  __shared__ int32_t s_bad[16];
-  __shared__ double s_w[2][16];
+// Target scan in two passes over blocks of kPrepRows rows (one thread per
+// row), so it spreads over the GPU at any N: k_prep_count reduces each block
+// to its valid-row count, range flag and weight sums (a PrepPart); then
+// k_prep_scatter gives each valid row its place in the ordered row map from
+// the counts of the blocks before it and a ballot within the block, and
+// block 0 sums the partials in block order into the control block.  Every
+// sum has a fixed order.
+constexpr int kPrepRows = 1024;
+
+struct PrepPart {
+  int32_t count;   // valid rows of the block
+  int32_t bad;     // 1 if a target of the block is out of range
+  double wt;       // sum of the class weights of the block's valid targets
+  double wa;       // sum of the class weights over the block's share of the vocabulary
+};
+
+#ifdef FLCE_HOST_KERNELS
+// fixed-order sum over the 1024 threads of a block (wave trees, then the 16
+// wave results in order); every thread gets the result
+__device__ __forceinline__ double block_sum_1024(double x, double* sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t per = ((n + 15) / 16 + 63) / 64 * 64;
-  const int64_t lo = wave * per, hi = lo + per < n ? lo + per : n;
-  int32_t cnt = 0, bad = 0;
-  double wt = 0.0, wa = 0.0;
-  for (int64_t i0 = lo; i0 < hi; i0 += 64) {
-    const int64_t i = i0 + lane;
-    const int32_t t = i < hi ? targets[i] : ignore_index;
-    const bool ok = t != ignore_index;
-    const bool in = ok && t >= 0 && static_cast<int64_t>(t) < v;
-    cnt += __popcll(__ballot(ok));
-    bad |= (ok && !in) ? 1 : 0;
-    if (weight && in) wt += weight[t];
-  }
-  if (weight)
-    for (int64_t c = static_cast<int64_t>(wave) * 64 + lane; c < v; c += 1024) wa += weight[c];
-  bad = __ballot(bad) != 0 ? 1 : 0;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    wt += __shfl_xor(wt, off);
-    wa += __shfl_xor(wa, off);
-  }
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  __syncthreads();
+  if (lane == 0) sm[wave] = x;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < 16; ++w) t += sm[w];
+  return t;
+}
+
+static __global__ __launch_bounds__(kPrepRows) void k_prep_count(const int32_t* __restrict__ targets,
+                                                                 int64_t n, int64_t v, int32_t ignore_index,
+                                                                 const float* __restrict__ weight,
+                                                                 PrepPart* __restrict__ part) {
+  __shared__ double sm[16];
+  __shared__ int32_t s_cnt[16], s_bad[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kPrepRows + threadIdx.x;
+  const int32_t t = i < n ? targets[i] : ignore_index;
+  const bool ok = t != ignore_index;
+  const bool in = ok && t >= 0 && static_cast<int64_t>(t) < v;
+  const int32_t cnt = __popcll(__ballot(ok));
+  const int32_t bad = __ballot(ok && !in) != 0 ? 1 : 0;
   if (lane == 0) {
     s_cnt[wave] = cnt;
     s_bad[wave] = bad;
-    s_w[0][wave] = wt;
-    s_w[1][wave] = wa;
   }
-  __syncthreads();
-  int32_t k = 0, nv = 0, any_bad = 0;
-  for (int w = 0; w < 16; ++w) {
-    k += w < wave ? s_cnt[w] : 0;
-    nv += s_cnt[w];
-    any_bad |= s_bad[w];
-  }
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes under this one
-  for (int64_t i0 = lo; i0 < hi; i0 += 64) {
-    const int64_t i = i0 + lane;
-    const bool ok = i < hi && targets[i] != ignore_index;
-    const uint64_t m = __ballot(ok);
-    if (ok) rows[k + __popcll(m & below)] = static_cast<int32_t>(i);
-    k += __popcll(m);
+  double wt = 0.0, wa = 0.0;
+  if (weight) {
+    wt = in ? static_cast<double>(weight[t]) : 0.0;
+    // this block's share of the vocabulary for the sum of all class weights
+    const int64_t per = (v + gridDim.x - 1) / gridDim.x;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * per;
+    const int64_t c1 = c0 + per < v ? c0 + per : v;
+    for (int64_t c = c0 + threadIdx.x; c < c1; c += kPrepRows) wa += weight[c];
+    wt = block_sum_1024(wt, sm);
+    wa = block_sum_1024(wa, sm);
+  } else {
+    __syncthreads();
   }
   if (threadIdx.x == 0) {
-    double wts = 0.0, was = 0.0;
+    int32_t c = 0, b = 0;
     for (int w = 0; w < 16; ++w) {
-      wts += s_w[0][w];
-      was += s_w[1][w];
+      c += s_cnt[w];
+      b |= s_bad[w];
     }
+    part[blockIdx.x] = PrepPart{c, b, wt, wa};
+  }
+}
+
+static __global__ __launch_bounds__(kPrepRows) void k_prep_scatter(
+    const int32_t* __restrict__ targets, int64_t n, int64_t v, int32_t ignore_index,
+    const float* __restrict__ grad_output, int32_t reduction_mean, const float* __restrict__ weight,
+    const PrepPart* __restrict__ part, Ctl* __restrict__ ctl, int32_t* __restrict__ rows) {
+  __shared__ double sm[16];
+  __shared__ int32_t s_cnt[16];
+  __shared__ int64_t s_base;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = gridDim.x;
+  // valid rows of the blocks before this one
+  int64_t before = 0;
+  for (int j = threadIdx.x; j < static_cast<int>(blockIdx.x); j += kPrepRows) before += part[j].count;
+  const double base = block_sum_1024(static_cast<double>(before), sm);   // exact: an integer < 2^23
+  if (threadIdx.x == 0) s_base = static_cast<int64_t>(base);
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kPrepRows + threadIdx.x;
+  const bool ok = i < n && targets[i] != ignore_index;
+  const uint64_t m = __ballot(ok);
+  if (lane == 0) s_cnt[wave] = __popcll(m);
+  __syncthreads();
+  int64_t k = s_base;
+  for (int w = 0; w < wave; ++w) k += s_cnt[w];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes under this one
+  if (ok) rows[k + __popcll(m & below)] = static_cast<int32_t>(i);
+  if (blockIdx.x != 0) return;
+  // block 0: totals over all blocks, each thread a contiguous range in order
+  const int per = (nb + kPrepRows - 1) / kPrepRows;
+  const int j0 = threadIdx.x * per, j1 = j0 + per < nb ? j0 + per : nb;
+  int64_t nv = 0;
+  int32_t any_bad = 0;
+  double wts = 0.0, was = 0.0;
+  for (int j = j0; j < j1; ++j) {
+    nv += part[j].count;
+    any_bad |= part[j].bad;
+    wts += part[j].wt;
+    was += part[j].wa;
+  }
+  nv = static_cast<int64_t>(block_sum_1024(static_cast<double>(nv), sm));
+  any_bad = block_sum_1024(static_cast<double>(any_bad), sm) > 0.0 ? 1 : 0;
+  wts = block_sum_1024(wts, sm);
+  was = block_sum_1024(was, sm);
+  if (threadIdx.x == 0) {
     const float g = grad_output ? grad_output[0] : 1.0f;
     const float den = weight ? static_cast<float>(wts) : static_cast<float>(nv);
-    ctl->n_valid = nv;
+    ctl->n_valid = static_cast<int32_t>(nv);
     ctl->status = any_bad;
     ctl->wsum = den;
     ctl->wall = weight ? static_cast<float>(was) : static_cast<float>(v);
