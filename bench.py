@@ -142,7 +142,8 @@ def main():
                     help="backward over this many packed rows at a time (0 = whole batch)")
     ap.add_argument("--dw-bf16", action="store_true", help="dW in bf16 instead of fp32")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the extra measurements (stored-logits schedule, token sweep)")
+                    help="skip the extra measurements (stored-logits schedule, token sweep, one-sequence "
+                         "share, library GEMM floor)")
     ap.add_argument("--stored-logits", action="store_true",
                     help="three-contraction schedule: logits kept per token chunk, not recomputed "
                          "(6 N D V FLOPs; the MFMA fractions are then quoted against 6 N D V)")
@@ -294,6 +295,7 @@ def main():
         if wl.name == "llama3_8b_batch8" and not args.graph:
             variants["token_sweep"] = bench_token_sweep(args, wl, x, w, t, dev)
             variants["llama3_8b_seq"] = bench_workload_variant(args, W.WORKLOADS["llama3_8b_seq"], dev)
+            variants["library_gemm_floor"] = bench_library_floor(args, wl, x, w, t, dev, ms)
 
     cpu = None
     if args.cpu_rows > 0:
@@ -430,6 +432,49 @@ def bench_workload_variant(args, wl, dev):
     rec = _fused_record(wl.name, wl.n, wl.d, wl.v, n_valid, ms, p50, mn, extra, nbytes, inputs, loss, steps)
     del x, w, t
     return rec
+
+
+def bench_library_floor(args, wl, x, w, t, dev, fused_ms):
+    """The same step's four contractions as plain library GEMMs (hipBLASLt
+    through torch.matmul), no epilogues: logits of the valid rows per
+    8192-wide vocabulary slice for the forward, then per slice the recomputed
+    logits, dW of the slice (logits^T X) and dX += logits W.  Outputs in bf16
+    (dW and the dX running sum included, so it moves fewer bytes than the
+    fused step).  Timed on the same GPU right after the fused step, as the
+    speed the vendor's GEMMs reach on the same 8 n_valid D V MFMA work under
+    the same power limit; the ratio is the fused step over it."""
+    import torch
+    ign = wl.ignore_index
+    xv = x[t != ign].contiguous()
+    nv = xv.shape[0]
+    width = 8192
+    z = torch.empty((nv, width), dtype=x.dtype, device=dev)
+    dw = torch.empty((wl.v, wl.d), dtype=x.dtype, device=dev)
+    dx = torch.zeros((nv, wl.d), dtype=x.dtype, device=dev)
+    slices = [(a, min(wl.v, a + width)) for a in range(0, wl.v, width)]
+
+    def step():
+        for a, b in slices:
+            torch.matmul(xv, w[a:b].t(), out=z[:, :b - a])
+        for a, b in slices:
+            zs = z[:, :b - a]
+            torch.matmul(xv, w[a:b].t(), out=zs)
+            torch.matmul(zs.t(), xv, out=dw[a:b])
+            dx.addmm_(zs, w[a:b])
+
+    step()
+    steps = max(3, min(args.steps, 5))
+    ms, ms_p50, ms_min = timed_steps(step, steps, torch.cuda.current_stream(dev))
+    log(f"library GEMM floor: {ms:.3f} ms/step (fused {fused_ms:.3f})")
+    res = {"what": "hipBLASLt (torch.matmul) bf16 GEMMs of the same step on the valid rows: "
+                   "forward logits and, per 8192-wide vocabulary slice, recomputed logits, "
+                   "dW slice and dX running sum; no epilogues, bf16 outputs",
+           "n_valid": int(nv), "steps": steps, "ms_per_step": round(ms, 3),
+           "ms_p50": round(ms_p50, 3), "ms_min": round(ms_min, 3),
+           "tflops_executed": round(8.0 * nv * wl.d * wl.v / (ms * 1e-3) / 1e12, 1),
+           "fused_step_over_floor": round(fused_ms / ms, 4)}
+    del xv, z, dw, dx
+    return res
 
 
 def bench_stored_variant(args, wl, x, w, t, b, opts, dev, n_valid):

@@ -756,41 +756,60 @@ __device__ __forceinline__ void store1(uint16_t* p, float a) {
 __device__ __forceinline__ void store1(float* p, float a) { *p = a; }
 
 // bf16 G tile -> G [n, ldg] and G^T [gcols, ldt] through LDS (free again once
-// gemm_tile returns): the tile is staged once per orientation with rows padded
-// to 528 bytes, then every row leaves as 32 coalesced 16-byte stores.
-constexpr int kStagePitch = 264;   // bf16 elements per staged row (256 + 8)
+// gemm_tile returns): the tile is staged once per orientation, then every row
+// leaves as 32 coalesced 16-byte stores.
+// G (row = token): rows padded to 528 bytes.
+constexpr int kStagePitch = 264;   // bf16 elements per staged token row (256 + 8)
 static_assert(256 * kStagePitch * 2 <= tile::kLdsBytes, "staged G tile exceeds LDS");
+// G^T (row = vocabulary): rows 576 bytes apart, and in rows with bit 2 set the
+// 16-byte chunks are moved by 8.  A wave's 4-byte write below covers tile rows
+// r, r+1, r+4, r+5 (r even) at 16 consecutive token pairs each; the pitch puts
+// r and r+1 16 banks apart, the chunk move r+4 and r+5 another 32, so the 64
+// lanes hit 64 distinct banks.
+constexpr int kStagePitchT = 288;
+static_assert(256 * kStagePitchT * 2 <= tile::kLdsBytes, "staged G^T tile exceeds LDS");
+__device__ __forceinline__ int gt_stage_off(int row, int col) {
+  return row * kStagePitchT + ((((col >> 3) ^ (((row >> 2) & 1) << 3)) << 3) | (col & 7));
+}
 
-// G tile held as bf16 pairs -> G [n, ldg] and G^T [gcols, ldt] through LDS
-// (free again once gemm_tile returns): the tile is staged once per
-// orientation with rows padded to 528 bytes, then every row leaves as 32
-// coalesced 16-byte stores.  gp[nb][mb][2q + h] holds tile rows
-// vw + mb*32 + 8q + 2h and the next one, for token column nb.
+// gp[nb][mb][2q + h] holds tile rows vw + mb*32 + 8q + 2h and the next one,
+// for token column nb.
 template <typename T>
 __device__ __forceinline__ void store_g_staged(const GArgs<T>& a, const uint32_t (&gp)[4][4][8],
                                                char* lds, int64_t n0, int64_t vl0, int vw, int wn,
                                                int lane, int tid, int64_t nv) {
   uint16_t* sm = reinterpret_cast<uint16_t*>(lds);
   const int tcol = wn * 128 + (lane & 31);        // tile-local token of (nb = 0)
-  // G^T: staged row = vocabulary, 256 tokens per row; the two halves of a
-  // pair go to consecutive rows
+  // G^T: neighbouring lanes hold neighbouring tokens, so each pair of lanes
+  // swaps its words (DPP, lanes 2k <-> 2k+1) and keeps one half of each: the
+  // even lane then holds row vl for its token and the next, the odd lane row
+  // vl + 1 for the previous token and its own, and each writes one 4-byte
+  // word.  Address: row (vw + odd) + the block's row offset, token
+  // (tcol - odd) + 32 nb, with the chunk move of gt_stage_off folded into nb
+  // (for lanes 32..63, whose rows have bit 2 set, 8 chunks = token block nb ^ 2).
+  const int odd = lane & 1, hi = lane >> 5;
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;   // v_perm bytes: odd {o.hi, w.hi}, even {w.lo, o.lo}
+  const int base = (vw + odd) * kStagePitchT + (tcol - odd);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < 4; ++nb) {
+    uint16_t* col = sm + base + 32 * (nb ^ (2 * hi));
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int vl = vw + mb * 32 + 8 * (i >> 1) + 2 * (i & 1);
         const uint32_t w = gp[nb][mb][i];
-        sm[vl * kStagePitch + tcol + nb * 32] = static_cast<uint16_t>(w);
-        sm[(vl + 1) * kStagePitch + tcol + nb * 32] = static_cast<uint16_t>(w >> 16);
+        const uint32_t o = static_cast<uint32_t>(
+            __builtin_amdgcn_mov_dpp(static_cast<int>(w), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+        *reinterpret_cast<uint32_t*>(col + (mb * 32 + 8 * (i >> 1) + 2 * (i & 1)) * kStagePitchT) =
+            __builtin_amdgcn_perm(o, w, sel);
       }
+  }
   __syncthreads();
   const int chunk = tid & 31, row0 = tid >> 5;
 #pragma unroll 4
   for (int i = 0; i < 32; ++i) {
     const int row = row0 + 8 * i;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(sm + row * kStagePitch + chunk * 8);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(sm + gt_stage_off(row, chunk * 8));
     *reinterpret_cast<u32x4*>(a.gt + (vl0 + row) * a.ldt + n0 + chunk * 8) = v;
   }
   __syncthreads();
