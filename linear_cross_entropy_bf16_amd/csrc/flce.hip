@@ -226,6 +226,11 @@ flce_status launched() { return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE
 
 char* at(void* ws, int64_t off) { return static_cast<char*>(ws) + off; }
 
+// Work-queue counters of the forward launches (take_item): 16 ints in bytes
+// 64..127 of the control block, after the Ctl fields.
+static_assert(sizeof(flce::Ctl) <= 64, "Ctl overlaps the forward's queue counters");
+int32_t* fwd_queue(void* ws, const Layout& L) { return reinterpret_cast<int32_t*>(at(ws, L.ctl + 64)); }
+
 void fill(float* p, int64_t count, float value, hipStream_t s) {
   if (count <= 0) return;
   hipLaunchKernelGGL(flce::k_fill, dim3(static_cast<unsigned>(cdiv(count, 256))), dim3(256), 0, s,
@@ -332,6 +337,7 @@ flce_status run_forward(const flce_params& p, const Layout& L, const void* x, co
   a.softcap = p.softcap;
   a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
   a.group = kFwdRasterGroup;
+  a.queue = fwd_queue(ws, L);
   a.part_m = reinterpret_cast<float*>(at(ws, L.part_m));
   a.part_d = reinterpret_cast<float*>(at(ws, L.part_d));
   a.part_s = reinterpret_cast<float*>(at(ws, L.part_s));
@@ -626,6 +632,7 @@ flce_status run_fused_stored(const flce_params& p, const StoredLayout& S, const 
       a.softcap = p.softcap;
       a.inv_softcap = p.softcap > 0.f ? 1.0f / p.softcap : 0.f;
       a.group = kFwdRasterGroup;
+      a.queue = fwd_queue(ws, L);
       a.part_m = reinterpret_cast<float*>(at(ws, L.part_m)) + c0;
       a.part_d = reinterpret_cast<float*>(at(ws, L.part_d)) + c0;
       a.part_s = reinterpret_cast<float*>(at(ws, L.part_s)) + c0;

@@ -454,6 +454,33 @@ __device__ __forceinline__ bool xcd_logical_n(int64_t wg, int64_t total, int64_t
   return i < per && L < total;
 }
 
+// Work queue over the XCDs: items [0, total) are cut into 8 contiguous ranges
+// of ceil(total / 8), range y meant for XCD y, and q[y] counts the items
+// handed out from range y.  A workgroup on XCD x takes the next item of its
+// own range and, once that is used up, of the others in turn, so an XCD that
+// runs faster also finishes a slower one's last items; -1 when all are taken.
+// One atomic per probe, nothing waits on another workgroup; which workgroup
+// computes an item does not change its result.
+__device__ __forceinline__ int64_t take_item(int32_t* q, int x, int64_t total) {
+  const int64_t per = (total + 7) >> 3;
+  for (int k = 0; k < 8; ++k) {
+    const int y = (x + k) & 7;
+    const int64_t lo = y * per;
+    const int64_t n = total - lo < per ? total - lo : per;
+    if (n <= 0) continue;
+    const int64_t t = atomicAdd(reinterpret_cast<int*>(q + y), 1);
+    if (t < n) return lo + t;
+  }
+  return -1;
+}
+
+// Grid for take_item: 1/16 more workgroups per XCD than its range holds, to
+// take over items of slower XCDs (the rest find every range used up and leave).
+__host__ __device__ constexpr int64_t queue_grid(int64_t items) {
+  const int64_t per = (items + 7) / 8;
+  return 8 * (per + (per + 15) / 16);
+}
+
 // Grouped raster: logical tile -> (a, b) with `group` consecutive a-tiles
 // sharing each b, so tiles in flight on one XCD reuse each other's panels.
 __device__ __forceinline__ void grouped(int64_t L, int64_t ta, int64_t tb, int64_t group,

@@ -309,6 +309,8 @@ struct FwdArgs {
   const Ctl* ctl;         // n_valid: rows of x (packed) that take part
   int64_t row0, cap;      // token chunk: first packed row (pointers above start there), capacity
   const float* weight;    // [v] class weights or null: part_s then holds sum_v w_v z_v
+  int32_t* queue;         // [8] work-queue counters of this launch, zero at its start (take_item),
+                          // or null: static assignment by workgroup id
   float* zs;              // null, or the raw logit tiles of the chunk, stored in register order
   int64_t zs_vt;          // vocabulary tiles per token tile in zs
 };
@@ -434,11 +436,30 @@ void k_fwd(FwdArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
   // wave-row exchange of the final partials; gemm_tile has released `lds` by then
   float (*xch)[2][4][32] = reinterpret_cast<float (*)[2][4][32]>(lds);
-  // token tiles of the valid rows only, spread evenly over the XCDs
+  // token tiles of the valid rows only, spread over the XCDs
   const int64_t nv = chunk_valid(a.ctl, a.row0, a.cap);
   const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;
   int64_t L;
-  if (!xcd_logical_n(blockIdx.x, n_tiles * a.n_chunks, L)) return;   // whole workgroup leaves
+  if (a.queue) {
+    // The XCDs do not run equally fast (one 6% behind another in measured
+    // launches), so the work items go out through take_item, keyed by the
+    // XCD the workgroup runs on (hardware register XCC_ID).  The item reaches
+    // the other threads through LDS before the slab stream uses it, and is
+    // made wave-uniform again (readfirstlane), so the tile addresses derived
+    // from it stay in scalar registers; taken as a per-lane value it made the
+    // forward spill 12 more registers and run 28% slower.  Items fit in 32
+    // bits (at most 2^14 token tiles times 2^12 chunks).
+    if (threadIdx.x == 0) {
+      const int xcd = static_cast<int>(__builtin_amdgcn_s_getreg((15 << 11) | 20)) & 7;
+      *reinterpret_cast<int32_t*>(lds) = static_cast<int32_t>(take_item(a.queue, xcd, n_tiles * a.n_chunks));
+    }
+    __syncthreads();
+    L = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int32_t*>(lds));
+    __syncthreads();
+    if (L < 0) return;                                              // whole workgroup leaves
+  } else if (!xcd_logical_n(blockIdx.x, n_tiles * a.n_chunks, L)) {
+    return;
+  }
   int64_t nt, ch;
   grouped(L, n_tiles, a.n_chunks, a.group, nt, ch);
 
