@@ -18,7 +18,7 @@ __global__ void k_zero_queue(int32_t* q) { q[threadIdx.x] = 0; }
 
 template <typename T, bool kBias, bool kSoftcap, bool kSumZ, bool kArgmax, bool kStore>
 void launch_fwd_mode(const FwdArgs<T>& a, const FwdGrid& g, hipStream_t s) {
-  if (a.queue) hipLaunchKernelGGL(k_zero_queue, dim3(1), dim3(16), 0, s, a.queue);
+  hipLaunchKernelGGL(k_zero_queue, dim3(1), dim3(16), 0, s, a.queue);
   if (g.main_chunks > 0) {
     FwdArgs<T> m = a;
     m.vt_base = 0;
@@ -27,7 +27,7 @@ void launch_fwd_mode(const FwdArgs<T>& a, const FwdGrid& g, hipStream_t s) {
     m.n_chunks = g.main_chunks;
     m.tiles_per_chunk = g.tiles_per_chunk;
     const int64_t items = g.n_tiles * m.n_chunks;
-    const int64_t grid = a.queue ? queue_grid(items) : (items + 7) / 8 * 8;
+    const int64_t grid = queue_grid(items);
     hipLaunchKernelGGL((k_fwd<T, kBias, kSoftcap, kSumZ, false, kArgmax, kStore>),
                        dim3(static_cast<unsigned>(grid)), dim3(tile::kThreads), 0, s, m);
   }
@@ -38,8 +38,8 @@ void launch_fwd_mode(const FwdArgs<T>& a, const FwdGrid& g, hipStream_t s) {
     t.chunk_base = g.main_chunks;
     t.n_chunks = 1;
     t.tiles_per_chunk = 1;
-    if (t.queue) t.queue += 8;
-    const int64_t grid = t.queue ? queue_grid(g.n_tiles) : (g.n_tiles + 7) / 8 * 8;
+    t.queue += 8;
+    const int64_t grid = queue_grid(g.n_tiles);
     hipLaunchKernelGGL((k_fwd<T, kBias, kSoftcap, kSumZ, true, kArgmax, kStore>),
                        dim3(static_cast<unsigned>(grid)), dim3(tile::kThreads), 0, s, t);
   }

@@ -309,8 +309,7 @@ struct FwdArgs {
   const Ctl* ctl;         // n_valid: rows of x (packed) that take part
   int64_t row0, cap;      // token chunk: first packed row (pointers above start there), capacity
   const float* weight;    // [v] class weights or null: part_s then holds sum_v w_v z_v
-  int32_t* queue;         // [8] work-queue counters of this launch, zero at its start (take_item),
-                          // or null: static assignment by workgroup id
+  int32_t* queue;         // [8] work-queue counters of this launch, zero at its start (take_item)
   float* zs;              // null, or the raw logit tiles of the chunk, stored in register order
   int64_t zs_vt;          // vocabulary tiles per token tile in zs
 };
@@ -440,7 +439,7 @@ void k_fwd(FwdArgs<T> a) {
   const int64_t nv = chunk_valid(a.ctl, a.row0, a.cap);
   const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;
   int64_t L;
-  if (a.queue) {
+  {
     // The XCDs do not run equally fast (one 6% behind another in measured
     // launches), so the work items go out through take_item, keyed by the
     // XCD the workgroup runs on (hardware register XCC_ID).  The item reaches
@@ -457,8 +456,6 @@ void k_fwd(FwdArgs<T> a) {
     L = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int32_t*>(lds));
     __syncthreads();
     if (L < 0) return;                                              // whole workgroup leaves
-  } else if (!xcd_logical_n(blockIdx.x, n_tiles * a.n_chunks, L)) {
-    return;
   }
   int64_t nt, ch;
   grouped(L, n_tiles, a.n_chunks, a.group, nt, ch);

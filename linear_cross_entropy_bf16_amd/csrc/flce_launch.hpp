@@ -13,9 +13,10 @@
 
 namespace flce {
 
-// Grid of the forward GEMM: whole vocabulary tiles go to one launch of
-// n_tiles x main_chunks workgroups (tiles_per_chunk tiles each); a partial last
-// vocabulary tile (V mod 256 rows) gets a launch of its own.
+// Grid of the forward GEMM: whole vocabulary tiles go to one launch over
+// n_tiles x main_chunks work items (tiles_per_chunk tiles each, handed out by
+// take_item); a partial last vocabulary tile (V mod 256 rows) gets a launch of
+// its own.
 struct FwdGrid {
   int64_t n_tiles;          // token tiles (upper bound: all rows valid)
   int64_t v_full, v_tiles;  // whole vocabulary tiles; all vocabulary tiles
@@ -28,6 +29,8 @@ enum class FwdMode { kPlain = 0, kArgmax = 1, kStore = 2 };
 
 // Option keys: forward  bit 0 bias, bit 1 softcap, bit 2 sum of z (smoothing);
 //              G kernel bit 0 bias, bit 1 softcap, bit 2 class weights.
+// a.queue: 16 ints of device memory, the work-queue counters of the two
+// launches (zeroed here first).
 template <typename T, int kKey>
 void launch_fwd(const FwdArgs<T>& a, const FwdGrid& g, FwdMode mode, hipStream_t s);
 
