@@ -717,30 +717,49 @@ static __global__ __launch_bounds__(256) void k_loss_final(const double* __restr
 // orientations ([tokens][slice] for dX, [slice][tokens] for dW and db).
 
 // out[c][r] = in[r][c] for r < rows, c < cols; 0 for the padding r < ld_out,
-// c < out_rows.  64 x 64 tiles through LDS, coalesced on both sides.
+// c < out_rows.  64 x 64 tiles through LDS.  Every global access is one
+// 16-byte vector (8 bf16 or 4 fp32 of a row): the library's row pitches are
+// multiples of 8 elements and its bases 16-byte aligned, so 64 lanes move
+// 1 KiB per load or store (one element per lane ran at ~1.75 TB/s).  A
+// thread loads vectors of tile rows into LDS, then gathers one vector of an
+// output row (a tile column) element by element.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, int64_t rows,
                                                    int64_t cols, int64_t ld_in,
                                                    T* __restrict__ out, int64_t out_rows,
                                                    int64_t ld_out, const Ctl* __restrict__ ctl,
                                                    int64_t row0) {
-  __shared__ T t[64][65];
+  constexpr int kV = 16 / static_cast<int>(sizeof(T));   // elements per vector
+  constexpr int kVpr = 64 / kV;                          // vectors per tile row
+  constexpr int kRpp = 256 / kVpr;                       // tile rows per pass of the block
+  constexpr int kPitch = 64 + kV;                        // LDS row pitch: 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) T t[64 * kPitch];
   if (ctl) rows = chunk_valid(ctl, row0, rows);   // X: only the chunk's packed valid rows
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int lv = threadIdx.x % kVpr, lr = threadIdx.x / kVpr;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rr = ty + 4 * i;
-    const int64_t r = r0 + rr, c = c0 + tx;
-    t[rr][tx] = (r < rows && c < cols) ? in[r * ld_in + c] : T(0);
+  for (int i = 0; i < 64 / kRpp; ++i) {
+    const int rr = lr + kRpp * i;
+    const int64_t r = r0 + rr, c = c0 + lv * kV;   // cols is a multiple of kV: a vector is all in or all out
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (r < rows && c < cols) v = *reinterpret_cast<const u32x4*>(in + r * ld_in + c);
+    *reinterpret_cast<u32x4*>(t + rr * kPitch + lv * kV) = v;
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int cc = ty + 4 * i;
-    const int64_t c = c0 + cc, r = r0 + tx;
-    if (c < out_rows && r < ld_out) out[c * ld_out + r] = t[tx][cc];
+  for (int i = 0; i < 64 / kRpp; ++i) {
+    const int cc = lr + kRpp * i;                  // tile column = output row
+    const int64_t c = c0 + cc, r = r0 + lv * kV;
+    if (c < out_rows && r < ld_out) {
+      union {
+        T e[kV];
+        u32x4 v;
+      } g;
+#pragma unroll
+      for (int j = 0; j < kV; ++j) g.e[j] = t[(lv * kV + j) * kPitch + cc];
+      *reinterpret_cast<u32x4*>(out + c * ld_out + r) = g.v;
+    }
   }
 }
 
