@@ -226,10 +226,16 @@ flce_status launched() { return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE
 
 char* at(void* ws, int64_t off) { return static_cast<char*>(ws) + off; }
 
-// Work-queue counters of the forward launches (take_item): 16 ints in bytes
-// 64..127 of the control block, after the Ctl fields.
-static_assert(sizeof(flce::Ctl) <= 64, "Ctl overlaps the forward's queue counters");
+// Work-queue counters in the control block, after the Ctl fields: the forward
+// launches' (take_item) in bytes 64..127, the backward's (claim_tile: G
+// launches 128..159, dX launches 160..191).
+static_assert(sizeof(flce::Ctl) <= 64, "Ctl overlaps the queue counters");
+static_assert(192 <= kAlign, "queue counters exceed the control block");
 int32_t* fwd_queue(void* ws, const Layout& L) { return reinterpret_cast<int32_t*>(at(ws, L.ctl + 64)); }
+int32_t* bwd_queue(void* ws, const Layout& L) { return reinterpret_cast<int32_t*>(at(ws, L.ctl + 128)); }
+
+// 16 counters back to zero (one block of 16 threads).
+__global__ void k_zero16(int32_t* q) { q[threadIdx.x] = 0; }
 
 void fill(float* p, int64_t count, float value, hipStream_t s) {
   if (count <= 0) return;
@@ -470,6 +476,12 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
   const int64_t d_tiles = cdiv(p.d, tile::kM);
   const int64_t c_tiles = L.chunk / tile::kN;   // token tiles of a chunk (upper bound)
   const bool has_bias = bias != nullptr;
+  // Tail counters of the G and dX launches: each launch's workgroup 0 zeroes
+  // the other kernel's set, which runs next in stream order; the first G
+  // launch's set is zeroed here.
+  int32_t* q_g = bwd_queue(ws, L);
+  int32_t* q_dx = q_g + 8;
+  if (p.n > 0) hipLaunchKernelGGL(k_zero16, dim3(1), dim3(16), 0, s, q_g);
   // Token chunks outer, vocabulary slices inner: dX of a chunk is finished
   // within its pass; dW and db of every slice accumulate over the chunks.
   for (int64_t ci = 0; ci < L.n_tok_chunks; ++ci) {
@@ -508,9 +520,11 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
         ga.g = g;
         ga.gt = gt;
         ga.s_tiles = s_tiles;
-        const int64_t g_grid = grid8(c_tiles * s_tiles);   // upper bound: all rows valid
+        const int64_t g_grid = flce::queue_grid(c_tiles * s_tiles);   // upper bound: all rows valid
         ga.group = kRasterGroup;
         ga.weight = p.class_weight;
+        ga.queue = q_g;
+        ga.queue_next = q_dx;
         dispatch_g<T>(ga, g_grid, has_bias, p.softcap > 0.f, s);
       }
       if (p.dw_bf16)
@@ -534,7 +548,9 @@ flce_status run_backward(const flce_params& p, const Layout& L, const void* x, c
         xa.dx = static_cast<T*>(dx);
         xa.first = si == 0;
         xa.d_tiles = d_tiles;
-        const int64_t x_grid = grid8(d_tiles * c_tiles);   // upper bound: all rows valid
+        xa.queue = q_dx;
+        xa.queue_next = q_g;
+        const int64_t x_grid = flce::queue_grid(d_tiles * c_tiles);   // upper bound: all rows valid
         flce::launch_dx<T>(xa, x_grid, si + 1 == n_slices, s);
       }
       if (has_bias)

@@ -481,6 +481,53 @@ __host__ __device__ constexpr int64_t queue_grid(int64_t items) {
   return 8 * (per + (per + 15) / 16);
 }
 
+// Tile of a workgroup in a launch of one tile per workgroup.  Without a queue:
+// xcd_logical_n.  With one: the tiles are cut into the 8 ranges of take_item;
+// the first 7/8 of each range go to workgroups by id exactly as in
+// xcd_logical_n (no atomic), the last 1/8 (its tail) through the queue, q[y]
+// counting the tail tiles of range y handed out.  A workgroup past its XCD's
+// head takes the next tail tile of the XCD it runs on (hardware XCC_ID), then
+// of the others, so a faster XCD finishes a slower one's last tiles (the grid,
+// queue_grid, has 1/16 more workgroups per XCD for that).  The tile reaches
+// the other threads through `lds` (free: called before any slab is loaded)
+// and is made wave-uniform, so addresses derived from it stay scalar.  Returns
+// false when the workgroup has no tile.
+__device__ __forceinline__ bool claim_tile(int64_t wg, int64_t total, int32_t* q, char* lds,
+                                           int64_t& L) {
+  if (!q) return xcd_logical_n(wg, total, L);
+  const int64_t per = (total + 7) >> 3;
+  const int64_t tail = (per + 7) >> 3;
+  auto head_of = [&](int64_t y, int64_t& n) {   // tiles of range y, and its head
+    const int64_t left = total - y * per;
+    n = left < 0 ? 0 : (left < per ? left : per);
+    return n > tail ? n - tail : 0;
+  };
+  const int64_t x = wg & 7, i = wg >> 3;
+  int64_t n_x;
+  const int64_t head_x = head_of(x, n_x);
+  if (i < head_x) {
+    L = x * per + i;
+    return true;
+  }
+  if (threadIdx.x == 0) {
+    const int hw = static_cast<int>(__builtin_amdgcn_s_getreg((15 << 11) | 20)) & 7;
+    int32_t item = -1;
+    for (int k = 0; k < 8 && item < 0; ++k) {
+      const int y = (hw + k) & 7;
+      int64_t n_y;
+      const int64_t h = head_of(y, n_y);
+      if (n_y - h <= 0) continue;
+      const int64_t t = atomicAdd(reinterpret_cast<int*>(q + y), 1);
+      if (t < n_y - h) item = static_cast<int32_t>(y * per + h + t);
+    }
+    *reinterpret_cast<int32_t*>(lds) = item;
+  }
+  __syncthreads();
+  L = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int32_t*>(lds));
+  __syncthreads();
+  return L >= 0;
+}
+
 // Grouped raster: logical tile -> (a, b) with `group` consecutive a-tiles
 // sharing each b, so tiles in flight on one XCD reuse each other's panels.
 __device__ __forceinline__ void grouped(int64_t L, int64_t ta, int64_t tb, int64_t group,

@@ -785,6 +785,8 @@ struct GArgs {
   const float* zs;      // null, or the chunk's raw logit tiles (see stored_tile): read, not recomputed
   int64_t zs_vt;        // vocabulary tiles per token tile in zs (the slice is then all of V)
   const float* weight;  // [v] class weights (with kWeight)
+  int32_t* queue;       // [8] tail counters of this launch (claim_tile), zero at its start, or null
+  int32_t* queue_next;  // [8] or null: the next launch's counters, zeroed by workgroup 0
 };
 
 __device__ __forceinline__ void store1(uint16_t* p, float a) {
@@ -968,10 +970,11 @@ template <typename T, bool kBias, bool kSoftcap, bool kWeight>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bwd_g(GArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
+  if (a.queue_next && blockIdx.x == 0 && threadIdx.x < 8) a.queue_next[threadIdx.x] = 0;
   const int64_t nv = chunk_valid(a.ctl, a.row0, a.n);
   const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;   // valid rows only
   int64_t L;
-  if (!xcd_logical_n(blockIdx.x, n_tiles * a.s_tiles, L)) return;
+  if (!claim_tile(blockIdx.x, n_tiles * a.s_tiles, a.queue, lds, L)) return;
   int64_t nt, st;
   grouped(L, n_tiles, a.s_tiles, a.group, nt, st);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1139,6 +1142,8 @@ struct DxArgs {
   int64_t d_tiles;
   const int32_t* rows;  // packed row -> row (from the chunk's first packed row)
   int64_t row0;         // token chunk: first packed row; n is its capacity
+  int32_t* queue;       // [8] tail counters of this launch (claim_tile), zero at its start, or null
+  int32_t* queue_next;  // [8] or null: the next launch's counters, zeroed by workgroup 0
 };
 
 // dX (+)= G_slice W_slice, computed as C[d, n] tile by tile.  The running
@@ -1257,10 +1262,11 @@ template <typename T, bool kLast>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_dx(DxArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char lds[tile::kLdsBytes];
+  if (a.queue_next && blockIdx.x == 0 && threadIdx.x < 8) a.queue_next[threadIdx.x] = 0;
   const int64_t nv = chunk_valid(a.ctl, a.row0, a.n);
   const int64_t n_tiles = (nv + tile::kN - 1) / tile::kN;   // valid rows only
   int64_t L;
-  if (!xcd_logical_n(blockIdx.x, a.d_tiles * n_tiles, L)) return;
+  if (!claim_tile(blockIdx.x, a.d_tiles * n_tiles, a.queue, lds, L)) return;
   dx_tile<T, kLast>(a, L, nv, n_tiles, lds);
 }
 
