@@ -51,8 +51,10 @@
  *    throws across this interface.  Just before its launches an entry point
  *    clears the calling thread's pending HIP error (hipGetLastError), so
  *    FLCE_ERR_DEVICE reports a failure of its own launches.
- *  - Results are deterministic: every reduction has a fixed order, and there
- *    are no global atomics.
+ *  - Results are deterministic: every reduction has a fixed order and no
+ *    value is accumulated with atomics.  The only atomics are work counters
+ *    in the workspace that decide which workgroup computes which tile; a
+ *    tile's result does not depend on that.
  *  - Concurrent calls that share a workspace race; give each in-flight call
  *    its own workspace.
  */

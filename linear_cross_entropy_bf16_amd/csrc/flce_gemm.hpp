@@ -438,15 +438,10 @@ __device__ __forceinline__ void gemm_prefetch(const Operand<T>& A, const Operand
 
 // ---------------------------------------------------------------- tile order
 // Workgroups are handed to the 8 XCDs round-robin by id.  Remap the id so each
-// XCD walks a contiguous range of logical tiles (grid is a multiple of 8).
-__device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t grid) {
-  const int64_t per = grid >> 3;
-  return (wg & 7) * per + (wg >> 3);
-}
-
-// The same for a tile count known only on the device (valid rows): the grid
-// is sized for the upper bound, each XCD takes an equal share of the `total`
-// tiles and its surplus workgroups return false.
+// XCD walks a contiguous range of logical tiles: the grid (a multiple of 8) is
+// sized for an upper bound of the tiles (the valid rows are known only on the
+// device), each XCD takes an equal share of the `total` tiles and its surplus
+// workgroups return false.
 __device__ __forceinline__ bool xcd_logical_n(int64_t wg, int64_t total, int64_t& L) {
   const int64_t per = (total + 7) >> 3;
   const int64_t i = wg >> 3;

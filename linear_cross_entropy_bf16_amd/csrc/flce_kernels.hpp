@@ -16,8 +16,10 @@
 //   k_dx          dX (+)= G_slice W_slice, scaled at the last slice (K = slice width)
 //   k_db          db[slice] = scale sum_n G_slice
 //
-// Every reduction has a fixed order and no kernel uses global atomics, so
-// results are bitwise reproducible run to run.
+// Every reduction has a fixed order and nothing is accumulated with atomics,
+// so results are bitwise reproducible run to run.  The only atomics are the
+// work counters of take_item / claim_tile, which decide which workgroup
+// computes which tile, not what it computes.
 #pragma once
 
 #include <hip/hip_runtime.h>
