@@ -344,6 +344,20 @@ def test_deterministic_bitwise():
     assert a["loss"] == b["loss"]
 
 
+def test_repeat_calls_bitwise_with_work_queues():
+    """The forward, G and dX launches hand their tiles out through per-XCD
+    work counters (which workgroup computes which tile changes from run to
+    run); the results must not.  A shape with thousands of forward items and
+    G tiles per slice, so the queues' tails are in use, called three times."""
+    inp = small_problem(12000, 512, 40000, "bf16", bias=True, seed=21)
+    o = O.LossOptions(label_smoothing=0.05, lse_square_scale=1e-4)
+    runs = [U.run_fused(inp, "bf16", o) for _ in range(3)]
+    for r in runs[1:]:
+        assert r["loss"] == runs[0]["loss"]
+        for k in ("lse", "dx", "dw", "db"):
+            assert np.array_equal(r[k], runs[0][k]), k
+
+
 def test_fused_equals_separate_calls():
     inp = small_problem(500, 128, 2000, "bf16", bias=True, seed=9)
     o = O.LossOptions(label_smoothing=0.1, lse_square_scale=1e-3)
